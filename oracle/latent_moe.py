@@ -1,0 +1,289 @@
+"""CPU oracle of the LatentMoE layer forward pass (numpy, float64).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, headers, tables or helpers) and imports nothing from it,
+nor from the synthetic-input package: every function takes plain arrays.
+
+What it computes, and where the pages state it
+----------------------------------------------
+"The Training and RL Infrastructure Behind MAI-Thinking-1" (MAI-Base-1):
+* section "The model the systems run", model table, MoE row: LatentMoE, a
+  shared down-projection to the latent width before dispatch, 8 of 512 experts
+  with softmax gating, expert FFN; Feed-forward row: SwiGLU.
+* same section, paragraph after the table: the router sees the full hidden
+  state while the experts work on the compressed latent.
+* section 2 "Numerics", "Pre-training and mid-training precision": router
+  logits, router weights, the routing GEMM and the MoE combine are FP32; the
+  residual stream is FP32; weights and activations default to BF16.
+* section 2, "Bitwise determinism": MoE top-k uses a stable sort, so ties break
+  the same way every run; fixed-order accumulation instead of atomics.
+* section 3, "Sharding and parallelism", "From capacity to dropless": dropless
+  routing (no capacity, no dropped tokens).
+"MAI-Base-2: Microsoft's 2.8T base model..." (MAI-Base-2), section "The
+model": 7 of 512 routed experts plus one shared expert every token passes
+through; MoE down-projection dimension; the shared expert is not down/up
+projected; tokens are projected down before dispatch and back up afterwards.
+
+Readings where the pages are silent (each is listed in the design notes):
+softmax over all E experts before top-k, selected probabilities used without
+renormalisation; router bias added to the logits before the softmax; top-k
+selection on the FP32 logits, ties to the lower expert index, slots ordered by
+logit descending; rows of one expert in ascending token order; SwiGLU is
+W_d (silu(W_g z) * (W_u z)) with silu(v) = v * sigmoid(v) and no biases; the
+latent projections are plain linear maps; the combine is done in the latent
+space (linear, so equal to combining after the up-projection); the shared
+expert's output is added with weight 1; no extra scaling of the routed output.
+
+Precision modes
+---------------
+``exact``         : nothing is rounded after the inputs (float64 throughout).
+``bf16_operands`` : every GEMM operand is BF16, as the pages make weights and
+                    activations BF16: the latent z, the SwiGLU activation h,
+                    the combined latent c and the shared expert's h are
+                    rounded to bf16 (round to nearest, ties to even) where they
+                    enter their next GEMM.  Expert outputs y, the combine and
+                    the layer output stay float64 (the pages keep the combine
+                    and the residual stream FP32).
+
+Parity pins: see ``tests/test_oracle.py`` (closed forms, brute force over all
+experts, invariants, special cases).  No function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MODES = ("exact", "bf16_operands")
+
+
+# ---------------------------------------------------------------------------
+# rounding
+# ---------------------------------------------------------------------------
+
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (8-bit significand,
+    ties to even), returned as float64.  Written from the definition: scale the
+    significand to [128, 256), round half to even, scale back."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)                 # v = m * 2**e, 0.5 <= |m| < 1
+    r = np.rint(np.ldexp(m, 8))        # np.rint rounds half to even
+    return np.ldexp(r, e - 8)
+
+
+def _maybe_bf16(v, mode):
+    if mode not in MODES:
+        raise ValueError(f"unknown mode {mode!r}")
+    return round_bf16(v) if mode == "bf16_operands" else v
+
+
+# ---------------------------------------------------------------------------
+# A1: router (softmax gating over all experts, stable top-k)
+# ---------------------------------------------------------------------------
+
+def router_logits(x, w_router, b_router=None):
+    """Router logits l = x W_r^T + b on the full hidden state (float64)."""
+    logits = np.asarray(x, np.float64) @ np.asarray(w_router, np.float64).T
+    if b_router is not None:
+        logits = logits + np.asarray(b_router, np.float64)[None, :]
+    return logits
+
+
+def softmax(logits):
+    """Softmax over the expert axis, max-subtracted."""
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def topk_stable(scores, k):
+    """Indices of the k largest scores per row, largest first; equal scores
+    keep ascending expert index (a stable sort of -score)."""
+    order = np.argsort(-np.asarray(scores), axis=1, kind="stable")
+    return order[:, :k]
+
+
+def route(x, w_router, b_router, k):
+    """Softmax gating with top-k.
+
+    Returns dict: logits (float64), logits_f32 (float32, the precision the
+    selection is taken in), probs (float64 softmax over all experts),
+    topk_idx [T,k] int32, topk_w [T,k] float64 (probabilities of the selected
+    experts, not renormalised)."""
+    logits = router_logits(x, w_router, b_router)
+    logits_f32 = logits.astype(np.float32)
+    probs = softmax(logits)
+    idx = topk_stable(logits_f32, k).astype(np.int32)
+    w = np.take_along_axis(probs, idx.astype(np.int64), axis=1)
+    return {"logits": logits, "logits_f32": logits_f32, "probs": probs,
+            "topk_idx": idx, "topk_w": w}
+
+
+# ---------------------------------------------------------------------------
+# A2: permutation of (token, slot) assignments into expert order
+# ---------------------------------------------------------------------------
+
+def permute(topk_idx, E):
+    """Stable counting sort of the assignments (t, j) by expert.
+
+    Returns expert_counts[E], expert_offsets[E+1] (exclusive prefix sum,
+    offsets[E] = T*k), row_token[T*k] (source token of each expert-ordered
+    row; ascending token order inside an expert) and assign_row[T,k] (the row
+    that assignment (t, j) occupies).  All int64."""
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    T, k = idx.shape
+    counts = np.bincount(idx.ravel(), minlength=E).astype(np.int64)
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(counts)
+    row_token = np.empty(T * k, np.int64)
+    assign_row = np.empty((T, k), np.int64)
+    for e in range(E):
+        toks, slots = np.nonzero(idx == e)     # row-major scan: ascending t
+        rows = offsets[e] + np.arange(toks.size)
+        row_token[rows] = toks
+        assign_row[toks, slots] = rows
+    return {"expert_counts": counts, "expert_offsets": offsets,
+            "row_token": row_token, "assign_row": assign_row}
+
+
+# ---------------------------------------------------------------------------
+# A3, A5, A6: latent down-projection and the SwiGLU experts
+# ---------------------------------------------------------------------------
+
+def silu(v):
+    """silu(v) = v * sigmoid(v)."""
+    v = np.asarray(v, np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def latent_down(x, w_dn, mode="exact"):
+    """z = x W_dn^T: the shared projection of every token to the latent width."""
+    return _maybe_bf16(np.asarray(x, np.float64) @ np.asarray(w_dn, np.float64).T, mode)
+
+
+def swiglu_expert(z_rows, w_gate, w_up, w_down, mode="exact"):
+    """y = (silu(z W_g^T) * (z W_u^T)) W_d^T for the rows routed to one expert."""
+    g = z_rows @ np.asarray(w_gate, np.float64).T
+    u = z_rows @ np.asarray(w_up, np.float64).T
+    h = _maybe_bf16(silu(g) * u, mode)
+    return h @ np.asarray(w_down, np.float64).T
+
+
+def expert_rows(z, perm, experts, mode="exact", expert_fn=None):
+    """Expert outputs y[T*k, L] in expert order: for every expert e, the rows
+    offsets[e] .. offsets[e+1] are its tokens' latents through its FFN.
+    ``experts[e]`` yields (W_gate[e], W_up[e], W_down[e]); ``expert_fn`` may
+    replace the SwiGLU (used by the identity-expert pin)."""
+    offsets = perm["expert_offsets"]
+    row_token = perm["row_token"]
+    E = offsets.size - 1
+    y = np.zeros((row_token.size, z.shape[1]), np.float64)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        zr = z[row_token[a:b]]
+        y[a:b] = expert_fn(e, zr) if expert_fn is not None else \
+            swiglu_expert(zr, *experts[e], mode=mode)
+    return y
+
+
+# ---------------------------------------------------------------------------
+# A7, A8, A9: combine, up-projection, shared expert
+# ---------------------------------------------------------------------------
+
+def combine(y_rows, topk_w, assign_row):
+    """c[t] = sum over j = 0..k-1 (ascending) of w[t, j] * y[assign_row[t, j]]."""
+    T, k = assign_row.shape
+    c = np.zeros((T, y_rows.shape[1]), np.float64)
+    for j in range(k):
+        c += np.asarray(topk_w, np.float64)[:, j:j + 1] * y_rows[assign_row[:, j]]
+    return c
+
+
+def latent_up(c, w_lat_up, mode="exact"):
+    """out = c W_up^T: projection of the combined latent back to the hidden width."""
+    return _maybe_bf16(c, mode) @ np.asarray(w_lat_up, np.float64).T
+
+
+def shared_expert(x, ws_gate, ws_up, ws_down, mode="exact"):
+    """Base-2 shared expert: SwiGLU on the full hidden state, no latent projection."""
+    x = np.asarray(x, np.float64)
+    g = x @ np.asarray(ws_gate, np.float64).T
+    u = x @ np.asarray(ws_up, np.float64).T
+    h = _maybe_bf16(silu(g) * u, mode)
+    return h @ np.asarray(ws_down, np.float64).T
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+# ---------------------------------------------------------------------------
+
+def forward(x, w_router, b_router, k, w_dn, experts, w_lat_up, shared=None,
+            mode="exact", routing=None, expert_fn=None):
+    """LatentMoE forward: route -> permute -> z = x W_dn^T -> experts on the
+    latent -> weighted combine -> up-projection (+ shared expert).
+
+    ``experts[e]`` -> (W_gate[e], W_up[e], W_down[e]); ``shared`` is None or
+    (Ws_gate, Ws_up, Ws_down); ``routing`` optionally replaces the router with
+    given (topk_idx, topk_w).  Returns a dict of every stage's result."""
+    x = np.asarray(x, np.float64)
+    E = int(np.asarray(w_router).shape[0]) if w_router is not None else len(experts)
+    if routing is None:
+        r = route(x, w_router, b_router, k)
+    else:
+        r = {"topk_idx": np.asarray(routing[0], np.int32),
+             "topk_w": np.asarray(routing[1], np.float64)}
+    p = permute(r["topk_idx"], E)
+    z = latent_down(x, w_dn, mode)
+    y = expert_rows(z, p, experts, mode, expert_fn)
+    c = combine(y, r["topk_w"], p["assign_row"])
+    out = latent_up(c, w_lat_up, mode)
+    if shared is not None:
+        out = out + shared_expert(x, *shared, mode=mode)
+    res = dict(r)
+    res.update(p)
+    res.update({"z": z, "y_rows": y, "c": c, "out": out})
+    return res
+
+
+def forward_tokens(x_rows, topk_idx, topk_w, w_dn, experts, w_lat_up, shared=None,
+                   mode="exact"):
+    """Per-token definition of the layer output, with no permutation: for each
+    token t, out[t] = (sum_j w[t,j] * expert_{idx[t,j]}(z_t)) W_up^T (+ shared).
+    Used for sampled tokens of shapes too large for ``forward``."""
+    x_rows = np.asarray(x_rows, np.float64)
+    z = latent_down(x_rows, w_dn, mode)
+    c = np.zeros_like(z)
+    for t in range(x_rows.shape[0]):
+        for j in range(topk_idx.shape[1]):
+            e = int(topk_idx[t, j])
+            c[t] += float(topk_w[t, j]) * swiglu_expert(z[t:t + 1], *experts[e], mode=mode)[0]
+    out = latent_up(c, w_lat_up, mode)
+    if shared is not None:
+        out = out + shared_expert(x_rows, *shared, mode=mode)
+    return {"z": z, "c": c, "out": out}
+
+
+def forward_dense_bruteforce(x, w_router, b_router, k, w_dn, experts, w_lat_up,
+                             shared=None, mode="exact", expert_fn=None):
+    """Brute force: evaluate every expert on every token, then keep the top-k
+    by a mask (no permutation, no gather).  For tiny inputs only."""
+    x = np.asarray(x, np.float64)
+    r = route(x, w_router, b_router, k)
+    T = x.shape[0]
+    E = int(np.asarray(w_router).shape[0])
+    mask = np.zeros((T, E), np.float64)
+    for t in range(T):
+        for j in range(k):
+            mask[t, r["topk_idx"][t, j]] = 1.0
+    z = latent_down(x, w_dn, mode)
+    c = np.zeros_like(z)
+    for e in range(E):
+        ye = expert_fn(e, z) if expert_fn is not None else swiglu_expert(z, *experts[e], mode=mode)
+        c += (mask[:, e] * r["probs"][:, e])[:, None] * ye
+    out = latent_up(c, w_lat_up, mode)
+    if shared is not None:
+        out = out + shared_expert(x, *shared, mode=mode)
+    return {"out": out, "c": c, "topk_idx": r["topk_idx"], "probs": r["probs"]}
