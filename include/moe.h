@@ -1,0 +1,211 @@
+/*
+ * libmoe — forward pass of the LatentMoE feed-forward layer on one AMD
+ * MI355X (gfx950), as a C ABI over hand-written HIP kernels.
+ *
+ * The layer (pages: "The Training and RL Infrastructure Behind MAI-Thinking-1",
+ * section "The model the systems run", model table MoE and Feed-forward rows
+ * and the paragraph after it; "MAI-Base-2: Microsoft's 2.8T base model...",
+ * section "The model"):
+ *
+ *   logits = x W_r^T + b            router on the full hidden state, FP32
+ *   p      = softmax(logits)        over all E experts
+ *   idx,w  = top-k of logits        stable: ties to the lower expert index;
+ *                                   w = p at the selected experts, not renormalised
+ *   z      = x W_dn^T               shared down-projection to the latent width L
+ *   y_r    = W_d,e (silu(W_g,e z_t) * (W_u,e z_t))   per routed (token, expert)
+ *   c_t    = sum_j w[t,j] y_{row(t,j)}               fixed order j = 0..k-1, FP32
+ *   out    = c W_up^T  [+ shared expert SwiGLU(x) on the full width]   FP32
+ *
+ * The call sequence of one forward pass is
+ *   moe_route -> moe_permute -> moe_latent_ffn_forward -> moe_combine
+ * on one stream.  A caller may skip moe_route and supply its own topk_idx /
+ * topk_w (router replay; "The Training and RL Infrastructure Behind
+ * MAI-Thinking-1", section 3 "From capacity to dropless" and section 4
+ * "Closing the learner-inference numerics gap").
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - All tensor pointers are DEVICE pointers, contiguous, row-major, 16-byte
+ *   aligned.  bf16 tensors are passed as uint16_t (raw bfloat16 bits).
+ * - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *   enqueues work on that stream and returns; nothing is copied to the host,
+ *   and per-expert sizes are read on the device only (device-resident token
+ *   metadata: "Frontier Pre-training at Microsoft AI", section "Reducing
+ *   per-expert overhead").
+ * - Ownership: the caller allocates and frees every buffer, including the
+ *   workspace `ws` (size from moe_workspace_bytes).  The library never
+ *   allocates or frees memory and never synchronises.  Buffer sizes depend
+ *   only on the shapes, never on the routing (dropless, fixed memory).
+ * - Errors: 0 (MOE_OK) on success, a negative MOE_ERR_* code otherwise.  All
+ *   arguments are checked on the host before anything is launched; on an
+ *   argument error nothing is enqueued.  T == 0 is a successful no-op.
+ *   Faults inside a kernel surface at the caller's next synchronisation, as
+ *   for any HIP call.  Non-finite inputs give undefined (but memory-safe)
+ *   results.
+ * - Determinism: identical inputs on the same device give bitwise-identical
+ *   outputs (no floating-point atomics; fixed reduction orders), as the pages
+ *   require of MoE top-k and of accumulations ("The Training and RL
+ *   Infrastructure Behind MAI-Thinking-1", section 2, "Bitwise determinism").
+ * - Limits: 1 <= k <= min(E, 16); E <= 1024; d, L, F, Fs multiples of 64
+ *   (Fs may be 0 = no shared expert); T * k < 2^31.
+ * - Thread safety: calls from several host threads on different streams are
+ *   safe; the only library state is the per-thread profiling-event registry.
+ */
+#ifndef LATENT_MOE_H
+#define LATENT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define MOE_OK               0
+#define MOE_ERR_INVALID_ARG (-1)  /* null pointer, negative size, k < 1, k > E   */
+#define MOE_ERR_UNSUPPORTED (-2)  /* outside the limits above, misaligned pointer */
+#define MOE_ERR_WORKSPACE   (-3)  /* ws_bytes smaller than moe_workspace_bytes()  */
+#define MOE_ERR_HIP         (-4)  /* a HIP launch/record call failed             */
+
+/* ---- workspace query ops ----------------------------------------------- */
+#define MOE_OP_ROUTE       0
+#define MOE_OP_PERMUTE     1
+#define MOE_OP_LATENT_FFN  2
+#define MOE_OP_COMBINE     3
+
+/*
+ * Bytes of device workspace that the entry point `op` needs for these shapes
+ * (arguments an op does not use are ignored).  Returns 0 for an unknown op
+ * or invalid shapes.
+ *   ROUTE      : three bf16 parts of W_r (3*E*d*2) + fp32 logits (T*E*4)
+ *   PERMUTE    : per-chunk expert counts and bases (2 * ceil(T/256) * E * 4)
+ *   LATENT_FFN : z (T*L*2) + SwiGLU activations H (T*k*F*2) + tile tables
+ *   COMBINE    : combined latent c in bf16 (T*L*2)
+ */
+size_t moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t L, int32_t E,
+                           int32_t k, int32_t F, int32_t Fs);
+
+/* Human-readable text of a status code (static storage, never NULL).  For
+ * MOE_ERR_HIP it includes the HIP error of the last failure on this thread. */
+const char* moe_status_string(int status);
+
+/*
+ * Router: softmax gating over all E experts on the full hidden state, top-k.
+ * Defined by "The Training and RL Infrastructure Behind MAI-Thinking-1",
+ * model table (MoE row: softmax gating, 8 of 512 experts), the paragraph
+ * after it (the router sees the full hidden state), section 2 "Pre-training
+ * and mid-training precision" (router weights, routing GEMM and logits FP32)
+ * and section 2 "Bitwise determinism" (stable top-k).
+ *
+ *   x          [T, d]  bf16   hidden states (exact bf16 values)
+ *   w_router   [E, d]  fp32   router weights
+ *   b_router   [E]     fp32   per-expert bias added to the logits before the
+ *                             softmax (affects selection and weights); NULL = 0
+ *   topk_idx   [T, k]  int32  out: selected experts, by logit descending,
+ *                             equal logits -> lower expert index first
+ *   topk_w     [T, k]  fp32   out: softmax probability (over all E) of each
+ *                             selected expert; not renormalised over the k
+ *   logits_out [T, E]  fp32   out, optional (NULL): the FP32 logits
+ * The routing GEMM accumulates exact bf16 x bf16 products of x and a three-way
+ * bf16 split of W_r (hi + mid + lo == W_r exactly) in fp32.
+ */
+int moe_route(const uint16_t* x, const float* w_router, const float* b_router,
+              int64_t T, int32_t d, int32_t E, int32_t k,
+              int32_t* topk_idx, float* topk_w, float* logits_out,
+              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Permutation of the T*k (token, slot) assignments into expert order: a
+ * stable counting sort by expert ("expert encode", "The Training and RL
+ * Infrastructure Behind MAI-Thinking-1", section 3 "Custom kernels"; device-
+ * resident token metadata, "Frontier Pre-training at Microsoft AI", "Reducing
+ * per-expert overhead").  Integer-exact and deterministic.
+ *
+ *   topk_idx        [T, k]  int32  in: expert of each (t, j); the k experts of
+ *                                  one token must be distinct, each in [0, E)
+ *   expert_counts   [E]     int32  out: assignments per expert
+ *   expert_offsets  [E+1]   int32  out: exclusive prefix sum; [E] = T*k
+ *   row_token       [T*k]   int32  out: source token of each expert-ordered
+ *                                  row; ascending token order within an expert
+ *   assign_row      [T, k]  int32  out: row occupied by assignment (t, j)
+ */
+int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E,
+                int32_t* expert_counts, int32_t* expert_offsets,
+                int32_t* row_token, int32_t* assign_row,
+                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Latent down-projection and the routed SwiGLU experts as grouped GEMMs
+ * (plus, for a Base-2 layer, the shared expert's gate/up half).
+ * "The Training and RL Infrastructure Behind MAI-Thinking-1": model table
+ * (shared down-projection before dispatch; expert FFN; SwiGLU), section 3
+ * "Custom kernels" (grouped GEMMs for MoE); "MAI-Base-2: Microsoft's 2.8T
+ * base model...", section "The model" (shared expert not down/up projected).
+ *
+ *   x               [T, d]        bf16   hidden states
+ *   w_lat_down      [L, d]        bf16   W_dn
+ *   expert_offsets  [E+1]         int32  from moe_permute
+ *   row_token       [T*k]         int32  from moe_permute
+ *   w_gate, w_up    [E, F, L]     bf16   W_g, W_u of every routed expert
+ *   w_down          [E, L, F]     bf16   W_d of every routed expert
+ *   ws_gate, ws_up  [Fs, d]       bf16   shared expert (NULL when Fs == 0)
+ *   y_rows          [T*k, L]      fp32   out: expert outputs, expert order
+ *   hs              [T, Fs]       bf16   out: shared expert activation
+ *                                        silu(x Ws_g^T) * (x Ws_u^T); NULL when Fs == 0
+ * z and the SwiGLU activations are bf16 (MFMA operands); accumulation is fp32.
+ */
+int moe_latent_ffn_forward(const uint16_t* x, const uint16_t* w_lat_down,
+                           const int32_t* expert_offsets, const int32_t* row_token,
+                           const uint16_t* w_gate, const uint16_t* w_up,
+                           const uint16_t* w_down,
+                           const uint16_t* ws_gate, const uint16_t* ws_up,
+                           int64_t T, int32_t d, int32_t L, int32_t E, int32_t k,
+                           int32_t F, int32_t Fs,
+                           float* y_rows, uint16_t* hs,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Weighted combine in FP32 and up-projection back to the hidden width (plus
+ * the shared expert's down half).  "The Training and RL Infrastructure
+ * Behind MAI-Thinking-1", section 2 (MoE combine and residual stream FP32;
+ * fixed-order accumulation instead of atomics); "MAI-Base-2...", section
+ * "The model" (projected back up after the experts; shared expert added).
+ *
+ *   y_rows      [T*k, L]  fp32   from moe_latent_ffn_forward
+ *   topk_w      [T, k]    fp32   gate weights
+ *   assign_row  [T, k]    int32  from moe_permute
+ *   w_lat_up    [d, L]    bf16   W_up
+ *   hs          [T, Fs]   bf16   shared activation (NULL when Fs == 0)
+ *   ws_down     [d, Fs]   bf16   shared expert W_d (NULL when Fs == 0)
+ *   out         [T, d]    fp32   out: bf16(c) W_up^T + hs Ws_d^T
+ * c_t = sum_{j=0..k-1} w[t,j] y[assign_row[t,j]] is a gather in fixed j
+ * order (fp32), rounded to bf16 only as the up-projection's MFMA operand.
+ */
+int moe_combine(const float* y_rows, const float* topk_w, const int32_t* assign_row,
+                const uint16_t* w_lat_up, const uint16_t* hs, const uint16_t* ws_down,
+                int64_t T, int32_t d, int32_t L, int32_t k, int32_t Fs,
+                float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- profiling hook ------------------------------------------------------
+ * Register two hipEvent_t (created by the caller) that the library records on
+ * the call's stream immediately before and after every launch of `kernel`
+ * made by THIS host thread, until replaced; NULL, NULL clears.  Lets a caller
+ * time one kernel of the sequence with events on the stream it runs on.
+ * Returns MOE_ERR_INVALID_ARG for an unknown kernel id. */
+#define MOE_KERNEL_ROUTER_GEMM   0   /* routing GEMM (split-bf16 MFMA)          */
+#define MOE_KERNEL_ROUTER_TOPK   1   /* softmax + top-k                         */
+#define MOE_KERNEL_PERMUTE       2   /* histogram/scan/scatter (first..last)    */
+#define MOE_KERNEL_LATENT_DOWN   3   /* z = x W_dn^T (+ shared gate/up)         */
+#define MOE_KERNEL_GATE_UP       4   /* grouped gate/up GEMM + SwiGLU           */
+#define MOE_KERNEL_EXPERT_DOWN   5   /* grouped expert down GEMM                */
+#define MOE_KERNEL_COMBINE       6   /* weighted gather-combine                 */
+#define MOE_KERNEL_LATENT_UP     7   /* out = c W_up^T (+ shared down)          */
+#define MOE_KERNEL_COUNT         8
+int moe_set_kernel_events(int kernel, void* start_event, void* stop_event);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* LATENT_MOE_H */

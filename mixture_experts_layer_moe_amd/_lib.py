@@ -1,0 +1,170 @@
+"""Thin Python binding of libmoe (ctypes): argument marshalling only.
+
+Every function has the name and meaning of the C entry point in
+``include/moe.h``; tensors are torch tensors on the GPU, passed by data
+pointer, with shapes read from the tensors.  Every step of the layer runs in
+libmoe's HIP kernels; this module computes nothing.  It raises if the library
+has not been built (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+_lib = None
+
+MOE_OK = 0
+MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_LATENT_FFN, MOE_OP_COMBINE = 0, 1, 2, 3
+KERNELS = {"router_gemm": 0, "router_topk": 1, "permute": 2, "latent_down": 3, "gate_up": 4,
+           "expert_down": 5, "combine": 6, "latent_up": 7}
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} failed with status {code}: {moe_status_string(code)}")
+        self.code = code
+
+
+def load():
+    """Load libmoe.so (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built: run `python -m mixture_experts_layer_moe_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.moe_workspace_bytes.restype = _sz
+    lib.moe_workspace_bytes.argtypes = [ctypes.c_int, _i64, _i32, _i32, _i32, _i32, _i32, _i32]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_route.restype = ctypes.c_int
+    lib.moe_route.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.moe_permute.restype = ctypes.c_int
+    lib.moe_permute.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.moe_latent_ffn_forward.restype = ctypes.c_int
+    lib.moe_latent_ffn_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                                           _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
+                                           _vp]
+    lib.moe_combine.restype = ctypes.c_int
+    lib.moe_combine.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp,
+                                _vp, _sz, _vp]
+    lib.moe_set_kernel_events.restype = ctypes.c_int
+    lib.moe_set_kernel_events.argtypes = [ctypes.c_int, _vp, _vp]
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(fn, code):
+    if code != MOE_OK:
+        raise MoEError(fn, code)
+
+
+def _need(t, name, dtype, ndim=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def moe_workspace_bytes(op, T, d, L, E, k, F, Fs=0):
+    return int(load().moe_workspace_bytes(op, T, d, L, E, k, F, Fs))
+
+
+def moe_status_string(code):
+    return load().moe_status_string(code).decode()
+
+
+def moe_set_kernel_events(kernel, start_event, stop_event):
+    """Register raw hipEvent_t handles (ints) recorded around `kernel` (name or id)."""
+    kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    _check("moe_set_kernel_events", load().moe_set_kernel_events(kid, start_event, stop_event))
+
+
+def moe_route(x, w_router, b_router, k, topk_idx, topk_w, logits_out=None, ws=None, stream=None):
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_router, "w_router", torch.float32, 2)
+    _need(b_router, "b_router", torch.float32, 1)
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    _need(logits_out, "logits_out", torch.float32, 2)
+    _need(ws, "ws", torch.uint8, 1)
+    T, d = x.shape
+    E = w_router.shape[0]
+    _check("moe_route", load().moe_route(_ptr(x), _ptr(w_router), _ptr(b_router), T, d, E, k,
+                                         _ptr(topk_idx), _ptr(topk_w), _ptr(logits_out), _ptr(ws),
+                                         _nbytes(ws), _stream(stream)))
+
+
+def moe_permute(topk_idx, E, expert_counts, expert_offsets, row_token, assign_row, ws,
+                stream=None):
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    for n, t in (("expert_counts", expert_counts), ("expert_offsets", expert_offsets),
+                 ("row_token", row_token), ("assign_row", assign_row)):
+        _need(t, n, torch.int32)
+    _need(ws, "ws", torch.uint8, 1)
+    T, k = topk_idx.shape
+    _check("moe_permute", load().moe_permute(_ptr(topk_idx), T, k, E, _ptr(expert_counts),
+                                             _ptr(expert_offsets), _ptr(row_token),
+                                             _ptr(assign_row), _ptr(ws), _nbytes(ws),
+                                             _stream(stream)))
+
+
+def moe_latent_ffn_forward(x, w_lat_down, expert_offsets, row_token, w_gate, w_up, w_down,
+                           ws_gate, ws_up, k, y_rows, hs, ws, stream=None):
+    for n, t in (("x", x), ("w_lat_down", w_lat_down), ("w_gate", w_gate), ("w_up", w_up),
+                 ("w_down", w_down), ("ws_gate", ws_gate), ("ws_up", ws_up), ("hs", hs)):
+        _need(t, n, torch.bfloat16)
+    _need(expert_offsets, "expert_offsets", torch.int32, 1)
+    _need(row_token, "row_token", torch.int32, 1)
+    _need(y_rows, "y_rows", torch.float32, 2)
+    _need(ws, "ws", torch.uint8, 1)
+    T, d = x.shape
+    L = w_lat_down.shape[0]
+    E, F = w_gate.shape[0], w_gate.shape[1]
+    Fs = 0 if ws_gate is None else ws_gate.shape[0]
+    _check("moe_latent_ffn_forward", load().moe_latent_ffn_forward(
+        _ptr(x), _ptr(w_lat_down), _ptr(expert_offsets), _ptr(row_token), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), T, d, L, E, k, F, Fs, _ptr(y_rows),
+        _ptr(hs), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_combine(y_rows, topk_w, assign_row, w_lat_up, hs, ws_down, out, ws, stream=None):
+    _need(y_rows, "y_rows", torch.float32, 2)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    _need(assign_row, "assign_row", torch.int32, 2)
+    for n, t in (("w_lat_up", w_lat_up), ("hs", hs), ("ws_down", ws_down)):
+        _need(t, n, torch.bfloat16)
+    _need(out, "out", torch.float32, 2)
+    _need(ws, "ws", torch.uint8, 1)
+    T, k = topk_w.shape
+    d, L = w_lat_up.shape
+    Fs = 0 if ws_down is None else ws_down.shape[1]
+    _check("moe_combine", load().moe_combine(_ptr(y_rows), _ptr(topk_w), _ptr(assign_row),
+                                             _ptr(w_lat_up), _ptr(hs), _ptr(ws_down), T, d, L, k,
+                                             Fs, _ptr(out), _ptr(ws), _nbytes(ws),
+                                             _stream(stream)))

@@ -1,0 +1,140 @@
+// Latent down-projection and the routed SwiGLU experts as grouped bf16 MFMA
+// GEMMs ("The Training and RL Infrastructure Behind MAI-Thinking-1": model
+// table — shared down-projection before dispatch, expert FFN, SwiGLU;
+// section 3 "Custom kernels" — grouped GEMMs for MoE; "Frontier Pre-training
+// at Microsoft AI", "Reducing per-expert overhead" — grouped computation per
+// expert group, device-resident token metadata).  Also the Base-2 shared
+// expert's gate/up half, on the full hidden width ("MAI-Base-2: Microsoft's
+// 2.8T base model...", section "The model").
+#include "launch.hpp"
+#include "gemm.hpp"
+#include "scan.hpp"
+
+namespace moe {
+
+ExpertGemmPlan plan_expert_gemms(int64_t rows, int E) {
+  // Few rows per expert (small batches): a 128-row M tile usually holds an
+  // expert's rows in one tile, so each weight byte is streamed from HBM once
+  // while halving the MFMA work of a 256-row tile.  Otherwise 256 x 256.
+  const int64_t avg = rows / (E > 0 ? E : 1);
+  ExpertGemmPlan p;
+  p.bm_gate_up = avg <= 128 ? 128 : 256;
+  p.bm_down = p.bm_gate_up;
+  return p;
+}
+
+template <int BM, int BN, int EPI>
+static hipError_t dense_gemm(GemmArgs a, int64_t M, hipStream_t s) {
+  a.M = (int)M;
+  a.m_tiles = (int)ceil_div(M, BM);
+  a.n_tiles = (int)ceil_div(EPI == EPI_SWIGLU ? 2 * (int64_t)a.N : a.N, BN);
+  a.grid = (int)(ceil_div((int64_t)a.m_tiles * a.n_tiles, 8) * 8);
+  return launch_gemm<BM, BN, 2, 2, false, false, EPI>(a, s);
+}
+
+// Big tiles when they alone fill the chip, else 128 x 128.
+static bool use_big_tiles(int64_t M, int64_t N) {
+  return ceil_div(M, 256) * ceil_div(N, 256) >= 512;
+}
+
+hipError_t launch_latent_down(const uint16_t* x, const uint16_t* w_dn, int64_t T, int d, int L,
+                              uint16_t* z, hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = x; a.seg[0].lda = d; a.seg[0].B = w_dn; a.seg[0].ldb = d; a.seg[0].K = d;
+  a.nseg = 1;
+  a.N = L;
+  a.C = z;
+  a.ldc = L;
+  if (use_big_tiles(T, L)) return dense_gemm<256, 256, EPI_BF16>(a, T, s);
+  return dense_gemm<128, 128, EPI_BF16>(a, T, s);
+}
+
+hipError_t launch_shared_gate_up(const uint16_t* x, const uint16_t* wsg, const uint16_t* wsu,
+                                 int64_t T, int d, int Fs, uint16_t* hs, hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = x; a.seg[0].lda = d; a.seg[0].B = wsg; a.seg[0].B2 = wsu; a.seg[0].ldb = d;
+  a.seg[0].K = d;
+  a.nseg = 1;
+  a.N = Fs;
+  a.C = hs;
+  a.ldc = Fs;
+  if (use_big_tiles(T, 2 * (int64_t)Fs)) return dense_gemm<256, 256, EPI_SWIGLU>(a, T, s);
+  return dense_gemm<128, 128, EPI_SWIGLU>(a, T, s);
+}
+
+// Per-expert M-tile counts -> exclusive prefix (two tile heights at once).
+__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ offsets,
+                                                           int E, int bm_a, int bm_b,
+                                                           int32_t* __restrict__ pre_a,
+                                                           int32_t* __restrict__ pre_b) {
+  const int e = threadIdx.x;
+  int rows = 0;
+  if (e < E) rows = offsets[e + 1] - offsets[e];
+  int ta, tb;
+  const int ea = block_exclusive_scan(e < E ? (rows + bm_a - 1) / bm_a : 0, &ta);
+  const int eb = block_exclusive_scan(e < E ? (rows + bm_b - 1) / bm_b : 0, &tb);
+  if (e < E) {
+    pre_a[e] = ea;
+    pre_b[e] = eb;
+  }
+  if (e == 0) {
+    pre_a[E] = ta;
+    pre_b[E] = tb;
+  }
+}
+
+hipError_t launch_tile_prefix(const int32_t* offsets, int E, int bm_a, int bm_b, int32_t* pre_a,
+                              int32_t* pre_b, hipStream_t s) {
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm_a, bm_b, pre_a,
+                     pre_b);
+  return hipGetLastError();
+}
+
+template <int BM, bool GATHER, int EPI>
+static hipError_t grouped_gemm(GemmArgs a, int64_t rows, hipStream_t s) {
+  constexpr int BN = 256;
+  a.n_tiles = (int)ceil_div(EPI == EPI_SWIGLU ? 2 * (int64_t)a.N : a.N, BN);
+  int mt;
+  a.grid = grouped_grid(rows, a.E, BM, a.n_tiles, &mt);
+  return launch_gemm<BM, BN, 2, 2, true, GATHER, EPI>(a, s);
+}
+
+hipError_t launch_gate_up(const uint16_t* z, const int32_t* offsets, const int32_t* row_token,
+                          const int32_t* tile_prefix, const uint16_t* w_gate,
+                          const uint16_t* w_up, int64_t T, int64_t rows, int E, int L, int F,
+                          int bm, uint16_t* H, hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = z; a.seg[0].lda = L; a.seg[0].B = w_gate; a.seg[0].B2 = w_up; a.seg[0].ldb = L;
+  a.seg[0].K = L;
+  a.nseg = 1;
+  a.N = F;
+  a.offsets = offsets;
+  a.tile_prefix = tile_prefix;
+  a.E = E;
+  a.b_expert_stride = (int64_t)F * L;
+  a.row_token = row_token;
+  a.M = (int)T;   // rows of z, the gathered matrix
+  a.C = H;
+  a.ldc = F;
+  if (bm == 128) return grouped_gemm<128, true, EPI_SWIGLU>(a, rows, s);
+  return grouped_gemm<256, true, EPI_SWIGLU>(a, rows, s);
+}
+
+hipError_t launch_expert_down(const uint16_t* H, const int32_t* offsets,
+                              const int32_t* tile_prefix, const uint16_t* w_down, int64_t rows,
+                              int E, int L, int F, int bm, float* Y, hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = H; a.seg[0].lda = F; a.seg[0].B = w_down; a.seg[0].ldb = F; a.seg[0].K = F;
+  a.nseg = 1;
+  a.N = L;
+  a.offsets = offsets;
+  a.tile_prefix = tile_prefix;
+  a.E = E;
+  a.b_expert_stride = (int64_t)L * F;
+  a.C = Y;
+  a.ldc = L;
+  if (bm == 128) return grouped_gemm<128, false, EPI_F32>(a, rows, s);
+  return grouped_gemm<256, false, EPI_F32>(a, rows, s);
+}
+
+}  // namespace moe

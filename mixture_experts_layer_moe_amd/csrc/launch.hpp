@@ -1,0 +1,51 @@
+// Host-side launchers of libmoe's kernels (internal; the public C ABI is
+// include/moe.h).  Every launcher only enqueues on `s` and returns the HIP
+// error of its launches.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+// route.hip
+hipError_t launch_router_gemm(const uint16_t* x, const float* w_router, const float* bias,
+                              int64_t T, int d, int E, uint16_t* w3, float* logits,
+                              hipStream_t s);
+hipError_t launch_softmax_topk(const float* logits, int64_t T, int E, int k, int32_t* topk_idx,
+                               float* topk_w, hipStream_t s);
+
+// permute.hip
+constexpr int PERM_CHUNK = 256;   // tokens per permutation workgroup
+hipError_t launch_permute(const int32_t* topk_idx, int64_t T, int k, int E, int32_t* counts,
+                          int32_t* offsets, int32_t* row_token, int32_t* assign_row,
+                          int32_t* chunk_counts, int32_t* chunk_base, hipStream_t s);
+hipError_t launch_permute_empty(int E, int32_t* counts, int32_t* offsets, hipStream_t s);
+
+// expert.hip
+struct ExpertGemmPlan {
+  int bm_gate_up;    // M tile of the gate/up grouped GEMM
+  int bm_down;       // M tile of the down grouped GEMM
+};
+ExpertGemmPlan plan_expert_gemms(int64_t rows, int E);
+hipError_t launch_latent_down(const uint16_t* x, const uint16_t* w_dn, int64_t T, int d, int L,
+                              uint16_t* z, hipStream_t s);
+hipError_t launch_shared_gate_up(const uint16_t* x, const uint16_t* wsg, const uint16_t* wsu,
+                                 int64_t T, int d, int Fs, uint16_t* hs, hipStream_t s);
+hipError_t launch_tile_prefix(const int32_t* offsets, int E, int bm_a, int bm_b, int32_t* pre_a,
+                              int32_t* pre_b, hipStream_t s);
+hipError_t launch_gate_up(const uint16_t* z, const int32_t* offsets, const int32_t* row_token,
+                          const int32_t* tile_prefix, const uint16_t* w_gate,
+                          const uint16_t* w_up, int64_t T, int64_t rows, int E, int L, int F,
+                          int bm, uint16_t* H, hipStream_t s);
+hipError_t launch_expert_down(const uint16_t* H, const int32_t* offsets,
+                              const int32_t* tile_prefix, const uint16_t* w_down, int64_t rows,
+                              int E, int L, int F, int bm, float* Y, hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const float* y_rows, const float* topk_w, const int32_t* assign_row,
+                          int64_t T, int L, int k, uint16_t* c, hipStream_t s);
+hipError_t launch_latent_up(const uint16_t* c, const uint16_t* w_up, const uint16_t* hs,
+                            const uint16_t* wsd, int64_t T, int d, int L, int Fs, float* out,
+                            hipStream_t s);
+
+}  // namespace moe

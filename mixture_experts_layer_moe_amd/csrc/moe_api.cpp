@@ -1,0 +1,244 @@
+// The C ABI of libmoe (declared and documented in include/moe.h): argument
+// checks on the host, workspace carving, launches.  No allocation, no
+// synchronisation, no host reads of device data.
+#include "../../include/moe.h"
+
+#include <stdio.h>
+#include <string.h>
+
+#include "launch.hpp"
+
+using namespace moe;
+
+namespace {
+
+thread_local hipError_t g_last_hip = hipSuccess;
+thread_local char g_msg[256];
+thread_local hipEvent_t g_events[K_COUNT][2];
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip = e;
+  return MOE_ERR_HIP;
+}
+
+bool dims_ok(int64_t v) { return v > 0 && v % 64 == 0 && v <= (1 << 20); }
+
+// Workspace layouts (byte offsets, each 256-aligned).
+struct RouteWs { size_t w3, logits, total; };
+RouteWs route_ws(int64_t T, int d, int E) {
+  RouteWs w;
+  w.w3 = 0;
+  w.logits = align_up((size_t)3 * E * d * 2);
+  w.total = w.logits + align_up((size_t)T * E * 4);
+  return w;
+}
+struct PermWs { size_t counts, base, total; };
+PermWs perm_ws(int64_t T, int E) {
+  const size_t nch = (size_t)ceil_div(T, PERM_CHUNK);
+  PermWs w;
+  w.counts = 0;
+  w.base = align_up(nch * E * 4);
+  w.total = w.base + align_up(nch * E * 4);
+  return w;
+}
+struct FfnWs { size_t z, h, pre_a, pre_b, total; };
+FfnWs ffn_ws(int64_t T, int L, int E, int k, int F) {
+  FfnWs w;
+  w.z = 0;
+  w.h = align_up((size_t)T * L * 2);
+  w.pre_a = w.h + align_up((size_t)T * k * F * 2);
+  w.pre_b = w.pre_a + align_up((size_t)(E + 1) * 4);
+  w.total = w.pre_b + align_up((size_t)(E + 1) * 4);
+  return w;
+}
+size_t combine_ws(int64_t T, int L) { return align_up((size_t)T * L * 2); }
+
+int check_route_dims(int64_t T, int d, int E, int k) {
+  if (T < 0 || d <= 0 || E <= 0 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (k > 16 || E > 1024 || !dims_ok(d)) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)k >= (int64_t(1) << 31) || T * (int64_t)E >= (int64_t(1) << 40))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+namespace moe {
+EventScope::EventScope(int id_, hipStream_t s_) : s(s_), id(id_) {
+  if (g_events[id][0]) hipEventRecord(g_events[id][0], s);
+}
+EventScope::~EventScope() {
+  if (g_events[id][1]) hipEventRecord(g_events[id][1], s);
+}
+}  // namespace moe
+
+extern "C" {
+
+size_t moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t L, int32_t E, int32_t k,
+                           int32_t F, int32_t Fs) {
+  (void)Fs;
+  if (T < 0 || E <= 0 || k < 1) return 0;
+  switch (op) {
+    case MOE_OP_ROUTE: return d > 0 ? route_ws(T, d, E).total : 0;
+    case MOE_OP_PERMUTE: return perm_ws(T, E).total;
+    case MOE_OP_LATENT_FFN: return (L > 0 && F > 0) ? ffn_ws(T, L, E, k, F).total : 0;
+    case MOE_OP_COMBINE: return L > 0 ? combine_ws(T, L) : 0;
+    default: return 0;
+  }
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size, k < 1 or k > E)";
+    case MOE_ERR_UNSUPPORTED:
+      return "unsupported (k > 16, E > 1024, a width not a positive multiple of 64, "
+             "T*k >= 2^31, or a pointer not 16-byte aligned)";
+    case MOE_ERR_WORKSPACE: return "workspace too small (see moe_workspace_bytes)";
+    case MOE_ERR_HIP:
+      snprintf(g_msg, sizeof g_msg, "HIP error: %s", hipGetErrorString(g_last_hip));
+      return g_msg;
+    default: return "unknown status";
+  }
+}
+
+int moe_set_kernel_events(int kernel, void* start_event, void* stop_event) {
+  if (kernel < 0 || kernel >= K_COUNT) return MOE_ERR_INVALID_ARG;
+  g_events[kernel][0] = (hipEvent_t)start_event;
+  g_events[kernel][1] = (hipEvent_t)stop_event;
+  return MOE_OK;
+}
+
+int moe_route(const uint16_t* x, const float* w_router, const float* b_router, int64_t T,
+              int32_t d, int32_t E, int32_t k, int32_t* topk_idx, float* topk_w,
+              float* logits_out, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_route_dims(T, d, E, k);
+  if (st) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_idx || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(ws) ||
+      (logits_out && !aligned16(logits_out)))
+    return MOE_ERR_UNSUPPORTED;
+  const RouteWs w = route_ws(T, d, E);
+  if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  float* logits = logits_out ? logits_out : (float*)(base + w.logits);
+  {
+    EventScope ev(K_ROUTER_GEMM, s);
+    st = hip_status(launch_router_gemm(x, w_router, b_router, T, d, E, (uint16_t*)(base + w.w3),
+                                       logits, s));
+  }
+  if (st) return st;
+  EventScope ev(K_ROUTER_TOPK, s);
+  return hip_status(launch_softmax_topk(logits, T, E, k, topk_idx, topk_w, s));
+}
+
+int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t* expert_counts,
+                int32_t* expert_offsets, int32_t* row_token, int32_t* assign_row, void* ws,
+                size_t ws_bytes, void* stream) {
+  if (T < 0 || E <= 0 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (k > 16 || E > 1024 || T * (int64_t)k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_idx || !row_token || !assign_row || !ws)) return MOE_ERR_INVALID_ARG;
+  const PermWs w = perm_ws(T, E);
+  if (T > 0 && ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  EventScope ev(K_PERMUTE, s);
+  if (T == 0) {
+    // an empty batch still defines the metadata: all counts and offsets zero
+    // (a fill kernel, not hipMemsetAsync, so the call stays graph-capturable)
+    return hip_status(launch_permute_empty(E, expert_counts, expert_offsets, s));
+  }
+  char* base = (char*)ws;
+  return hip_status(launch_permute(topk_idx, T, k, E, expert_counts, expert_offsets, row_token,
+                                   assign_row, (int32_t*)(base + w.counts),
+                                   (int32_t*)(base + w.base), s));
+}
+
+int moe_latent_ffn_forward(const uint16_t* x, const uint16_t* w_lat_down,
+                           const int32_t* expert_offsets, const int32_t* row_token,
+                           const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                           const uint16_t* ws_gate, const uint16_t* ws_up, int64_t T, int32_t d,
+                           int32_t L, int32_t E, int32_t k, int32_t F, int32_t Fs,
+                           float* y_rows, uint16_t* hs, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (T < 0 || E <= 0 || k < 1 || k > E || Fs < 0) return MOE_ERR_INVALID_ARG;
+  if (k > 16 || E > 1024 || !dims_ok(d) || !dims_ok(L) || !dims_ok(F) ||
+      (Fs > 0 && !dims_ok(Fs)) || T * (int64_t)k >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_lat_down || !expert_offsets || !row_token || !w_gate || !w_up || !w_down ||
+      !y_rows || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (Fs > 0 && (!ws_gate || !ws_up || !hs)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, w_lat_down, w_gate, w_up, w_down, y_rows, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  if (Fs > 0 && (!aligned16(ws_gate) || !aligned16(ws_up) || !aligned16(hs)))
+    return MOE_ERR_UNSUPPORTED;
+  const FfnWs w = ffn_ws(T, L, E, k, F);
+  if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  uint16_t* z = (uint16_t*)(base + w.z);
+  uint16_t* H = (uint16_t*)(base + w.h);
+  int32_t* pre_a = (int32_t*)(base + w.pre_a);
+  int32_t* pre_b = (int32_t*)(base + w.pre_b);
+  const int64_t rows = T * k;
+  const ExpertGemmPlan plan = plan_expert_gemms(rows, E);
+  int st;
+  {
+    EventScope ev(K_LATENT_DOWN, s);
+    st = hip_status(launch_latent_down(x, w_lat_down, T, d, L, z, s));
+    if (!st && Fs > 0) st = hip_status(launch_shared_gate_up(x, ws_gate, ws_up, T, d, Fs, hs, s));
+  }
+  if (st) return st;
+  st = hip_status(launch_tile_prefix(expert_offsets, E, plan.bm_gate_up, plan.bm_down, pre_a,
+                                     pre_b, s));
+  if (st) return st;
+  {
+    EventScope ev(K_GATE_UP, s);
+    st = hip_status(launch_gate_up(z, expert_offsets, row_token, pre_a, w_gate, w_up, T, rows, E,
+                                   L, F, plan.bm_gate_up, H, s));
+  }
+  if (st) return st;
+  EventScope ev(K_EXPERT_DOWN, s);
+  return hip_status(launch_expert_down(H, expert_offsets, pre_b, w_down, rows, E, L, F,
+                                       plan.bm_down, y_rows, s));
+}
+
+int moe_combine(const float* y_rows, const float* topk_w, const int32_t* assign_row,
+                const uint16_t* w_lat_up, const uint16_t* hs, const uint16_t* ws_down, int64_t T,
+                int32_t d, int32_t L, int32_t k, int32_t Fs, float* out, void* ws,
+                size_t ws_bytes, void* stream) {
+  if (T < 0 || k < 1 || Fs < 0) return MOE_ERR_INVALID_ARG;
+  if (k > 16 || !dims_ok(d) || !dims_ok(L) || (Fs > 0 && !dims_ok(Fs)) ||
+      T * (int64_t)k >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y_rows || !topk_w || !assign_row || !w_lat_up || !out || !ws) return MOE_ERR_INVALID_ARG;
+  if (Fs > 0 && (!hs || !ws_down)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_rows) || !aligned16(w_lat_up) || !aligned16(out) || !aligned16(ws) ||
+      (Fs > 0 && (!aligned16(hs) || !aligned16(ws_down))))
+    return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < combine_ws(T, L)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t* c = (uint16_t*)ws;
+  int st;
+  {
+    EventScope ev(K_COMBINE, s);
+    st = hip_status(launch_combine(y_rows, topk_w, assign_row, T, L, k, c, s));
+  }
+  if (st) return st;
+  EventScope ev(K_LATENT_UP, s);
+  return hip_status(launch_latent_up(c, w_lat_up, hs, ws_down, T, d, L, Fs, out, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+"""One LatentMoE forward pass through libmoe's four entry points.
+
+``LatentMoEBuffers`` allocates (with torch, once) every output and workspace
+buffer a forward pass of a given shape needs; ``forward`` then only enqueues
+moe_route -> moe_permute -> moe_latent_ffn_forward -> moe_combine on one
+stream.  Buffer sizes depend only on the shapes (fixed memory, dropless).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+from . import _lib
+
+
+@dataclasses.dataclass
+class LatentMoEWeights:
+    w_router: torch.Tensor            # [E, d] fp32
+    b_router: torch.Tensor | None     # [E] fp32
+    w_lat_down: torch.Tensor          # [L, d] bf16
+    w_gate: torch.Tensor              # [E, F, L] bf16
+    w_up: torch.Tensor                # [E, F, L] bf16
+    w_down: torch.Tensor              # [E, L, F] bf16
+    w_lat_up: torch.Tensor            # [d, L] bf16
+    ws_gate: torch.Tensor | None = None   # [Fs, d] bf16
+    ws_up: torch.Tensor | None = None     # [Fs, d] bf16
+    ws_down: torch.Tensor | None = None   # [d, Fs] bf16
+
+    @property
+    def dims(self):
+        E, F, L = self.w_gate.shape
+        d = self.w_lat_up.shape[0]
+        Fs = 0 if self.ws_gate is None else self.ws_gate.shape[0]
+        return d, L, E, F, Fs
+
+
+class LatentMoEBuffers:
+    def __init__(self, T, d, L, E, k, F, Fs=0, device="cuda"):
+        self.T, self.d, self.L, self.E, self.k, self.F, self.Fs = T, d, L, E, k, F, Fs
+        dev = torch.device(device)
+        i32, f32 = torch.int32, torch.float32
+        self.topk_idx = torch.empty((T, k), dtype=i32, device=dev)
+        self.topk_w = torch.empty((T, k), dtype=f32, device=dev)
+        self.expert_counts = torch.empty(E, dtype=i32, device=dev)
+        self.expert_offsets = torch.empty(E + 1, dtype=i32, device=dev)
+        self.row_token = torch.empty(T * k, dtype=i32, device=dev)
+        self.assign_row = torch.empty((T, k), dtype=i32, device=dev)
+        self.y_rows = torch.empty((T * k, L), dtype=f32, device=dev)
+        self.hs = torch.empty((T, Fs), dtype=torch.bfloat16, device=dev) if Fs else None
+        self.out = torch.empty((T, d), dtype=f32, device=dev)
+        nb = max(_lib.moe_workspace_bytes(op, T, d, L, E, k, F, Fs) for op in range(4))
+        # one workspace reused by the four calls (they run in order on one stream)
+        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+
+
+def forward(x, w: LatentMoEWeights, k, buf: LatentMoEBuffers, stream=None, route=True):
+    """Enqueue one forward pass; results land in ``buf`` (buf.out is [T, d] fp32).
+    With route=False the caller's buf.topk_idx / buf.topk_w are used (router replay)."""
+    if route:
+        _lib.moe_route(x, w.w_router, w.b_router, k, buf.topk_idx, buf.topk_w, ws=buf.ws,
+                       stream=stream)
+    _lib.moe_permute(buf.topk_idx, buf.E, buf.expert_counts, buf.expert_offsets, buf.row_token,
+                     buf.assign_row, buf.ws, stream=stream)
+    _lib.moe_latent_ffn_forward(x, w.w_lat_down, buf.expert_offsets, buf.row_token, w.w_gate,
+                                w.w_up, w.w_down, w.ws_gate, w.ws_up, k, buf.y_rows, buf.hs,
+                                buf.ws, stream=stream)
+    _lib.moe_combine(buf.y_rows, buf.topk_w, buf.assign_row, w.w_lat_up, buf.hs, w.ws_down,
+                     buf.out, buf.ws, stream=stream)
+    return buf.out

@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point that include/moe.h declares, sizes workspaces as documented
+and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_moe_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib.load()
+    names = declared_functions()
+    assert {"moe_route", "moe_permute", "moe_latent_ffn_forward", "moe_combine",
+            "moe_workspace_bytes", "moe_status_string", "moe_set_kernel_events"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(_lib.moe_status_string(code), str)
+    assert "workspace" in _lib.moe_status_string(-3)
+
+
+def test_workspace_sizes():
+    a = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    T, d, L, E, k, F = 4096, 6656, 3072, 512, 8, 10240
+    assert _lib.moe_workspace_bytes(0, T, d, L, E, k, F) == a(3 * E * d * 2) + a(T * E * 4)
+    assert _lib.moe_workspace_bytes(1, T, d, L, E, k, F) == 2 * a(16 * E * 4)
+    assert _lib.moe_workspace_bytes(2, T, d, L, E, k, F) == \
+        a(T * L * 2) + a(T * k * F * 2) + 2 * a((E + 1) * 4)
+    assert _lib.moe_workspace_bytes(3, T, d, L, E, k, F) == a(T * L * 2)
+    assert _lib.moe_workspace_bytes(9, T, d, L, E, k, F) == 0
+    assert _lib.moe_workspace_bytes(0, -1, d, L, E, k, F) == 0
+
+
+def test_kernel_event_ids():
+    lib = _lib.load()
+    assert lib.moe_set_kernel_events(8, None, None) == -1
+    assert lib.moe_set_kernel_events(-1, None, None) == -1
+    assert lib.moe_set_kernel_events(4, None, None) == 0
+
+
+P = 1 << 20   # a 16-byte aligned fake device address; never dereferenced on these paths
+
+
+@pytest.mark.parametrize("T,d,E,k,want", [
+    (-1, 512, 16, 2, -1), (8, 512, 16, 0, -1), (8, 512, 16, 17, -1), (8, 512, 0, 1, -1),
+    (8, 512, 32, 17, -2), (8, 512, 2048, 8, -2), (8, 500, 16, 2, -2), (8, 0, 16, 2, -1),
+])
+def test_route_rejects_bad_shapes(T, d, E, k, want):
+    lib = _lib.load()
+    assert lib.moe_route(P, P, None, T, d, E, k, P, P, None, P, 1 << 40, None) == want
+
+
+def test_route_rejects_null_misaligned_and_small_workspace():
+    lib = _lib.load()
+    assert lib.moe_route(None, P, None, 8, 512, 16, 2, P, P, None, P, 1 << 40, None) == -1
+    assert lib.moe_route(P, P, None, 8, 512, 16, 2, None, P, None, P, 1 << 40, None) == -1
+    assert lib.moe_route(P + 2, P, None, 8, 512, 16, 2, P, P, None, P, 1 << 40, None) == -2
+    need = _lib.moe_workspace_bytes(0, 8, 512, 0, 16, 2, 0)
+    assert lib.moe_route(P, P, None, 8, 512, 16, 2, P, P, None, P, need - 1, None) == -3
+    # T == 0 is a no-op success (nothing launched)
+    assert lib.moe_route(P, P, None, 0, 512, 16, 2, P, P, None, P, 0, None) == 0
+
+
+def test_permute_rejects_bad_args():
+    lib = _lib.load()
+    assert lib.moe_permute(P, 8, 0, 16, P, P, P, P, P, 1 << 30, None) == -1
+    assert lib.moe_permute(P, 8, 4, 2, P, P, P, P, P, 1 << 30, None) == -1
+    assert lib.moe_permute(P, 8, 2, 2048, P, P, P, P, P, 1 << 30, None) == -2
+    assert lib.moe_permute(P, 8, 2, 16, None, P, P, P, P, 1 << 30, None) == -1
+    assert lib.moe_permute(P, 8, 2, 16, P, P, P, P, P, 10, None) == -3
+    assert lib.moe_permute(P, (1 << 31) // 8, 8, 16, P, P, P, P, P, 1 << 40, None) == -2
+
+
+def _ffn(lib, T=8, d=512, L=256, E=16, k=2, F=512, Fs=0, x=P, wsb=1 << 40, hs=None, wsg=None):
+    return lib.moe_latent_ffn_forward(x, P, P, P, P, P, P, wsg, wsg, T, d, L, E, k, F, Fs, P, hs,
+                                      P, wsb, None)
+
+
+def test_latent_ffn_rejects_bad_args():
+    lib = _lib.load()
+    assert _ffn(lib, L=200) == -2
+    assert _ffn(lib, F=0) == -2
+    assert _ffn(lib, Fs=-64) == -1
+    assert _ffn(lib, Fs=128) == -1            # shared widths without shared pointers
+    assert _ffn(lib, x=None) == -1
+    assert _ffn(lib, x=P + 8) == -2
+    assert _ffn(lib, wsb=100) == -3
+    assert _ffn(lib, T=0) == 0
+
+
+def test_combine_rejects_bad_args():
+    lib = _lib.load()
+    assert lib.moe_combine(P, P, P, P, None, None, 8, 512, 256, 0, 0, P, P, 1 << 30, None) == -1
+    assert lib.moe_combine(P, P, P, P, None, None, 8, 500, 256, 2, 0, P, P, 1 << 30, None) == -2
+    assert lib.moe_combine(P, P, P, P, None, None, 8, 512, 256, 2, 64, P, P, 1 << 30, None) == -1
+    assert lib.moe_combine(P, P, P, P, None, None, 8, 512, 256, 2, 0, P, P, 16, None) == -3
+    assert lib.moe_combine(None, P, P, P, None, None, 8, 512, 256, 2, 0, P, P, 1 << 30, None) == -1
+    assert lib.moe_combine(P, P, P, P, None, None, 0, 512, 256, 2, 0, P, P, 0, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.load()

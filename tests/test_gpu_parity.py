@@ -1,0 +1,215 @@
+"""GPU parity of libmoe's four entry points against the CPU oracle.
+
+Inputs are seeded synthetic tensors from moe_synth (identical bytes on host
+and device).  Sizes span several tiles and ragged tails yet keep the float64
+oracle to seconds.  The comparison rules are those of tests/gpu_util.py:
+routing exact up to near-ties (oracle logit gap < 1e-4), gate weights to
+1e-5 relative, permutation arrays bit-exact, outputs max|err|/RMS <= 2e-2
+against the bf16-operand oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_moe_amd as moe
+from moe_synth import CONFIGS, MoEConfig, device, gen
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny": CONFIGS["tiny"],
+    # ragged everywhere: T, L and F tails inside a tile, E not a tile multiple
+    "ragged": MoEConfig("ragged", T=300, d=320, L=192, E=24, k=3, F=320, seed=3),
+    # Base-2 structure at a small size: top-7 plus a shared expert
+    "shared": MoEConfig("shared", T=200, d=512, L=256, E=32, k=7, F=384, Fs=640, seed=5),
+    # the ABI limits: E = 1024, k = 16
+    "wide": MoEConfig("wide", T=130, d=256, L=128, E=1024, k=16, F=128, seed=7),
+    # few experts with many rows each: several M tiles per expert
+    "deep": MoEConfig("deep", T=2048, d=256, L=256, E=8, k=2, F=512, seed=9),
+    # Zipf-like router bias: hot experts and empty experts
+    "zipf": MoEConfig("zipf", T=1024, d=256, L=128, E=64, k=4, F=256, zipf_bias=True, seed=11),
+}
+
+
+@pytest.fixture(scope="module")
+def cuda():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.load()
+    return torch.device("cuda:0")
+
+
+_cache = {}
+
+
+def setup_case(name, dev):
+    if name in _cache:
+        return _cache[name]
+    cfg = CASES[name]
+    U.log(f"[case {name}] {cfg}")
+    host = gen.host_inputs_f64(cfg)
+    dv = device.device_inputs(cfg, dev)
+    torch.cuda.synchronize()
+    _cache[name] = (cfg, host, dv)
+    return _cache[name]
+
+
+def weights_of(dv):
+    return moe.LatentMoEWeights(dv["w_router"], dv["b_router"], dv["w_dn"], dv["w_gate"],
+                                dv["w_up"], dv["w_down"], dv["w_lat_up"], dv.get("ws_gate"),
+                                dv.get("ws_up"), dv.get("ws_down"))
+
+
+def test_synthetic_inputs_identical_on_device(cuda):
+    cfg = CASES["ragged"]
+    for name in gen.tensor_specs(cfg):
+        t = device.device_tensor(cfg, name, cuda)
+        got = t.view(torch.int16).cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(got, gen.host_tensor_bits(cfg, name), err_msg=name)
+    # a slice far into a large tensor (high counter word in use)
+    big = CONFIGS["base1_small_batch"]
+    start = 511 * 10240 * 3072 + 12345
+    t = torch.empty(4096, dtype=torch.bfloat16, device=cuda)
+    device.fill_(t, big, "w_gate", start=start)
+    want = gen.normal_bf16_bits(gen.tensor_key(big.seed, gen.TID["w_gate"]), 3072 ** -0.5, start, 4096)
+    np.testing.assert_array_equal(t.view(torch.int16).cpu().numpy().view(np.uint16), want)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_route(cuda, name):
+    cfg, host, dv = setup_case(name, cuda)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    idx = torch.empty((T, k), dtype=torch.int32, device=cuda)
+    w = torch.empty((T, k), dtype=torch.float32, device=cuda)
+    logits = torch.empty((T, E), dtype=torch.float32, device=cuda)
+    ws = torch.empty(moe.moe_workspace_bytes(0, T, cfg.d, 0, E, k, 0), dtype=torch.uint8, device=cuda)
+    moe.moe_route(dv["x"], dv["w_router"], dv["b_router"], k, idx, w, logits_out=logits, ws=ws)
+    torch.cuda.synchronize()
+    import oracle
+    ro = oracle.route(host["x"], host["w_router"], host["b_router"], k)
+    lerr = np.abs(U.to_np(logits) - ro["logits"]).max()
+    U.log(f"[{name}] max |logit err| = {lerr:.3e}")
+    assert lerr < 1e-5
+    swaps = U.routing_swaps(U.to_np(idx), ro["topk_idx"], ro["logits"])
+    wr = U.check_topk_w(U.to_np(idx), U.to_np(w), ro["probs"])
+    U.log(f"[{name}] near-tie swaps: {len(swaps)} tokens; topk_w max rel err {wr:.2e}")
+    assert len(swaps) <= max(2, T // 200)
+
+
+PERM_CASES = [
+    ("tiny", 256, 16, 2, "random"), ("one", 1, 4, 1, "random"), ("chunk-1", 255, 32, 4, "random"),
+    ("chunk", 256, 32, 4, "random"), ("chunk+1", 257, 32, 4, "random"),
+    ("limits", 700, 1024, 16, "random"), ("hot", 3000, 64, 4, "hot"),
+    ("base1", 4096, 512, 8, "random"), ("sparse", 1000, 512, 2, "few"),
+]
+
+
+@pytest.mark.parametrize("case", PERM_CASES, ids=[c[0] for c in PERM_CASES])
+def test_permute_bit_exact(cuda, case):
+    import oracle
+    name, T, E, k, kind = case
+    U.log(f"[permute {name}] T={T} E={E} k={k} {kind}")
+    r = np.random.default_rng(T * 7 + E)
+    if kind == "hot":
+        idx = np.tile(np.arange(E - k, E), (T, 1))
+        idx[::3] = np.arange(k)
+    elif kind == "few":      # only 5 experts ever used
+        idx = np.stack([r.permutation(5)[:k] for _ in range(T)]) * 100
+    else:
+        idx = np.stack([r.permutation(E)[:k] for _ in range(T)])
+    idx = idx.astype(np.int32)
+    want = oracle.permute(idx, E)
+    t_idx = torch.from_numpy(idx).to(cuda)
+    counts = torch.full((E,), -7, dtype=torch.int32, device=cuda)
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=cuda)
+    row_token = torch.full((T * k,), -7, dtype=torch.int32, device=cuda)
+    assign_row = torch.full((T, k), -7, dtype=torch.int32, device=cuda)
+    ws = torch.empty(moe.moe_workspace_bytes(1, T, 64, 64, E, k, 64), dtype=torch.uint8, device=cuda)
+    moe.moe_permute(t_idx, E, counts, offsets, row_token, assign_row, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(U.to_np(counts), want["expert_counts"])
+    np.testing.assert_array_equal(U.to_np(offsets), want["expert_offsets"])
+    np.testing.assert_array_equal(U.to_np(row_token), want["row_token"])
+    np.testing.assert_array_equal(U.to_np(assign_row), want["assign_row"])
+
+
+def test_permute_empty_batch(cuda):
+    E = 16
+    counts = torch.full((E,), -7, dtype=torch.int32, device=cuda)
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=cuda)
+    dummy = torch.empty(16, dtype=torch.int32, device=cuda)
+    idx = torch.empty((0, 2), dtype=torch.int32, device=cuda)
+    moe.moe_permute(idx, E, counts, offsets, dummy, dummy, None)
+    torch.cuda.synchronize()
+    assert (counts == 0).all() and (offsets == 0).all()
+
+
+def _replayed_buffers(cfg, dv, ro, cuda):
+    """Buffers whose routing is the oracle's (router replay through the ABI)."""
+    buf = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, cfg.Fs, device=cuda)
+    buf.topk_idx.copy_(torch.from_numpy(np.asarray(ro["topk_idx"], np.int32)))
+    buf.topk_w.copy_(torch.from_numpy(np.asarray(ro["topk_w"], np.float32)))
+    return buf
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layer_with_oracle_routing(cuda, name):
+    """Permute + experts + combine on the oracle's routing (router replay)."""
+    cfg, host, dv = setup_case(name, cuda)
+    ro = U.oracle_forward(cfg, host, "bf16_operands")
+    # the GPU gets the fp32 gate weights; the oracle uses the same fp32 values
+    w32 = np.asarray(ro["topk_w"], np.float32).astype(np.float64)
+    ro = U.oracle_forward(cfg, host, "bf16_operands", routing=(ro["topk_idx"], w32))
+    ex = U.oracle_forward(cfg, host, "exact", routing=(ro["topk_idx"], w32))
+    buf = _replayed_buffers(cfg, dv, ro, cuda)
+    moe.forward(dv["x"], weights_of(dv), cfg.k, buf, route=False)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(U.to_np(buf.expert_offsets), ro["expert_offsets"])
+    np.testing.assert_array_equal(U.to_np(buf.row_token), ro["row_token"])
+    np.testing.assert_array_equal(U.to_np(buf.assign_row), ro["assign_row"])
+    ey = U.rel_err(U.to_np(buf.y_rows), ro["y_rows"])
+    eo = U.rel_err(U.to_np(buf.out), ro["out"])
+    ee = U.rel_err(U.to_np(buf.out), ex["out"])
+    U.log(f"[{name}] y_rows err max/rms {ey[0]:.2e}/{ey[1]:.2e}; out vs bf16-operand oracle "
+          f"{eo[0]:.2e}/{eo[1]:.2e}; vs exact {ee[0]:.2e}/{ee[1]:.2e}")
+    assert ey[0] <= U.OUT_TOL
+    assert eo[0] <= U.OUT_TOL
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_end_to_end(cuda, name):
+    """The whole path, router included, against the oracle's own routing."""
+    cfg, host, dv = setup_case(name, cuda)
+    ro = U.oracle_forward(cfg, host, "bf16_operands")
+    buf = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, cfg.Fs, device=cuda)
+    moe.forward(dv["x"], weights_of(dv), cfg.k, buf)
+    torch.cuda.synchronize()
+    gidx = U.to_np(buf.topk_idx)
+    swaps = U.routing_swaps(gidx, ro["topk_idx"], ro["logits"])
+    U.check_topk_w(gidx, U.to_np(buf.topk_w), ro["probs"])
+    if len(swaps) == 0:
+        np.testing.assert_array_equal(U.to_np(buf.expert_offsets), ro["expert_offsets"])
+        np.testing.assert_array_equal(U.to_np(buf.row_token), ro["row_token"])
+        np.testing.assert_array_equal(U.to_np(buf.assign_row), ro["assign_row"])
+    else:
+        U.check_perm_valid(gidx, cfg.E, U.to_np(buf.expert_counts), U.to_np(buf.expert_offsets),
+                           U.to_np(buf.row_token), U.to_np(buf.assign_row))
+    keep = np.setdiff1d(np.arange(cfg.T), swaps)
+    eo = U.rel_err(U.to_np(buf.out)[keep], ro["out"][keep])
+    U.log(f"[{name}] e2e: swaps {len(swaps)}; out err max/rms {eo[0]:.2e}/{eo[1]:.2e}")
+    assert eo[0] <= U.OUT_TOL
+
+
+def test_bitwise_determinism(cuda):
+    cfg, host, dv = setup_case("shared", cuda)
+    outs = []
+    for _ in range(3):
+        buf = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, cfg.Fs, device=cuda)
+        moe.forward(dv["x"], weights_of(dv), cfg.k, buf)
+        torch.cuda.synchronize()
+        outs.append([buf.topk_idx.cpu(), buf.topk_w.cpu(), buf.row_token.cpu(), buf.y_rows.cpu(),
+                     buf.out.cpu()])
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                               b.view(torch.int32) if b.dtype == torch.float32 else b)
