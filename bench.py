@@ -1,0 +1,287 @@
+"""LatentMoE layer forward throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+
+One step = one forward pass of the whole layer (moe_route -> moe_permute ->
+moe_latent_ffn_forward -> moe_combine, every stage a libmoe HIP kernel) over
+one batch of seeded synthetic input already resident in HBM.  Prints one JSON
+line: tokens/s of the timed steps, the roofline of the dominant kernel (the
+grouped gate/up GEMM) measured with HIP events recorded by the library around
+that kernel on the stream it runs on, per-kernel average times, and the CPU
+oracle timed on a bounded sample of the same workload.
+
+Default workload: the MAI-Base-1-shaped layer at T=4,096 tokens (d=6,656,
+latent 3,072, 512 experts, top-8, SwiGLU width 10,240; bf16 operands, fp32
+accumulation), all 512 experts resident (~97 GB of expert weights).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+MFMA_BF16_PEAK = 2.5e15    # MI355X dense bf16 MFMA, FLOP/s
+METRIC = "LatentMoE layer fwd tokens/sec on 1 MI355X; % bf16 MFMA peak / % HBM BW"
+KERNEL_NAMES = ["router_gemm", "router_topk", "permute", "latent_down", "gate_up",
+                "expert_down", "combine", "latent_up"]
+DOMINANT = "gate_up"
+# Sources that define the dominant kernel; stored counter readings are only
+# valid for the code they were taken on.
+DOMINANT_SOURCES = ["mixture_experts_layer_moe_amd/csrc/gemm.hpp",
+                    "mixture_experts_layer_moe_amd/csrc/expert.hip"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="base1_small_batch")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain device copy of known size (for HBM counter scaling)")
+    return p.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch has loaded (same process runtime)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        assert rc == 0, f"hipEventElapsedTime rc={rc}"
+        return ms.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    for rel in DOMINANT_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(config_name):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3
+    counter readings, if they were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{DOMINANT}_{config_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("sources_sha256_16") != sources_digest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def dominant_work(cfg, counts):
+    """Algorithmic FLOPs and bytes of one launch of the grouped gate/up GEMM:
+    2 GEMMs of 2*rows*L*F FLOPs; bytes = gate+up weights of every expert that
+    received a row (each read once) + the gathered latent rows (bf16) + H out."""
+    import numpy as np
+    touched = int(np.count_nonzero(counts))
+    rows = cfg.T * cfg.k
+    flops = 4.0 * rows * cfg.L * cfg.F
+    nbytes = touched * 2.0 * cfg.F * cfg.L * 2 + rows * cfg.L * 2.0 + rows * cfg.F * 2.0
+    return flops, nbytes, touched
+
+
+def layer_bytes(cfg, touched):
+    """Algorithmic HBM bytes of the whole layer: weights touched once, x in,
+    fp32 out (intermediates excluded)."""
+    T, d, L, E, F, Fs = cfg.T, cfg.d, cfg.L, cfg.E, cfg.F, cfg.Fs
+    w = touched * 3.0 * F * L * 2 + 2.0 * d * L * 2 + E * d * 4.0 + 3.0 * d * Fs * 2
+    return w + T * d * 2.0 + T * d * 4.0
+
+
+def cpu_baseline(cfg, n_tok=256, n_exp=8, seed=0):
+    """The oracle (float64 numpy, as it stands) on a bounded sample of the
+    workload, extrapolated to tokens/s of the whole layer:
+      router + permutation over all T tokens (timed in full),
+      latent down, combine and up-projection on n_tok tokens (x T/n_tok),
+      n_exp experts' SwiGLU FFNs on their routed rows (x E/n_exp).
+    Input generation is not timed."""
+    import numpy as np
+    import oracle
+    from moe_synth import gen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    x = gen.host_tensor_f64(cfg, "x")
+    w_r = gen.router_weights(cfg).astype(np.float64)
+    b = gen.router_bias(cfg)
+    b = None if b is None else b.astype(np.float64)
+    w_dn = gen.host_tensor_f64(cfg, "w_dn")
+    w_up = gen.host_tensor_f64(cfg, "w_lat_up")
+    shared = None
+    if cfg.Fs:
+        shared = tuple(gen.host_tensor_f64(cfg, n) for n in ("ws_gate", "ws_up", "ws_down"))
+    t0 = time.perf_counter()
+    r = oracle.route(x, w_r, b, cfg.k)
+    p = oracle.permute(r["topk_idx"], cfg.E)
+    t_route = time.perf_counter() - t0
+    rng = np.random.default_rng(seed)
+    toks = np.sort(rng.choice(cfg.T, size=min(n_tok, cfg.T), replace=False))
+    t0 = time.perf_counter()
+    z = oracle.latent_down(x[toks], w_dn, "bf16_operands")
+    ys = np.stack([z] * cfg.k, axis=1).reshape(-1, cfg.L)     # stand-in expert rows, same shapes
+    ar = np.arange(len(toks) * cfg.k).reshape(len(toks), cfg.k)
+    c = oracle.combine(ys, r["topk_w"][toks], ar)
+    out = oracle.latent_up(c, w_up, "bf16_operands")
+    if shared is not None:
+        out = out + oracle.shared_expert(x[toks], *shared, mode="bf16_operands")
+    t_tok = time.perf_counter() - t0
+    counts = p["expert_counts"]
+    nonempty = np.nonzero(counts)[0]
+    sample = rng.choice(nonempty, size=min(n_exp, nonempty.size), replace=False)
+    t_exp = 0.0
+    rows_done = 0
+    for e in sample:
+        wts = gen.expert_weights_f64(cfg, int(e))
+        a, bnd = int(p["expert_offsets"][e]), int(p["expert_offsets"][e + 1])
+        zr = oracle.latent_down(x[p["row_token"][a:bnd]], w_dn, "bf16_operands")
+        t0 = time.perf_counter()
+        oracle.swiglu_expert(zr, *wts, mode="bf16_operands")
+        t_exp += time.perf_counter() - t0
+        rows_done += bnd - a
+        del wts
+    # experts scale by rows (their cost is linear in the rows they receive)
+    t_exp_total = t_exp * (cfg.T * cfg.k) / max(rows_done, 1)
+    total = t_route + t_tok * cfg.T / len(toks) + t_exp_total
+    return {
+        "value": cfg.T / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"float64 numpy oracle: router + permutation over all {cfg.T} tokens "
+                   f"({t_route:.2f} s), latent down/combine/up on {len(toks)} tokens "
+                   f"({t_tok:.2f} s, scaled x{cfg.T / len(toks):.0f}), SwiGLU experts on "
+                   f"{len(sample)} sampled experts = {rows_done} routed rows ({t_exp:.2f} s, "
+                   f"scaled by rows to all {cfg.T * cfg.k}); extrapolated {total:.1f} s per "
+                   f"forward pass"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_moe_amd as moe
+    from moe_synth import CONFIGS, device
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    print(f"[bench] {cfg.description}; generating inputs on the GPU", file=sys.stderr, flush=True)
+    dv = device.device_inputs(cfg, dev)
+    w = moe.LatentMoEWeights(dv["w_router"], dv["b_router"], dv["w_dn"], dv["w_gate"], dv["w_up"],
+                             dv["w_down"], dv["w_lat_up"], dv.get("ws_gate"), dv.get("ws_up"),
+                             dv.get("ws_down"))
+    buf = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, cfg.Fs, device=dev)
+    x = dv["x"]
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)   # plain copy of exactly 1 GiB read + 1 GiB written
+        torch.cuda.synchronize()
+        del src, dst
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        moe.forward(x, w, cfg.k, buf)
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    ev = {name: [(hip.create(), hip.create()) for _ in range(args.steps)] for name in KERNEL_NAMES}
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for name in KERNEL_NAMES:
+            moe.moe_set_kernel_events(name, *ev[name][i])
+        moe.forward(x, w, cfg.k, buf)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for name in KERNEL_NAMES:
+        moe.moe_set_kernel_events(name, None, None)
+    kern_ms = {name: float(np.mean([hip.elapsed_ms(a, b) for a, b in ev[name]]))
+               for name in KERNEL_NAMES}
+    for pairs in ev.values():
+        for a, b in pairs:
+            hip.destroy(a)
+            hip.destroy(b)
+
+    elapsed = t1 - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    value = cfg.T * args.steps / elapsed
+    counts = buf.expert_counts.cpu().numpy()
+    flops, nbytes, touched = dominant_work(cfg, counts)
+    dom_s = kern_ms[DOMINANT] * 1e-3
+    ai = flops / nbytes
+    if ai < MFMA_BF16_PEAK / HBM_PEAK:
+        roof = {"bound": "hbm", "achieved": nbytes / dom_s / 1e9, "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / dom_s / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = stored_traffic(cfg.name)
+    roof["kernel"] = "grouped gate/up GEMM + SwiGLU (gemm_kernel GROUPED GATHER EPI_SWIGLU)"
+    roof["algorithmic_per_launch"] = {"flops": flops, "bytes": nbytes, "experts_touched": touched}
+
+    step_s = ms_per_step * 1e-3
+    layer = {
+        "mfma_frac": cfg.flops() / step_s / MFMA_BF16_PEAK,
+        "hbm_frac": layer_bytes(cfg, touched) / step_s / HBM_PEAK,
+        "kernels_ms": {k: round(v, 4) for k, v in kern_ms.items()},
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.description, "T": cfg.T, "d": cfg.d, "latent": cfg.L,
+                   "experts": cfg.E, "top_k": cfg.k, "ffn": cfg.F, "shared_ffn": cfg.Fs,
+                   "seed": cfg.seed},
+        "roofline": roof, "layer": layer, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -47,7 +47,7 @@
  *   require of MoE top-k and of accumulations ("The Training and RL
  *   Infrastructure Behind MAI-Thinking-1", section 2, "Bitwise determinism").
  * - Limits: 1 <= k <= min(E, 16); E <= 1024; d, L, F, Fs multiples of 64
- *   (Fs may be 0 = no shared expert); T * k < 2^31.
+ *   (Fs may be 0 = no shared expert); T * k < 2^31; T * L * 2 < 2^31 bytes.
  * - Thread safety: calls from several host threads on different streams are
  *   safe; the only library state is the per-thread profiling-event registry.
  */
@@ -81,6 +81,7 @@ extern "C" {
  *   ROUTE      : three bf16 parts of W_r (3*E*d*2) + fp32 logits (T*E*4)
  *   PERMUTE    : per-chunk expert counts and bases (2 * ceil(T/256) * E * 4)
  *   LATENT_FFN : z (T*L*2) + SwiGLU activations H (T*k*F*2) + tile tables
+ *                (2 * (E+1) + 2 * ceil-bound of 128-row M tiles, int32)
  *   COMBINE    : combined latent c in bf16 (T*L*2)
  */
 size_t moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t L, int32_t E,

@@ -9,6 +9,9 @@
 
 namespace moe {
 
+template <int EPI>
+hipError_t dense_gemm_auto(GemmArgs a, int64_t M, hipStream_t s);   // expert.hip
+
 // c[t, :] = sum_{j=0..k-1} w[t, j] * y[assign_row[t, j], :]   (fp32, j ascending)
 // A gather (each output row read from its k expert rows), so no atomics and a
 // fixed summation order.  One workgroup per token; 4 floats per thread step.
@@ -65,18 +68,7 @@ hipError_t launch_latent_up(const uint16_t* c, const uint16_t* w_up, const uint1
   a.N = d;
   a.C = out;
   a.ldc = d;
-  a.M = (int)T;
-  const bool big = ceil_div(T, 256) * ceil_div(d, 256) >= 512;
-  if (big) {
-    a.m_tiles = (int)ceil_div(T, 256);
-    a.n_tiles = (int)ceil_div(d, 256);
-    a.grid = (int)(ceil_div((int64_t)a.m_tiles * a.n_tiles, 8) * 8);
-    return launch_gemm<256, 256, 2, 2, false, false, EPI_F32>(a, s);
-  }
-  a.m_tiles = (int)ceil_div(T, 128);
-  a.n_tiles = (int)ceil_div(d, 128);
-  a.grid = (int)(ceil_div((int64_t)a.m_tiles * a.n_tiles, 8) * 8);
-  return launch_gemm<128, 128, 2, 2, false, false, EPI_F32>(a, s);
+  return dense_gemm_auto<EPI_F32>(a, T, s);
 }
 
 }  // namespace moe

@@ -37,4 +37,11 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Upper bound of sum_e ceil(M_e / BM) over any routing of `rows` rows to E
+// experts (each non-empty expert adds at most one partial tile).
+inline int64_t grouped_mtile_bound(int64_t rows, int E, int BM) {
+  const int64_t nonempty = rows < E ? rows : E;
+  return (rows + nonempty * (BM - 1)) / BM;
+}
+
 }  // namespace moe

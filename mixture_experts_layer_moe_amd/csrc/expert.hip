@@ -13,9 +13,10 @@
 namespace moe {
 
 ExpertGemmPlan plan_expert_gemms(int64_t rows, int E) {
-  // Few rows per expert (small batches): a 128-row M tile usually holds an
-  // expert's rows in one tile, so each weight byte is streamed from HBM once
-  // while halving the MFMA work of a 256-row tile.  Otherwise 256 x 256.
+  // Few rows per expert (small batches, weight streaming): 128-row M tiles
+  // usually hold an expert's rows in one tile, so each weight byte is read
+  // from HBM once; a 3-deep load ring keeps two 48 KB stages in flight per CU.
+  // Otherwise (compute-bound) 256 x 256 tiles.
   const int64_t avg = rows / (E > 0 ? E : 1);
   ExpertGemmPlan p;
   p.bm_gate_up = avg <= 128 ? 128 : 256;
@@ -23,19 +24,27 @@ ExpertGemmPlan plan_expert_gemms(int64_t rows, int E) {
   return p;
 }
 
-template <int BM, int BN, int EPI>
+// Dense GEMM tile choice: 256 x 256 when that alone gives every CU two tiles,
+// else 128 x 256.
+static bool big_dense(int64_t M, int64_t Ncols) {
+  return ceil_div(M, 256) * ceil_div(Ncols, 256) >= 2 * (int64_t)device_cu_count();
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int EPI>
 static hipError_t dense_gemm(GemmArgs a, int64_t M, hipStream_t s) {
   a.M = (int)M;
   a.m_tiles = (int)ceil_div(M, BM);
   a.n_tiles = (int)ceil_div(EPI == EPI_SWIGLU ? 2 * (int64_t)a.N : a.N, BN);
-  a.grid = (int)(ceil_div((int64_t)a.m_tiles * a.n_tiles, 8) * 8);
-  return launch_gemm<BM, BN, 2, 2, false, false, EPI>(a, s);
+  return launch_gemm<BM, BN, WM, WN, NS, false, false, EPI>(a, (int64_t)a.m_tiles * a.n_tiles, s);
 }
 
-// Big tiles when they alone fill the chip, else 128 x 128.
-static bool use_big_tiles(int64_t M, int64_t N) {
-  return ceil_div(M, 256) * ceil_div(N, 256) >= 512;
+template <int EPI>
+hipError_t dense_gemm_auto(GemmArgs a, int64_t M, hipStream_t s) {
+  const int64_t ncols = EPI == EPI_SWIGLU ? 2 * (int64_t)a.N : a.N;
+  if (big_dense(M, ncols)) return dense_gemm<256, 256, 2, 2, 2, EPI>(a, M, s);
+  return dense_gemm<128, 256, 1, 4, 3, EPI>(a, M, s);
 }
+template hipError_t dense_gemm_auto<EPI_F32>(GemmArgs, int64_t, hipStream_t);
 
 hipError_t launch_latent_down(const uint16_t* x, const uint16_t* w_dn, int64_t T, int d, int L,
                               uint16_t* z, hipStream_t s) {
@@ -45,8 +54,7 @@ hipError_t launch_latent_down(const uint16_t* x, const uint16_t* w_dn, int64_t T
   a.N = L;
   a.C = z;
   a.ldc = L;
-  if (use_big_tiles(T, L)) return dense_gemm<256, 256, EPI_BF16>(a, T, s);
-  return dense_gemm<128, 128, EPI_BF16>(a, T, s);
+  return dense_gemm_auto<EPI_BF16>(a, T, s);
 }
 
 hipError_t launch_shared_gate_up(const uint16_t* x, const uint16_t* wsg, const uint16_t* wsu,
@@ -58,24 +66,30 @@ hipError_t launch_shared_gate_up(const uint16_t* x, const uint16_t* wsg, const u
   a.N = Fs;
   a.C = hs;
   a.ldc = Fs;
-  if (use_big_tiles(T, 2 * (int64_t)Fs)) return dense_gemm<256, 256, EPI_SWIGLU>(a, T, s);
-  return dense_gemm<128, 128, EPI_SWIGLU>(a, T, s);
+  return dense_gemm_auto<EPI_SWIGLU>(a, T, s);
 }
 
-// Per-expert M-tile counts -> exclusive prefix (two tile heights at once).
+// Per-expert M-tile counts -> exclusive prefix, and the expert of every M
+// tile, for two tile heights at once (gate/up and down GEMMs).
 __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ offsets,
                                                            int E, int bm_a, int bm_b,
                                                            int32_t* __restrict__ pre_a,
-                                                           int32_t* __restrict__ pre_b) {
+                                                           int32_t* __restrict__ pre_b,
+                                                           int32_t* __restrict__ exp_a,
+                                                           int32_t* __restrict__ exp_b) {
   const int e = threadIdx.x;
   int rows = 0;
   if (e < E) rows = offsets[e + 1] - offsets[e];
+  const int ma = e < E ? (rows + bm_a - 1) / bm_a : 0;
+  const int mb = e < E ? (rows + bm_b - 1) / bm_b : 0;
   int ta, tb;
-  const int ea = block_exclusive_scan(e < E ? (rows + bm_a - 1) / bm_a : 0, &ta);
-  const int eb = block_exclusive_scan(e < E ? (rows + bm_b - 1) / bm_b : 0, &tb);
+  const int ea = block_exclusive_scan(ma, &ta);
+  const int eb = block_exclusive_scan(mb, &tb);
   if (e < E) {
     pre_a[e] = ea;
     pre_b[e] = eb;
+    for (int i = 0; i < ma; ++i) exp_a[ea + i] = e;
+    for (int i = 0; i < mb; ++i) exp_b[eb + i] = e;
   }
   if (e == 0) {
     pre_a[E] = ta;
@@ -84,9 +98,9 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
 }
 
 hipError_t launch_tile_prefix(const int32_t* offsets, int E, int bm_a, int bm_b, int32_t* pre_a,
-                              int32_t* pre_b, hipStream_t s) {
+                              int32_t* pre_b, int32_t* exp_a, int32_t* exp_b, hipStream_t s) {
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm_a, bm_b, pre_a,
-                     pre_b);
+                     pre_b, exp_a, exp_b);
   return hipGetLastError();
 }
 
@@ -94,15 +108,15 @@ template <int BM, bool GATHER, int EPI>
 static hipError_t grouped_gemm(GemmArgs a, int64_t rows, hipStream_t s) {
   constexpr int BN = 256;
   a.n_tiles = (int)ceil_div(EPI == EPI_SWIGLU ? 2 * (int64_t)a.N : a.N, BN);
-  int mt;
-  a.grid = grouped_grid(rows, a.E, BM, a.n_tiles, &mt);
-  return launch_gemm<BM, BN, 2, 2, true, GATHER, EPI>(a, s);
+  const int64_t bound = grouped_mtile_bound(rows, a.E, BM) * a.n_tiles;
+  if constexpr (BM == 128) return launch_gemm<128, BN, 1, 4, 3, true, GATHER, EPI>(a, bound, s);
+  else return launch_gemm<256, BN, 2, 2, 2, true, GATHER, EPI>(a, bound, s);
 }
 
 hipError_t launch_gate_up(const uint16_t* z, const int32_t* offsets, const int32_t* row_token,
-                          const int32_t* tile_prefix, const uint16_t* w_gate,
-                          const uint16_t* w_up, int64_t T, int64_t rows, int E, int L, int F,
-                          int bm, uint16_t* H, hipStream_t s) {
+                          const int32_t* tile_prefix, const int32_t* tile_expert,
+                          const uint16_t* w_gate, const uint16_t* w_up, int64_t T, int64_t rows,
+                          int E, int L, int F, int bm, uint16_t* H, hipStream_t s) {
   GemmArgs a = {};
   a.seg[0].A = z; a.seg[0].lda = L; a.seg[0].B = w_gate; a.seg[0].B2 = w_up; a.seg[0].ldb = L;
   a.seg[0].K = L;
@@ -110,6 +124,7 @@ hipError_t launch_gate_up(const uint16_t* z, const int32_t* offsets, const int32
   a.N = F;
   a.offsets = offsets;
   a.tile_prefix = tile_prefix;
+  a.tile_expert = tile_expert;
   a.E = E;
   a.b_expert_stride = (int64_t)F * L;
   a.row_token = row_token;
@@ -121,20 +136,35 @@ hipError_t launch_gate_up(const uint16_t* z, const int32_t* offsets, const int32
 }
 
 hipError_t launch_expert_down(const uint16_t* H, const int32_t* offsets,
-                              const int32_t* tile_prefix, const uint16_t* w_down, int64_t rows,
-                              int E, int L, int F, int bm, float* Y, hipStream_t s) {
+                              const int32_t* tile_prefix, const int32_t* tile_expert,
+                              const uint16_t* w_down, int64_t rows, int E, int L, int F, int bm,
+                              float* Y, hipStream_t s) {
   GemmArgs a = {};
   a.seg[0].A = H; a.seg[0].lda = F; a.seg[0].B = w_down; a.seg[0].ldb = F; a.seg[0].K = F;
   a.nseg = 1;
   a.N = L;
   a.offsets = offsets;
   a.tile_prefix = tile_prefix;
+  a.tile_expert = tile_expert;
   a.E = E;
   a.b_expert_stride = (int64_t)L * F;
   a.C = Y;
   a.ldc = L;
   if (bm == 128) return grouped_gemm<128, false, EPI_F32>(a, rows, s);
   return grouped_gemm<256, false, EPI_F32>(a, rows, s);
+}
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 }  // namespace moe

@@ -47,14 +47,18 @@ PermWs perm_ws(int64_t T, int E) {
   w.total = w.base + align_up(nch * E * 4);
   return w;
 }
-struct FfnWs { size_t z, h, pre_a, pre_b, total; };
+struct FfnWs { size_t z, h, pre_a, pre_b, exp_a, exp_b, total; };
 FfnWs ffn_ws(int64_t T, int L, int E, int k, int F) {
+  // tile tables sized for the smallest M tile any plan uses (128 rows)
+  const size_t mt = (size_t)grouped_mtile_bound(T * k, E, 128);
   FfnWs w;
   w.z = 0;
   w.h = align_up((size_t)T * L * 2);
   w.pre_a = w.h + align_up((size_t)T * k * F * 2);
   w.pre_b = w.pre_a + align_up((size_t)(E + 1) * 4);
-  w.total = w.pre_b + align_up((size_t)(E + 1) * 4);
+  w.exp_a = w.pre_b + align_up((size_t)(E + 1) * 4);
+  w.exp_b = w.exp_a + align_up(mt * 4);
+  w.total = w.exp_b + align_up(mt * 4);
   return w;
 }
 size_t combine_ws(int64_t T, int L) { return align_up((size_t)T * L * 2); }
@@ -173,6 +177,8 @@ int moe_latent_ffn_forward(const uint16_t* x, const uint16_t* w_lat_down,
   if (k > 16 || E > 1024 || !dims_ok(d) || !dims_ok(L) || !dims_ok(F) ||
       (Fs > 0 && !dims_ok(Fs)) || T * (int64_t)k >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
+  // the gathered latent z[T, L] is addressed with 32-bit byte offsets
+  if ((int64_t)T * L * 2 >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !w_lat_down || !expert_offsets || !row_token || !w_gate || !w_up || !w_down ||
       !y_rows || !ws)
@@ -191,6 +197,8 @@ int moe_latent_ffn_forward(const uint16_t* x, const uint16_t* w_lat_down,
   uint16_t* H = (uint16_t*)(base + w.h);
   int32_t* pre_a = (int32_t*)(base + w.pre_a);
   int32_t* pre_b = (int32_t*)(base + w.pre_b);
+  int32_t* exp_a = (int32_t*)(base + w.exp_a);
+  int32_t* exp_b = (int32_t*)(base + w.exp_b);
   const int64_t rows = T * k;
   const ExpertGemmPlan plan = plan_expert_gemms(rows, E);
   int st;
@@ -201,16 +209,16 @@ int moe_latent_ffn_forward(const uint16_t* x, const uint16_t* w_lat_down,
   }
   if (st) return st;
   st = hip_status(launch_tile_prefix(expert_offsets, E, plan.bm_gate_up, plan.bm_down, pre_a,
-                                     pre_b, s));
+                                     pre_b, exp_a, exp_b, s));
   if (st) return st;
   {
     EventScope ev(K_GATE_UP, s);
-    st = hip_status(launch_gate_up(z, expert_offsets, row_token, pre_a, w_gate, w_up, T, rows, E,
-                                   L, F, plan.bm_gate_up, H, s));
+    st = hip_status(launch_gate_up(z, expert_offsets, row_token, pre_a, exp_a, w_gate, w_up, T,
+                                   rows, E, L, F, plan.bm_gate_up, H, s));
   }
   if (st) return st;
   EventScope ev(K_EXPERT_DOWN, s);
-  return hip_status(launch_expert_down(H, expert_offsets, pre_b, w_down, rows, E, L, F,
+  return hip_status(launch_expert_down(H, expert_offsets, pre_b, exp_b, w_down, rows, E, L, F,
                                        plan.bm_down, y_rows, s));
 }
 

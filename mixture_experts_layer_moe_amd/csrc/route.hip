@@ -38,7 +38,7 @@ hipError_t launch_router_gemm(const uint16_t* x, const float* w_router, const fl
                      w_router, w3, n);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  constexpr int BM = 128, BN = 128;
+  constexpr int BM = 64, BN = 128;
   GemmArgs a = {};
   for (int p = 0; p < 3; ++p) {
     a.seg[p].A = x;
@@ -55,8 +55,8 @@ hipError_t launch_router_gemm(const uint16_t* x, const float* w_router, const fl
   a.bias = bias;
   a.m_tiles = (int)ceil_div(T, BM);
   a.n_tiles = (int)ceil_div(E, BN);
-  a.grid = (int)(ceil_div((int64_t)a.m_tiles * a.n_tiles, 8) * 8);
-  return launch_gemm<BM, BN, 2, 2, false, false, EPI_F32_BIAS>(a, s);
+  return launch_gemm<BM, BN, 2, 2, 4, false, false, EPI_F32_BIAS>(
+      a, (int64_t)a.m_tiles * a.n_tiles, s);
 }
 
 // ---------------------------------------------------------------------------
