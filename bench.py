@@ -208,11 +208,10 @@ def main():
     torch.cuda.synchronize()
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        src.fill_(1)
         for _ in range(3):
-            dst.copy_(src)   # plain copy of exactly 1 GiB read + 1 GiB written
+            device.calibration_copy(src, dst)   # one dispatch: 1 GiB read + 1 GiB written
         torch.cuda.synchronize()
         del src, dst
 

@@ -48,3 +48,19 @@ extern "C" int synth_fill_bf16(uint16_t* out, int64_t n, int64_t start, uint32_t
                      out, n, start, k0, k1, table);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
+
+// Plain device copy of n 16-byte words in one dispatch, used only to calibrate
+// HBM byte counters (a kernel with known traffic: 16*n bytes read, 16*n written).
+__global__ void synth_calib_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                        int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+extern "C" int synth_calib_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes <= 0 || (bytes & 15)) return -1;
+  hipLaunchKernelGGL(synth_calib_copy_kernel, dim3(4096), dim3(256), 0, (hipStream_t)stream,
+                     (const uint4*)src, (uint4*)dst, bytes / 16);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}

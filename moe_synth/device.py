@@ -26,7 +26,21 @@ def _load():
         _lib.synth_fill_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p,
                                          ctypes.c_void_p]
+        _lib.synth_calib_copy.restype = ctypes.c_int
+        _lib.synth_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_void_p]
     return _lib
+
+
+def calibration_copy(src: torch.Tensor, dst: torch.Tensor):
+    """One dispatch of a plain copy kernel (synth_calib_copy_kernel) of src into dst,
+    for scaling HBM byte counters: reads and writes exactly src's bytes."""
+    nbytes = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() >= nbytes
+    rc = _load().synth_calib_copy(src.data_ptr(), dst.data_ptr(), nbytes,
+                                  torch.cuda.current_stream(src.device).cuda_stream)
+    if rc != 0:
+        raise RuntimeError("synth_calib_copy failed")
 
 
 def _table(sigma, device):

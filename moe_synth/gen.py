@@ -18,7 +18,9 @@ on the host with numpy's PCG64 and uploaded.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import functools
+import os
 
 import numpy as np
 from scipy.special import ndtri
@@ -76,7 +78,18 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
-    return bf16_bits_to_f32(bits).astype(np.float64)
+    bits = np.asarray(bits, dtype=np.uint16)
+    if bits.size <= _CHUNK:
+        return bf16_bits_to_f32(bits).astype(np.float64)
+    flat = bits.reshape(-1)
+    out = np.empty(flat.size, np.float64)
+
+    def work(i0):
+        out[i0:i0 + _CHUNK] = bf16_bits_to_f32(flat[i0:i0 + _CHUNK])
+
+    with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, range(0, flat.size, _CHUNK)))
+    return out.reshape(bits.shape)
 
 
 @functools.lru_cache(maxsize=64)
@@ -89,10 +102,32 @@ def normal_table_bits(sigma: float) -> np.ndarray:
     return t
 
 
+_CHUNK = 1 << 18
+
+
+def _threads() -> int:
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return max(1, min(16, os.cpu_count() or 1))
+
+
 def normal_bf16_bits(key: tuple[int, int], sigma: float, start: int, count: int) -> np.ndarray:
-    """bf16 bits of elements start .. start+count-1 of one synthetic tensor."""
-    h = hash_counter(start, count, key)
-    return normal_table_bits(sigma)[h >> np.uint32(16)]
+    """bf16 bits of elements start .. start+count-1 of one synthetic tensor.
+    Large requests are evaluated in cache-sized chunks on a thread pool (numpy
+    releases the GIL inside these loops); the result does not depend on it."""
+    table = normal_table_bits(sigma)
+    if count <= _CHUNK:
+        return table[hash_counter(start, count, key) >> np.uint32(16)]
+    out = np.empty(count, np.uint16)
+
+    def work(i0):
+        n = min(_CHUNK, count - i0)
+        out[i0:i0 + n] = table[hash_counter(start + i0, n, key) >> np.uint32(16)]
+
+    with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, range(0, count, _CHUNK)))
+    return out
 
 
 # ---------------------------------------------------------------------------
