@@ -30,19 +30,19 @@ static bool big_dense(int64_t M, int64_t Ncols) {
   return ceil_div(M, 256) * ceil_div(Ncols, 256) >= 2 * (int64_t)device_cu_count();
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int EPI>
+template <class C, int EPI>
 static hipError_t dense_gemm(GemmArgs a, int64_t M, hipStream_t s) {
   a.M = (int)M;
-  a.m_tiles = (int)ceil_div(M, BM);
-  a.n_tiles = (int)ceil_div(EPI == EPI_SWIGLU ? 2 * (int64_t)a.N : a.N, BN);
-  return launch_gemm<BM, BN, WM, WN, NS, false, false, EPI>(a, (int64_t)a.m_tiles * a.n_tiles, s);
+  a.m_tiles = (int)ceil_div(M, C::bm);
+  a.n_tiles = (int)ceil_div(EPI == EPI_SWIGLU ? 2 * (int64_t)a.N : a.N, C::bn);
+  return launch_gemm<C, false, false, EPI>(a, (int64_t)a.m_tiles * a.n_tiles, s);
 }
 
 template <int EPI>
 hipError_t dense_gemm_auto(GemmArgs a, int64_t M, hipStream_t s) {
   const int64_t ncols = EPI == EPI_SWIGLU ? 2 * (int64_t)a.N : a.N;
-  if (big_dense(M, ncols)) return dense_gemm<256, 256, 2, 2, 2, EPI>(a, M, s);
-  return dense_gemm<128, 256, 1, 4, 3, EPI>(a, M, s);
+  if (big_dense(M, ncols)) return dense_gemm<TileBig, EPI>(a, M, s);
+  return dense_gemm<TileMid, EPI>(a, M, s);
 }
 template hipError_t dense_gemm_auto<EPI_F32>(GemmArgs, int64_t, hipStream_t);
 
@@ -106,11 +106,11 @@ hipError_t launch_tile_prefix(const int32_t* offsets, int E, int bm_a, int bm_b,
 
 template <int BM, bool GATHER, int EPI>
 static hipError_t grouped_gemm(GemmArgs a, int64_t rows, hipStream_t s) {
-  constexpr int BN = 256;
-  a.n_tiles = (int)ceil_div(EPI == EPI_SWIGLU ? 2 * (int64_t)a.N : a.N, BN);
+  using C = std::conditional_t<BM == 128, TileStream, TileBig>;
+  static_assert(C::bm == BM, "tile height");
+  a.n_tiles = (int)ceil_div(EPI == EPI_SWIGLU ? 2 * (int64_t)a.N : a.N, C::bn);
   const int64_t bound = grouped_mtile_bound(rows, a.E, BM) * a.n_tiles;
-  if constexpr (BM == 128) return launch_gemm<128, BN, 1, 4, 3, true, GATHER, EPI>(a, bound, s);
-  else return launch_gemm<256, BN, 2, 2, 2, true, GATHER, EPI>(a, bound, s);
+  return launch_gemm<C, true, GATHER, EPI>(a, bound, s);
 }
 
 hipError_t launch_gate_up(const uint16_t* z, const int32_t* offsets, const int32_t* row_token,

@@ -38,7 +38,6 @@ hipError_t launch_router_gemm(const uint16_t* x, const float* w_router, const fl
                      w_router, w3, n);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  constexpr int BM = 64, BN = 128;
   GemmArgs a = {};
   for (int p = 0; p < 3; ++p) {
     a.seg[p].A = x;
@@ -53,10 +52,17 @@ hipError_t launch_router_gemm(const uint16_t* x, const float* w_router, const fl
   a.C = logits;
   a.ldc = E;
   a.bias = bias;
-  a.m_tiles = (int)ceil_div(T, BM);
-  a.n_tiles = (int)ceil_div(E, BN);
-  return launch_gemm<BM, BN, 2, 2, 4, false, false, EPI_F32_BIAS>(
-      a, (int64_t)a.m_tiles * a.n_tiles, s);
+  // large batches: 256 x 256 tiles already give every CU a tile
+  if (ceil_div(T, TileBig::bm) * ceil_div(E, TileBig::bn) >= device_cu_count()) {
+    a.m_tiles = (int)ceil_div(T, TileBig::bm);
+    a.n_tiles = (int)ceil_div(E, TileBig::bn);
+    return launch_gemm<TileBig, false, false, EPI_F32_BIAS>(a, (int64_t)a.m_tiles * a.n_tiles,
+                                                            s);
+  }
+  a.m_tiles = (int)ceil_div(T, TileRouter::bm);
+  a.n_tiles = (int)ceil_div(E, TileRouter::bn);
+  return launch_gemm<TileRouter, false, false, EPI_F32_BIAS>(a, (int64_t)a.m_tiles * a.n_tiles,
+                                                             s);
 }
 
 // ---------------------------------------------------------------------------
