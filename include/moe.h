@@ -81,7 +81,7 @@ extern "C" {
  *   ROUTE      : three bf16 parts of W_r (3*E*d*2) + fp32 logits (T*E*4)
  *   PERMUTE    : per-chunk expert counts and bases (2 * ceil(T/256) * E * 4)
  *   LATENT_FFN : z (T*L*2) + SwiGLU activations H (T*k*F*2) + tile tables
- *                (2 * (E+1) + 2 * ceil-bound of 128-row M tiles, int32)
+ *                (2 * (E+1) + 2 * ceil-bound of 128-row M tiles + 16, int32)
  *   COMBINE    : combined latent c in bf16 (T*L*2)
  */
 size_t moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t L, int32_t E,

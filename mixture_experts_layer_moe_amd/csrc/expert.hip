@@ -76,8 +76,10 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ pre_a,
                                                            int32_t* __restrict__ pre_b,
                                                            int32_t* __restrict__ exp_a,
-                                                           int32_t* __restrict__ exp_b) {
+                                                           int32_t* __restrict__ exp_b,
+                                                           int32_t* __restrict__ queues) {
   const int e = threadIdx.x;
+  if (e < 16) queues[e] = 0;   // per-XCD tile counters of the two grouped GEMMs
   int rows = 0;
   if (e < E) rows = offsets[e + 1] - offsets[e];
   const int ma = e < E ? (rows + bm_a - 1) / bm_a : 0;
@@ -98,9 +100,10 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
 }
 
 hipError_t launch_tile_prefix(const int32_t* offsets, int E, int bm_a, int bm_b, int32_t* pre_a,
-                              int32_t* pre_b, int32_t* exp_a, int32_t* exp_b, hipStream_t s) {
+                              int32_t* pre_b, int32_t* exp_a, int32_t* exp_b, int32_t* queues,
+                              hipStream_t s) {
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm_a, bm_b, pre_a,
-                     pre_b, exp_a, exp_b);
+                     pre_b, exp_a, exp_b, queues);
   return hipGetLastError();
 }
 
@@ -115,8 +118,8 @@ static hipError_t grouped_gemm(GemmArgs a, int64_t rows, hipStream_t s) {
 
 hipError_t launch_gate_up(const uint16_t* z, const int32_t* offsets, const int32_t* row_token,
                           const int32_t* tile_prefix, const int32_t* tile_expert,
-                          const uint16_t* w_gate, const uint16_t* w_up, int64_t T, int64_t rows,
-                          int E, int L, int F, int bm, uint16_t* H, hipStream_t s) {
+                          int32_t* queue, const uint16_t* w_gate, const uint16_t* w_up, int64_t T,
+                          int64_t rows, int E, int L, int F, int bm, uint16_t* H, hipStream_t s) {
   GemmArgs a = {};
   a.seg[0].A = z; a.seg[0].lda = L; a.seg[0].B = w_gate; a.seg[0].B2 = w_up; a.seg[0].ldb = L;
   a.seg[0].K = L;
@@ -128,6 +131,7 @@ hipError_t launch_gate_up(const uint16_t* z, const int32_t* offsets, const int32
   a.E = E;
   a.b_expert_stride = (int64_t)F * L;
   a.row_token = row_token;
+  a.queue = queue;
   a.M = (int)T;   // rows of z, the gathered matrix
   a.C = H;
   a.ldc = F;
@@ -137,8 +141,8 @@ hipError_t launch_gate_up(const uint16_t* z, const int32_t* offsets, const int32
 
 hipError_t launch_expert_down(const uint16_t* H, const int32_t* offsets,
                               const int32_t* tile_prefix, const int32_t* tile_expert,
-                              const uint16_t* w_down, int64_t rows, int E, int L, int F, int bm,
-                              float* Y, hipStream_t s) {
+                              int32_t* queue, const uint16_t* w_down, int64_t rows, int E, int L,
+                              int F, int bm, float* Y, hipStream_t s) {
   GemmArgs a = {};
   a.seg[0].A = H; a.seg[0].lda = F; a.seg[0].B = w_down; a.seg[0].ldb = F; a.seg[0].K = F;
   a.nseg = 1;
@@ -146,6 +150,7 @@ hipError_t launch_expert_down(const uint16_t* H, const int32_t* offsets,
   a.offsets = offsets;
   a.tile_prefix = tile_prefix;
   a.tile_expert = tile_expert;
+  a.queue = queue;
   a.E = E;
   a.b_expert_stride = (int64_t)L * F;
   a.C = Y;

@@ -7,9 +7,14 @@
 //   * Persistent, XCD-balanced: the grid is a multiple of 8 workgroups, one per
 //     CU; workgroup b runs on XCD b % 8.  The tile list (known only on the
 //     device for grouped GEMMs) is cut into 8 contiguous ranges, one per XCD,
-//     and the workgroups of an XCD walk their range round-robin, so the CUs of
-//     one XCD work on neighbouring tiles at the same time: tiles that share an
-//     expert's weight panel or an activation panel share that XCD's L2.
+//     so the CUs of one XCD work on neighbouring tiles: tiles that share an
+//     expert's weight panel or an activation panel share that XCD's L2.  With
+//     a queue (grouped GEMMs) each workgroup takes the next tile of its XCD's
+//     range from an atomic counter when it finishes one, so the tiles in
+//     flight on an XCD stay a contiguous window (workgroups never drift apart,
+//     and M tiles that read the same weight tile run together); without one
+//     the range is walked round-robin.  Either way each tile is computed the
+//     same way, so results do not depend on the assignment.
 //   * Operands go global -> LDS directly (buffer_load_dwordx4 ... lds), no
 //     register staging, in an NSTAGE-deep ring of BK-wide K stages (BK = 64:
 //     128-byte LDS rows; BK = 32: 64-byte rows, so a 256x256 tile fits four
@@ -69,6 +74,7 @@ struct GemmArgs {
   int E;
   int64_t b_expert_stride;
   const int32_t* row_token;    // GATHER
+  int32_t* queue;              // optional: 8 per-XCD tile counters, zero at launch
   void* C;
   int64_t ldc;
   const float* bias;           // EPI_F32_BIAS
@@ -139,7 +145,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(EPI != EPI_SWIGLU || WTN % 64 == 0, "swiglu pairs");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4 && LPS * (NSTAGE - 2) < 64, "stages");
-  __shared__ uint4 smem[NSTAGE * STAGE];
+  __shared__ uint4 smem[NSTAGE * STAGE + 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -164,7 +170,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   for (int s = 0; s < 3; ++s) if (s < a.nseg) ktotal += a.seg[s].K;
   const int nk = ktotal / BK;
 
-  for (int t = t_begin + (blockIdx.x >> 3); t < t_end; t += nj) {
+  // The queue's tile index is broadcast through the last 16-byte slot of the
+  // LDS array (one LDS object only, so the compiler's LDS-DMA alias tracking
+  // does not add waits in the K loop).
+  auto next_tile = [&](int prev) -> int {
+    if (a.queue == nullptr) return prev < 0 ? t_begin + (blockIdx.x >> 3) : prev + nj;
+    int* slot = (int*)&smem[NSTAGE * STAGE];
+    if (tid == 0) *slot = t_begin + atomicAdd(&a.queue[xcd], 1);
+    lds_barrier();     // every thread read the previous value before the end-of-tile barrier
+    return *slot;
+  };
+  for (int t = next_tile(-1); t < t_end; t = next_tile(t)) {
     // ---- decode the tile ----
     int r0, mrows, n_tile;
     int64_t b_off = 0;

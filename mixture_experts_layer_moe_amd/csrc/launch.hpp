@@ -32,15 +32,16 @@ hipError_t launch_latent_down(const uint16_t* x, const uint16_t* w_dn, int64_t T
 hipError_t launch_shared_gate_up(const uint16_t* x, const uint16_t* wsg, const uint16_t* wsu,
                                  int64_t T, int d, int Fs, uint16_t* hs, hipStream_t s);
 hipError_t launch_tile_prefix(const int32_t* offsets, int E, int bm_a, int bm_b, int32_t* pre_a,
-                              int32_t* pre_b, int32_t* exp_a, int32_t* exp_b, hipStream_t s);
+                              int32_t* pre_b, int32_t* exp_a, int32_t* exp_b, int32_t* queues,
+                              hipStream_t s);
 hipError_t launch_gate_up(const uint16_t* z, const int32_t* offsets, const int32_t* row_token,
                           const int32_t* tile_prefix, const int32_t* tile_expert,
-                          const uint16_t* w_gate, const uint16_t* w_up, int64_t T, int64_t rows,
-                          int E, int L, int F, int bm, uint16_t* H, hipStream_t s);
+                          int32_t* queue, const uint16_t* w_gate, const uint16_t* w_up, int64_t T,
+                          int64_t rows, int E, int L, int F, int bm, uint16_t* H, hipStream_t s);
 hipError_t launch_expert_down(const uint16_t* H, const int32_t* offsets,
                               const int32_t* tile_prefix, const int32_t* tile_expert,
-                              const uint16_t* w_down, int64_t rows, int E, int L, int F, int bm,
-                              float* Y, hipStream_t s);
+                              int32_t* queue, const uint16_t* w_down, int64_t rows, int E, int L,
+                              int F, int bm, float* Y, hipStream_t s);
 
 int device_cu_count();
 

@@ -47,7 +47,7 @@ PermWs perm_ws(int64_t T, int E) {
   w.total = w.base + align_up(nch * E * 4);
   return w;
 }
-struct FfnWs { size_t z, h, pre_a, pre_b, exp_a, exp_b, total; };
+struct FfnWs { size_t z, h, pre_a, pre_b, exp_a, exp_b, queues, total; };
 FfnWs ffn_ws(int64_t T, int L, int E, int k, int F) {
   // tile tables sized for the smallest M tile any plan uses (128 rows)
   const size_t mt = (size_t)grouped_mtile_bound(T * k, E, 128);
@@ -58,7 +58,8 @@ FfnWs ffn_ws(int64_t T, int L, int E, int k, int F) {
   w.pre_b = w.pre_a + align_up((size_t)(E + 1) * 4);
   w.exp_a = w.pre_b + align_up((size_t)(E + 1) * 4);
   w.exp_b = w.exp_a + align_up(mt * 4);
-  w.total = w.exp_b + align_up(mt * 4);
+  w.queues = w.exp_b + align_up(mt * 4);
+  w.total = w.queues + align_up(16 * 4);
   return w;
 }
 size_t combine_ws(int64_t T, int L) { return align_up((size_t)T * L * 2); }
@@ -199,6 +200,7 @@ int moe_latent_ffn_forward(const uint16_t* x, const uint16_t* w_lat_down,
   int32_t* pre_b = (int32_t*)(base + w.pre_b);
   int32_t* exp_a = (int32_t*)(base + w.exp_a);
   int32_t* exp_b = (int32_t*)(base + w.exp_b);
+  int32_t* queues = (int32_t*)(base + w.queues);
   const int64_t rows = T * k;
   const ExpertGemmPlan plan = plan_expert_gemms(rows, E);
   int st;
@@ -209,17 +211,17 @@ int moe_latent_ffn_forward(const uint16_t* x, const uint16_t* w_lat_down,
   }
   if (st) return st;
   st = hip_status(launch_tile_prefix(expert_offsets, E, plan.bm_gate_up, plan.bm_down, pre_a,
-                                     pre_b, exp_a, exp_b, s));
+                                     pre_b, exp_a, exp_b, queues, s));
   if (st) return st;
   {
     EventScope ev(K_GATE_UP, s);
-    st = hip_status(launch_gate_up(z, expert_offsets, row_token, pre_a, exp_a, w_gate, w_up, T,
-                                   rows, E, L, F, plan.bm_gate_up, H, s));
+    st = hip_status(launch_gate_up(z, expert_offsets, row_token, pre_a, exp_a, queues, w_gate,
+                                   w_up, T, rows, E, L, F, plan.bm_gate_up, H, s));
   }
   if (st) return st;
   EventScope ev(K_EXPERT_DOWN, s);
-  return hip_status(launch_expert_down(H, expert_offsets, pre_b, exp_b, w_down, rows, E, L, F,
-                                       plan.bm_down, y_rows, s));
+  return hip_status(launch_expert_down(H, expert_offsets, pre_b, exp_b, queues + 8, w_down, rows,
+                                       E, L, F, plan.bm_down, y_rows, s));
 }
 
 int moe_combine(const float* y_rows, const float* topk_w, const int32_t* assign_row,

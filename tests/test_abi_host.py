@@ -41,7 +41,7 @@ def test_workspace_sizes():
     assert _lib.moe_workspace_bytes(1, T, d, L, E, k, F) == 2 * a(16 * E * 4)
     mt = (T * k + min(E, T * k) * 127) // 128      # M tiles of 128 rows, any routing
     assert _lib.moe_workspace_bytes(2, T, d, L, E, k, F) == \
-        a(T * L * 2) + a(T * k * F * 2) + 2 * a((E + 1) * 4) + 2 * a(mt * 4)
+        a(T * L * 2) + a(T * k * F * 2) + 2 * a((E + 1) * 4) + 2 * a(mt * 4) + a(16 * 4)
     assert _lib.moe_workspace_bytes(3, T, d, L, E, k, F) == a(T * L * 2)
     assert _lib.moe_workspace_bytes(9, T, d, L, E, k, F) == 0
     assert _lib.moe_workspace_bytes(0, -1, d, L, E, k, F) == 0
