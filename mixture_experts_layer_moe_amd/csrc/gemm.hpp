@@ -52,6 +52,7 @@
 namespace moe {
 
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9)
+constexpr int DENSE_GM = 4;                     // M panels per tile group (dense GEMMs)
 
 enum GemmEpi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_BIAS = 2, EPI_SWIGLU = 3 };
 
@@ -195,8 +196,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       mrows = min(BM, a.offsets[e + 1] - r0);
       b_off = (int64_t)e * a.b_expert_stride;
     } else {
-      n_tile = t / a.m_tiles;
-      r0 = (t - n_tile * a.m_tiles) * BM;
+      // Groups of DENSE_GM M panels: inside a group the tiles go N tile by N
+      // tile with the M panel fastest, so a window of concurrent tiles spans a
+      // few M panels and a few N tiles and both operands are re-read rarely.
+      const int g = t / (DENSE_GM * a.n_tiles);
+      const int gm = min(DENSE_GM, a.m_tiles - g * DENSE_GM);
+      const int r = t - g * DENSE_GM * a.n_tiles;
+      n_tile = r / gm;
+      r0 = (g * DENSE_GM + (r - n_tile * gm)) * BM;
       mrows = min(BM, a.M - r0);
     }
     const int n0 = EPI == EPI_SWIGLU ? n_tile * (BN / 2) : n_tile * BN;   // first output col
