@@ -20,7 +20,8 @@ What it computes, and where the pages state it
 * section 2, "Bitwise determinism": MoE top-k uses a stable sort, so ties break
   the same way every run; fixed-order accumulation instead of atomics.
 * section 3, "Sharding and parallelism", "From capacity to dropless": dropless
-  routing (no capacity, no dropped tokens).
+  routing (no capacity, no dropped tokens); a global-batch load-balancing
+  loss aggregated across workers and micro-batches; a loss-free balancer.
 "MAI-Base-2: Microsoft's 2.8T base model..." (MAI-Base-2), section "The
 model": 7 of 512 routed experts plus one shared expert every token passes
 through; MoE down-projection dimension; the shared expert is not down/up
@@ -34,7 +35,10 @@ logit descending; rows of one expert in ascending token order; SwiGLU is
 W_d (silu(W_g z) * (W_u z)) with silu(v) = v * sigmoid(v) and no biases; the
 latent projections are plain linear maps; the combine is done in the latent
 space (linear, so equal to combining after the up-projection); the shared
-expert's output is added with weight 1; no extra scaling of the routed output.
+expert's output is added with weight 1; no extra scaling of the routed output;
+the load-balancing statistics are per-expert sums (assignment counts and router
+probabilities), additive across micro-batches and workers; the loss-free
+balancer is a per-expert bias that steers selection only.
 
 Precision modes
 ---------------
@@ -103,20 +107,42 @@ def topk_stable(scores, k):
     return order[:, :k]
 
 
-def route(x, w_router, b_router, k):
+BIAS_MODES = ("logits", "selection")
+
+
+def route(x, w_router, b_router, k, bias_mode="logits"):
     """Softmax gating with top-k.
 
-    Returns dict: logits (float64), logits_f32 (float32, the precision the
-    selection is taken in), probs (float64 softmax over all experts),
-    topk_idx [T,k] int32, topk_w [T,k] float64 (probabilities of the selected
-    experts, not renormalised)."""
+    bias_mode "logits": the bias is part of the logits (selection and weights).
+    bias_mode "selection": the bias only steers which experts are selected (a
+    loss-free balancer); the weights are the softmax of the unbiased logits.
+
+    Returns dict: logits (float64 selection logits, bias included),
+    logits_f32 (float32, the precision the selection is taken in), probs
+    (float64 softmax over all experts of the weight logits), topk_idx [T,k]
+    int32, topk_w [T,k] float64 (probabilities of the selected experts, not
+    renormalised)."""
+    if bias_mode not in BIAS_MODES:
+        raise ValueError(f"unknown bias mode {bias_mode!r}")
     logits = router_logits(x, w_router, b_router)
     logits_f32 = logits.astype(np.float32)
-    probs = softmax(logits)
+    if bias_mode == "selection" and b_router is not None:
+        probs = softmax(router_logits(x, w_router, None))
+    else:
+        probs = softmax(logits)
     idx = topk_stable(logits_f32, k).astype(np.int32)
     w = np.take_along_axis(probs, idx.astype(np.int64), axis=1)
     return {"logits": logits, "logits_f32": logits_f32, "probs": probs,
             "topk_idx": idx, "topk_w": w}
+
+
+def lbl_stats(probs, topk_idx, E):
+    """Per-expert statistics of a global-batch load-balancing loss, as sums
+    so that micro-batches and workers aggregate by addition: the number of
+    (token, slot) assignments routed to each expert and the sum over tokens
+    of each expert's router probability."""
+    counts = np.bincount(np.asarray(topk_idx, np.int64).ravel(), minlength=E)
+    return {"counts": counts, "prob_sum": np.asarray(probs, np.float64).sum(axis=0)}
 
 
 # ---------------------------------------------------------------------------

@@ -116,6 +116,46 @@ def test_route_bias_enters_before_softmax():
     np.testing.assert_allclose(r["topk_w"], [[10 / 19, 4 / 19]], atol=1e-15)
 
 
+def test_route_bias_for_selection_only():
+    # loss-free balancer: the bias picks expert 0, the weights stay those of
+    # the unbiased softmax (0.1, 0.2, 0.3, 0.4), not renormalised
+    target = np.log(np.array([[1.0, 2.0, 3.0, 4.0]]))
+    x, w_r = _router_for_logits(target)
+    r = om.route(x, w_r, np.log(np.array([10.0, 1.0, 1.0, 1.0])), 2, bias_mode="selection")
+    np.testing.assert_array_equal(r["topk_idx"], [[0, 3]])
+    np.testing.assert_allclose(r["topk_w"], [[0.1, 0.4]], atol=1e-15)
+    np.testing.assert_allclose(r["probs"], [[0.1, 0.2, 0.3, 0.4]], atol=1e-15)
+    # without a bias both modes are the same
+    a = om.route(x, w_r, None, 2, bias_mode="selection")
+    b = om.route(x, w_r, None, 2)
+    np.testing.assert_array_equal(a["topk_idx"], b["topk_idx"])
+    np.testing.assert_array_equal(a["topk_w"], b["topk_w"])
+    with pytest.raises(ValueError):
+        om.route(x, w_r, None, 2, bias_mode="other")
+
+
+def test_lbl_stats_closed_form_and_invariants():
+    target = np.log(np.array([[1.0, 2.0, 3.0, 4.0], [4.0, 3.0, 2.0, 1.0], [2.0, 2.0, 2.0, 2.0]]))
+    x, w_r = _router_for_logits(target)
+    r = om.route(x, w_r, None, 2)
+    st = om.lbl_stats(r["probs"], r["topk_idx"], 4)
+    # selections: (3,2), (0,1), (0,1)
+    np.testing.assert_array_equal(st["counts"], [2, 2, 1, 1])
+    np.testing.assert_allclose(st["prob_sum"], [0.1 + 0.4 + 0.25, 0.2 + 0.3 + 0.25,
+                                                0.3 + 0.2 + 0.25, 0.4 + 0.1 + 0.25], atol=1e-15)
+    lay = _random_layer(21, T=50, E=12, k=3, bias=True)
+    for mode in om.BIAS_MODES:
+        rr = om.route(lay["x"], lay["w_router"], lay["b_router"], 3, bias_mode=mode)
+        s2 = om.lbl_stats(rr["probs"], rr["topk_idx"], 12)
+        assert s2["counts"].sum() == 50 * 3
+        np.testing.assert_allclose(s2["prob_sum"].sum(), 50.0, rtol=1e-13)
+        # additive over micro-batches
+        h1 = om.lbl_stats(rr["probs"][:20], rr["topk_idx"][:20], 12)
+        h2 = om.lbl_stats(rr["probs"][20:], rr["topk_idx"][20:], 12)
+        np.testing.assert_array_equal(h1["counts"] + h2["counts"], s2["counts"])
+        np.testing.assert_allclose(h1["prob_sum"] + h2["prob_sum"], s2["prob_sum"], rtol=1e-13)
+
+
 def test_route_ties_go_to_lower_index():
     x, w_r = _router_for_logits(np.zeros((3, 6)))
     r = om.route(x, w_r, None, 4)
