@@ -79,6 +79,7 @@ extern "C" {
  * (arguments an op does not use are ignored).  Returns 0 for an unknown op
  * or invalid shapes.
  *   ROUTE      : three bf16 parts of W_r (3*E*d*2) + fp32 logits (T*E*4)
+ *                + probability partials ((n + ceil(n/64))*E*4, n = ceil(T/16))
  *   PERMUTE    : per-chunk expert counts and bases (2 * ceil(T/256) * E * 4)
  *   LATENT_FFN : z (T*L*2) + SwiGLU activations H (T*k*F*2) + tile tables
  *                (2 * (E+1) + 2 * ceil-bound of 128-row M tiles + 16, int32)
@@ -115,6 +116,34 @@ int moe_route(const uint16_t* x, const float* w_router, const float* b_router,
               int64_t T, int32_t d, int32_t E, int32_t k,
               int32_t* topk_idx, float* topk_w, float* logits_out,
               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_route with two options, for training-style use:
+ *
+ *   bias_mode  MOE_BIAS_LOGITS    : b_router is part of the logits (moe_route)
+ *              MOE_BIAS_SELECTION : b_router only steers which experts are
+ *                                   selected; topk_w are the softmax of the
+ *                                   unbiased logits (a loss-free balancer,
+ *                                   "The Training and RL Infrastructure Behind
+ *                                   MAI-Thinking-1", section 3 "From capacity
+ *                                   to dropless"); logits_out is unbiased
+ *   prob_sum   [E] fp32, optional (NULL): sum over the T tokens of each
+ *              expert's router probability.  With the per-expert assignment
+ *              counts of moe_permute these are the statistics of a
+ *              global-batch load-balancing loss; both are sums, so callers
+ *              aggregate micro-batches and workers by adding them (same
+ *              section; "Frontier Pre-training at Microsoft AI", "Reducing
+ *              per-expert overhead": one batched reduction across layers).
+ *              Reduced in a fixed order: deterministic.
+ * Other arguments, workspace and errors as for moe_route (an unknown
+ * bias_mode is MOE_ERR_INVALID_ARG).
+ */
+#define MOE_BIAS_LOGITS    0
+#define MOE_BIAS_SELECTION 1
+int moe_route_ex(const uint16_t* x, const float* w_router, const float* b_router,
+                 int32_t bias_mode, int64_t T, int32_t d, int32_t E, int32_t k,
+                 int32_t* topk_idx, float* topk_w, float* logits_out, float* prob_sum,
+                 void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Permutation of the T*k (token, slot) assignments into expert order: a

@@ -4,7 +4,7 @@ The compute lives in libmoe.so (hand-written HIP kernels behind the C ABI of
 include/moe.h); this package is its Python binding.  Importing the package
 does not load the library; the first call does, and raises if it is missing.
 """
-from ._lib import (MoEError, load, moe_combine, moe_latent_ffn_forward,  # noqa: F401
-                   moe_permute, moe_route, moe_set_kernel_events, moe_status_string,
-                   moe_workspace_bytes)
+from ._lib import (MOE_BIAS_LOGITS, MOE_BIAS_SELECTION, MoEError, load,  # noqa: F401
+                   moe_combine, moe_latent_ffn_forward, moe_permute, moe_route, moe_route_ex,
+                   moe_set_kernel_events, moe_status_string, moe_workspace_bytes)
 from .layer import LatentMoEBuffers, LatentMoEWeights, forward  # noqa: F401

@@ -17,6 +17,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so"
 _lib = None
 
 MOE_OK = 0
+MOE_BIAS_LOGITS, MOE_BIAS_SELECTION = 0, 1
 MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_LATENT_FFN, MOE_OP_COMBINE = 0, 1, 2, 3
 KERNELS = {"router_gemm": 0, "router_topk": 1, "permute": 2, "latent_down": 3, "gate_up": 4,
            "expert_down": 5, "combine": 6, "latent_up": 7}
@@ -44,6 +45,9 @@ def load():
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_route.restype = ctypes.c_int
     lib.moe_route.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.moe_route_ex.restype = ctypes.c_int
+    lib.moe_route_ex.argtypes = [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                 _vp, _sz, _vp]
     lib.moe_permute.restype = ctypes.c_int
     lib.moe_permute.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
     lib.moe_latent_ffn_forward.restype = ctypes.c_int
@@ -118,6 +122,23 @@ def moe_route(x, w_router, b_router, k, topk_idx, topk_w, logits_out=None, ws=No
     _check("moe_route", load().moe_route(_ptr(x), _ptr(w_router), _ptr(b_router), T, d, E, k,
                                          _ptr(topk_idx), _ptr(topk_w), _ptr(logits_out), _ptr(ws),
                                          _nbytes(ws), _stream(stream)))
+
+
+def moe_route_ex(x, w_router, b_router, bias_mode, k, topk_idx, topk_w, logits_out=None,
+                 prob_sum=None, ws=None, stream=None):
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_router, "w_router", torch.float32, 2)
+    _need(b_router, "b_router", torch.float32, 1)
+    _need(topk_idx, "topk_idx", torch.int32, 2)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    _need(logits_out, "logits_out", torch.float32, 2)
+    _need(prob_sum, "prob_sum", torch.float32, 1)
+    _need(ws, "ws", torch.uint8, 1)
+    T, d = x.shape
+    E = w_router.shape[0]
+    _check("moe_route_ex", load().moe_route_ex(
+        _ptr(x), _ptr(w_router), _ptr(b_router), int(bias_mode), T, d, E, k, _ptr(topk_idx),
+        _ptr(topk_w), _ptr(logits_out), _ptr(prob_sum), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_permute(topk_idx, E, expert_counts, expert_offsets, row_token, assign_row, ws,

@@ -11,8 +11,15 @@ namespace moe {
 hipError_t launch_router_gemm(const uint16_t* x, const float* w_router, const float* bias,
                               int64_t T, int d, int E, uint16_t* w3, float* logits,
                               hipStream_t s);
-hipError_t launch_softmax_topk(const float* logits, int64_t T, int E, int k, int32_t* topk_idx,
-                               float* topk_w, hipStream_t s);
+// Softmax over all E logits and top-k.  sel_bias (nullable): per-expert bias
+// added to the selection values only.  prob_sum (nullable): per-expert sum of
+// probabilities over all tokens (prob_part: topk_partial_floats(T, E) floats
+// of scratch for the deterministic fixed-order reduction).
+int64_t topk_chunks(int64_t T);
+int64_t topk_partial_floats(int64_t T, int E);
+hipError_t launch_softmax_topk(const float* logits, const float* sel_bias, int64_t T, int E, int k,
+                               int32_t* topk_idx, float* topk_w, float* prob_part,
+                               float* prob_sum, hipStream_t s);
 
 // permute.hip
 constexpr int PERM_CHUNK = 256;   // tokens per permutation workgroup

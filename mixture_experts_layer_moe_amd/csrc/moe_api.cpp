@@ -30,12 +30,13 @@ int hip_status(hipError_t e) {
 bool dims_ok(int64_t v) { return v > 0 && v % 64 == 0 && v <= (1 << 20); }
 
 // Workspace layouts (byte offsets, each 256-aligned).
-struct RouteWs { size_t w3, logits, total; };
+struct RouteWs { size_t w3, logits, part, total; };
 RouteWs route_ws(int64_t T, int d, int E) {
   RouteWs w;
   w.w3 = 0;
   w.logits = align_up((size_t)3 * E * d * 2);
-  w.total = w.logits + align_up((size_t)T * E * 4);
+  w.part = w.logits + align_up((size_t)T * E * 4);
+  w.total = w.part + align_up((size_t)topk_partial_floats(T, E) * 4);
   return w;
 }
 struct PermWs { size_t counts, base, total; };
@@ -120,11 +121,13 @@ int moe_set_kernel_events(int kernel, void* start_event, void* stop_event) {
   return MOE_OK;
 }
 
-int moe_route(const uint16_t* x, const float* w_router, const float* b_router, int64_t T,
-              int32_t d, int32_t E, int32_t k, int32_t* topk_idx, float* topk_w,
-              float* logits_out, void* ws, size_t ws_bytes, void* stream) {
+int moe_route_ex(const uint16_t* x, const float* w_router, const float* b_router,
+                 int32_t bias_mode, int64_t T, int32_t d, int32_t E, int32_t k,
+                 int32_t* topk_idx, float* topk_w, float* logits_out, float* prob_sum,
+                 void* ws, size_t ws_bytes, void* stream) {
   int st = check_route_dims(T, d, E, k);
   if (st) return st;
+  if (bias_mode != MOE_BIAS_LOGITS && bias_mode != MOE_BIAS_SELECTION) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !w_router || !topk_idx || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(ws) ||
@@ -135,14 +138,27 @@ int moe_route(const uint16_t* x, const float* w_router, const float* b_router, i
   hipStream_t s = (hipStream_t)stream;
   char* base = (char*)ws;
   float* logits = logits_out ? logits_out : (float*)(base + w.logits);
+  // bias in the logits: added by the GEMM epilogue; selection only: added by
+  // the top-k kernel to the selection values
+  const float* gemm_bias = bias_mode == MOE_BIAS_LOGITS ? b_router : nullptr;
+  const float* sel_bias = bias_mode == MOE_BIAS_SELECTION ? b_router : nullptr;
   {
     EventScope ev(K_ROUTER_GEMM, s);
-    st = hip_status(launch_router_gemm(x, w_router, b_router, T, d, E, (uint16_t*)(base + w.w3),
+    st = hip_status(launch_router_gemm(x, w_router, gemm_bias, T, d, E, (uint16_t*)(base + w.w3),
                                        logits, s));
   }
   if (st) return st;
   EventScope ev(K_ROUTER_TOPK, s);
-  return hip_status(launch_softmax_topk(logits, T, E, k, topk_idx, topk_w, s));
+  return hip_status(launch_softmax_topk(logits, sel_bias, T, E, k, topk_idx, topk_w,
+                                        prob_sum ? (float*)(base + w.part) : nullptr, prob_sum,
+                                        s));
+}
+
+int moe_route(const uint16_t* x, const float* w_router, const float* b_router, int64_t T,
+              int32_t d, int32_t E, int32_t k, int32_t* topk_idx, float* topk_w,
+              float* logits_out, void* ws, size_t ws_bytes, void* stream) {
+  return moe_route_ex(x, w_router, b_router, MOE_BIAS_LOGITS, T, d, E, k, topk_idx, topk_w,
+                      logits_out, nullptr, ws, ws_bytes, stream);
 }
 
 int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t* expert_counts,

@@ -22,7 +22,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = _lib.load()
     names = declared_functions()
-    assert {"moe_route", "moe_permute", "moe_latent_ffn_forward", "moe_combine",
+    assert {"moe_route", "moe_route_ex", "moe_permute", "moe_latent_ffn_forward", "moe_combine",
             "moe_workspace_bytes", "moe_status_string", "moe_set_kernel_events"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -37,7 +37,9 @@ def test_status_strings():
 def test_workspace_sizes():
     a = lambda v: (v + 255) // 256 * 256  # noqa: E731
     T, d, L, E, k, F = 4096, 6656, 3072, 512, 8, 10240
-    assert _lib.moe_workspace_bytes(0, T, d, L, E, k, F) == a(3 * E * d * 2) + a(T * E * 4)
+    n = (T + 15) // 16   # 16-token chunks of the probability partials
+    assert _lib.moe_workspace_bytes(0, T, d, L, E, k, F) == \
+        a(3 * E * d * 2) + a(T * E * 4) + a((n + (n + 63) // 64) * E * 4)
     assert _lib.moe_workspace_bytes(1, T, d, L, E, k, F) == 2 * a(16 * E * 4)
     mt = (T * k + min(E, T * k) * 127) // 128      # M tiles of 128 rows, any routing
     assert _lib.moe_workspace_bytes(2, T, d, L, E, k, F) == \
@@ -75,6 +77,18 @@ def test_route_rejects_null_misaligned_and_small_workspace():
     assert lib.moe_route(P, P, None, 8, 512, 16, 2, P, P, None, P, need - 1, None) == -3
     # T == 0 is a no-op success (nothing launched)
     assert lib.moe_route(P, P, None, 0, 512, 16, 2, P, P, None, P, 0, None) == 0
+
+
+def test_route_ex_rejects_unknown_bias_mode():
+    lib = _lib.load()
+    lib.moe_route_ex.restype = ctypes.c_int
+    lib.moe_route_ex.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                 ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert lib.moe_route_ex(P, P, P, 2, 8, 512, 16, 2, P, P, None, None, P, 1 << 40, None) == -1
+    assert lib.moe_route_ex(P, P, P, -1, 8, 512, 16, 2, P, P, None, None, P, 1 << 40, None) == -1
+    assert lib.moe_route_ex(P, P, P, 1, 0, 512, 16, 2, P, P, None, None, P, 0, None) == 0
 
 
 def test_permute_rejects_bad_args():
