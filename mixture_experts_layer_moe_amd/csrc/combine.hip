@@ -9,7 +9,7 @@
 
 namespace moe {
 
-template <int EPI>
+template <int EPI, int NSEG>
 hipError_t dense_gemm_auto(GemmArgs a, int64_t M, hipStream_t s);   // expert.hip
 
 // c[t, :] = sum_{j=0..k-1} w[t, j] * y[assign_row[t, j], :]   (fp32, j ascending)
@@ -68,7 +68,8 @@ hipError_t launch_latent_up(const uint16_t* c, const uint16_t* w_up, const uint1
   a.N = d;
   a.C = out;
   a.ldc = d;
-  return dense_gemm_auto<EPI_F32>(a, T, s);
+  if (Fs > 0) return dense_gemm_auto<EPI_F32, 2>(a, T, s);
+  return dense_gemm_auto<EPI_F32, 1>(a, T, s);
 }
 
 }  // namespace moe

@@ -30,21 +30,22 @@ static bool big_dense(int64_t M, int64_t Ncols) {
   return ceil_div(M, 256) * ceil_div(Ncols, 256) >= 2 * (int64_t)device_cu_count();
 }
 
-template <class C, int EPI>
+template <class C, int EPI, int NSEG>
 static hipError_t dense_gemm(GemmArgs a, int64_t M, hipStream_t s) {
   a.M = (int)M;
   a.m_tiles = (int)ceil_div(M, C::bm);
   a.n_tiles = (int)ceil_div(EPI == EPI_SWIGLU ? 2 * (int64_t)a.N : a.N, C::bn);
-  return launch_gemm<C, false, false, EPI>(a, (int64_t)a.m_tiles * a.n_tiles, s);
+  return launch_gemm<C, false, false, EPI, NSEG>(a, (int64_t)a.m_tiles * a.n_tiles, s);
 }
 
-template <int EPI>
+template <int EPI, int NSEG>
 hipError_t dense_gemm_auto(GemmArgs a, int64_t M, hipStream_t s) {
   const int64_t ncols = EPI == EPI_SWIGLU ? 2 * (int64_t)a.N : a.N;
-  if (big_dense(M, ncols)) return dense_gemm<TileBig, EPI>(a, M, s);
-  return dense_gemm<TileMid, EPI>(a, M, s);
+  if (big_dense(M, ncols)) return dense_gemm<TileBig, EPI, NSEG>(a, M, s);
+  return dense_gemm<TileMid, EPI, NSEG>(a, M, s);
 }
-template hipError_t dense_gemm_auto<EPI_F32>(GemmArgs, int64_t, hipStream_t);
+template hipError_t dense_gemm_auto<EPI_F32, 1>(GemmArgs, int64_t, hipStream_t);
+template hipError_t dense_gemm_auto<EPI_F32, 2>(GemmArgs, int64_t, hipStream_t);
 
 hipError_t launch_latent_down(const uint16_t* x, const uint16_t* w_dn, int64_t T, int d, int L,
                               uint16_t* z, hipStream_t s) {
@@ -54,7 +55,7 @@ hipError_t launch_latent_down(const uint16_t* x, const uint16_t* w_dn, int64_t T
   a.N = L;
   a.C = z;
   a.ldc = L;
-  return dense_gemm_auto<EPI_BF16>(a, T, s);
+  return dense_gemm_auto<EPI_BF16, 1>(a, T, s);
 }
 
 hipError_t launch_shared_gate_up(const uint16_t* x, const uint16_t* wsg, const uint16_t* wsu,
@@ -66,7 +67,7 @@ hipError_t launch_shared_gate_up(const uint16_t* x, const uint16_t* wsg, const u
   a.N = Fs;
   a.C = hs;
   a.ldc = Fs;
-  return dense_gemm_auto<EPI_SWIGLU>(a, T, s);
+  return dense_gemm_auto<EPI_SWIGLU, 1>(a, T, s);
 }
 
 // Per-expert M-tile counts -> exclusive prefix, and the expert of every M

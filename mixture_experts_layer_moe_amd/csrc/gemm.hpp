@@ -33,6 +33,9 @@
 //   * Up to three K segments (A_s, B_s, K_s) chain in one accumulation: the
 //     split-bf16 router (x against the hi/mid/lo parts of W_r) and the
 //     up-projection with the shared expert's down-projection appended along K.
+//     The segment count is a template parameter and every segment's buffer
+//     descriptors are built once per tile, so the K loop does no scalar
+//     memory loads (whose lgkmcnt waits would also drain the LDS reads).
 //   * GROUPED: M is the expert-ordered row list; tiles never straddle two
 //     experts.  Device tables (prefix of per-expert M-tile counts and the
 //     expert of every M-tile) map a tile index to (expert, M-tile, N-tile)
@@ -130,7 +133,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool GROUPED, bool GATHER, int EPI,
-          bool BNT>
+          bool BNT, int NSEG>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -144,14 +147,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   static_assert(BK == 32 || BK == 64, "stage width");
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile / waves");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+  (void)WTM;
   static_assert(EPI != EPI_SWIGLU || WTN % 64 == 0, "swiglu pairs");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4 && LPS * (NSTAGE - 2) < 64, "stages");
+  static_assert(NSEG >= 1 && NSEG <= 3 && (!GATHER || NSEG == 1), "K segments");
   __shared__ uint4 smem[NSTAGE * STAGE + 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-  const int wm0 = (wave / WN) * WTM;
+  // The tile's 32-row blocks are dealt to the WM wave rows in turn (block b
+  // to wave row b % WM), so a tile with few valid rows still spreads its
+  // MFMA work over every SIMD.
+  const int wrow = wave / WN;
   const int wn0 = (wave % WN) * WTN;
   const int lrow = lane / KCH;                     // row inside a DMA row group
   const int lchunk = (lane % KCH) ^ swz<KCH>(lrow);   // chunk this lane fetches
@@ -166,9 +174,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   const int t_begin = (int)((int64_t)total * xcd / 8);
   const int t_end = (int)((int64_t)total * (xcd + 1) / 8);
 
+  // K segment boundaries and strides, read once (static indices only, so
+  // they stay in scalar registers instead of being re-read in the K loop)
+  int kseg[3] = {0, 0, 0};
+  uint32_t lda2[3] = {0, 0, 0}, ldb2[3] = {0, 0, 0};
   int ktotal = 0;
-#pragma unroll
-  for (int s = 0; s < 3; ++s) if (s < a.nseg) ktotal += a.seg[s].K;
+  static_for<0, NSEG>([&](auto sc) {
+    constexpr int S = decltype(sc)::value;
+    kseg[S] = a.seg[S].K;
+    lda2[S] = (uint32_t)(a.seg[S].lda * 2);
+    ldb2[S] = (uint32_t)(a.seg[S].ldb * 2);
+    ktotal += kseg[S];
+  });
   const int nk = ktotal / BK;
 
   // The queue's tile index is broadcast through the last 16-byte slot of the
@@ -179,21 +196,25 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
     int* slot = (int*)&smem[NSTAGE * STAGE];
     if (tid == 0) *slot = t_begin + atomicAdd(&a.queue[xcd], 1);
     lds_barrier();     // every thread read the previous value before the end-of-tile barrier
-    return *slot;
+    // the same value in every lane: make it wave-uniform, so the tile's
+    // indices and buffer descriptors live in scalar registers (a descriptor
+    // in vector registers turns every DMA into a waterfall loop)
+    return __builtin_amdgcn_readfirstlane(*slot);
   };
   for (int t = next_tile(-1); t < t_end; t = next_tile(t)) {
     // ---- decode the tile ----
     int r0, mrows, n_tile;
     int64_t b_off = 0;
     if constexpr (GROUPED) {
-      const int e = a.tile_expert[t / a.n_tiles];
-      const int p0 = a.tile_prefix[e];
-      const int mt = a.tile_prefix[e + 1] - p0;
+      // table reads at a uniform address: every lane gets the same value
+      const int e = __builtin_amdgcn_readfirstlane(a.tile_expert[t / a.n_tiles]);
+      const int p0 = __builtin_amdgcn_readfirstlane(a.tile_prefix[e]);
+      const int mt = __builtin_amdgcn_readfirstlane(a.tile_prefix[e + 1]) - p0;
       const int rem = t - p0 * a.n_tiles;
       n_tile = rem / mt;
       const int m_local = rem - n_tile * mt;
-      r0 = a.offsets[e] + m_local * BM;
-      mrows = min(BM, a.offsets[e + 1] - r0);
+      r0 = __builtin_amdgcn_readfirstlane(a.offsets[e]) + m_local * BM;
+      mrows = min(BM, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - r0);
       b_off = (int64_t)e * a.b_expert_stride;
     } else {
       // Groups of DENSE_GM M panels: inside a group the tiles go N tile by N
@@ -225,60 +246,67 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       }
     }
 
+    // Buffer descriptors of every K segment for this tile (scalar registers).
+    __amdgpu_buffer_rsrc_t rA[NSEG], rB[NSEG], rU[NSEG];
+    static_for<0, NSEG>([&](auto sc) {
+      constexpr int S = decltype(sc)::value;
+      const GemmSeg& g = a.seg[S];
+      if constexpr (GATHER) rA[S] = make_rsrc(g.A, (int64_t)a.M * g.lda * 2);
+      else rA[S] = make_rsrc(g.A + (int64_t)r0 * g.lda, (int64_t)mrows * g.lda * 2);
+      rB[S] = make_rsrc(g.B + b_off + (int64_t)n0 * g.ldb, (int64_t)nrows * g.ldb * 2);
+      if constexpr (EPI == EPI_SWIGLU)
+        rU[S] = make_rsrc(g.B2 + b_off + (int64_t)n0 * g.ldb, (int64_t)nrows * g.ldb * 2);
+    });
+
     // DMA loads of stage kt.  A stage's instructions are split into NPART
     // parts (instruction i belongs to part i % NPART; PART < 0 = all) so that
     // the loads of a prefetched stage can be spread between the MFMA
     // sub-steps of the stage being computed instead of stalling in one block.
     constexpr int NPART = BK / 16;
-    auto issue = [&](int kt, auto part_c) {
+    auto issue_seg = [&](auto seg_c, int kt, int k0, auto part_c) {
+      constexpr int S = decltype(seg_c)::value;
       constexpr int PART = decltype(part_c)::value;
-      int s = 0, k0 = kt * BK;
-      if (a.nseg > 1 && k0 >= a.seg[0].K) {
-        k0 -= a.seg[0].K; s = 1;
-        if (a.nseg > 2 && k0 >= a.seg[1].K) { k0 -= a.seg[1].K; s = 2; }
-      }
-      const GemmSeg& g = a.seg[s];
       uint4* sa = smem + (kt % NSTAGE) * STAGE;
       uint4* sb = sa + BM * KCH;
       const uint32_t kbytes = (uint32_t)(k0 + lchunk * 8) * 2;
-      if constexpr (GATHER) {
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (int64_t)a.M * g.lda * 2);
 #pragma unroll
-        for (int i = 0; i < A_INS; ++i)
-          if (PART < 0 || i % NPART == PART)
-            dma16(ra, sa + (wave + i * NW) * 64, a_goff[i] + kbytes);
-      } else {
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A + (int64_t)r0 * g.lda,
-                                                   (int64_t)mrows * g.lda * 2);
-#pragma unroll
-        for (int i = 0; i < A_INS; ++i) {
-          if (!(PART < 0 || i % NPART == PART)) continue;
+      for (int i = 0; i < A_INS; ++i) {
+        if (!(PART < 0 || i % NPART == PART)) continue;
+        if constexpr (GATHER) {
+          dma16(rA[S], sa + (wave + i * NW) * 64, a_goff[i] + kbytes);
+        } else {
           const int rl = (wave + i * NW) * RPI + lrow;
-          dma16(ra, sa + (wave + i * NW) * 64, (uint32_t)(rl * g.lda * 2) + kbytes);
+          dma16(rA[S], sa + (wave + i * NW) * 64, (uint32_t)rl * lda2[S] + kbytes);
         }
       }
-      if constexpr (EPI == EPI_SWIGLU) {
-        const __amdgpu_buffer_rsrc_t rg = make_rsrc(g.B + b_off + (int64_t)n0 * g.ldb,
-                                                   (int64_t)nrows * g.ldb * 2);
-        const __amdgpu_buffer_rsrc_t ru = make_rsrc(g.B2 + b_off + (int64_t)n0 * g.ldb,
-                                                   (int64_t)nrows * g.ldb * 2);
 #pragma unroll
-        for (int i = 0; i < B_INS; ++i) {
-          if (!(PART < 0 || (A_INS + i) % NPART == PART)) continue;
-          const int rho0 = (wave + i * NW) * RPI;     // a DMA group never straddles a 32-row block
+      for (int i = 0; i < B_INS; ++i) {
+        if (!(PART < 0 || (A_INS + i) % NPART == PART)) continue;
+        const int rho0 = (wave + i * NW) * RPI;     // a DMA group never straddles a 32-row block
+        if constexpr (EPI == EPI_SWIGLU) {
           const int hrow = (rho0 >> 6) * 32 + (rho0 & 31) + lrow;
-          const uint32_t off = (uint32_t)(hrow * g.ldb * 2) + kbytes;
-          if ((rho0 >> 5) & 1) dma16<BNT>(ru, sb + rho0 * KCH, off);
-          else dma16<BNT>(rg, sb + rho0 * KCH, off);
+          const uint32_t off = (uint32_t)hrow * ldb2[S] + kbytes;
+          if ((rho0 >> 5) & 1) dma16<BNT>(rU[S], sb + rho0 * KCH, off);
+          else dma16<BNT>(rB[S], sb + rho0 * KCH, off);
+        } else {
+          dma16<BNT>(rB[S], sb + rho0 * KCH, (uint32_t)(rho0 + lrow) * ldb2[S] + kbytes);
         }
+      }
+    };
+    auto issue = [&](int kt, auto part_c) {
+      int k0 = kt * BK;
+      if constexpr (NSEG == 1) {
+        issue_seg(std::integral_constant<int, 0>{}, kt, k0, part_c);
       } else {
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B + b_off + (int64_t)n0 * g.ldb,
-                                                   (int64_t)nrows * g.ldb * 2);
-#pragma unroll
-        for (int i = 0; i < B_INS; ++i) {
-          if (!(PART < 0 || (A_INS + i) % NPART == PART)) continue;
-          const int rho0 = (wave + i * NW) * RPI;
-          dma16<BNT>(rb, sb + rho0 * KCH, (uint32_t)((rho0 + lrow) * g.ldb * 2) + kbytes);
+        if (k0 < kseg[0]) {
+          issue_seg(std::integral_constant<int, 0>{}, kt, k0, part_c);
+        } else {
+          k0 -= kseg[0];
+          if (NSEG == 2 || k0 < kseg[1]) {
+            issue_seg(std::integral_constant<int, 1>{}, kt, k0, part_c);
+          } else {
+            issue_seg(std::integral_constant<int, NSEG - 1>{}, kt, k0 - kseg[1], part_c);
+          }
         }
       }
     };
@@ -321,7 +349,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
           constexpr int kk = decltype(kk_c)::value;
           if (prefetch) issue(kt + NSTAGE - 1, kk_c);
           if constexpr (NACT > 0) {
-            // rows wm0 + 32 i + fr all have the same swizzle as row fr
+            // rows 32 (i WM + wrow) + fr all have the same swizzle as row fr
             const int ch = (kk * 2 + fq) ^ swz<KCH>(fr);
             bf16x8 bfr[TN], afr[NACT];
 #pragma unroll
@@ -329,7 +357,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
               bfr[j] = __builtin_bit_cast(bf16x8, sb[(wn0 + j * 32 + fr) * KCH + ch]);
 #pragma unroll
             for (int i = 0; i < NACT; ++i)
-              afr[i] = __builtin_bit_cast(bf16x8, sa[(wm0 + i * 32 + fr) * KCH + ch]);
+              afr[i] = __builtin_bit_cast(bf16x8, sa[((i * WM + wrow) * 32 + fr) * KCH + ch]);
 #pragma unroll
             for (int i = 0; i < NACT; ++i)
 #pragma unroll
@@ -340,7 +368,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
         });
       }
     };
-    const int nact = max(0, min(TM, (mrows - wm0 + 31) / 32));
+    const int nblk = (mrows + 31) / 32;   // valid 32-row blocks of the tile
+    const int nact = nblk > wrow ? min(TM, (nblk - wrow + WM - 1) / WM) : 0;
     static_assert(TM <= 16, "row blocks");
     switch (nact) {
 #define MOE_NACT_CASE(n) \
@@ -359,7 +388,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int rl = wm0 + i * 32 + 8 * (r >> 2) + 4 * fq + (r & 3);
+        const int rl = (i * WM + wrow) * 32 + 8 * (r >> 2) + 4 * fq + (r & 3);
         if (rl >= mrows) continue;
         const int64_t row = r0 + rl;
         if constexpr (EPI == EPI_SWIGLU) {
@@ -424,12 +453,13 @@ using TileBig = TileCfg<256, 256, 64, 2, 4, 2, false>;
 using TileMid = TileCfg<128, 256, 64, 2, 4, 3, false>;
 using TileRouter = TileCfg<64, 128, 64, 2, 2, 4, false>;
 
-template <class C, bool GROUPED, bool GATHER, int EPI>
+template <class C, bool GROUPED, bool GATHER, int EPI, int NSEG = 1>
 hipError_t launch_gemm(const GemmArgs& a, int64_t tiles_upper_bound, hipStream_t s) {
   if (tiles_upper_bound <= 0) return hipSuccess;
+  if (a.nseg != NSEG) return hipErrorInvalidValue;
   const int grid = persistent_grid(tiles_upper_bound);
   hipLaunchKernelGGL((gemm_kernel<C::bm, C::bn, C::bk, C::wm, C::wn, C::nstage, GROUPED, GATHER,
-                                  EPI, C::bnt>),
+                                  EPI, C::bnt, NSEG>),
                      dim3(grid), dim3(64 * C::wm * C::wn), 0, s, a);
   return hipGetLastError();
 }

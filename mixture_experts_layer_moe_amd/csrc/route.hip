@@ -56,12 +56,12 @@ hipError_t launch_router_gemm(const uint16_t* x, const float* w_router, const fl
   if (ceil_div(T, TileBig::bm) * ceil_div(E, TileBig::bn) >= device_cu_count()) {
     a.m_tiles = (int)ceil_div(T, TileBig::bm);
     a.n_tiles = (int)ceil_div(E, TileBig::bn);
-    return launch_gemm<TileBig, false, false, EPI_F32_BIAS>(a, (int64_t)a.m_tiles * a.n_tiles,
+    return launch_gemm<TileBig, false, false, EPI_F32_BIAS, 3>(a, (int64_t)a.m_tiles * a.n_tiles,
                                                             s);
   }
   a.m_tiles = (int)ceil_div(T, TileRouter::bm);
   a.n_tiles = (int)ceil_div(E, TileRouter::bn);
-  return launch_gemm<TileRouter, false, false, EPI_F32_BIAS>(a, (int64_t)a.m_tiles * a.n_tiles,
+  return launch_gemm<TileRouter, false, false, EPI_F32_BIAS, 3>(a, (int64_t)a.m_tiles * a.n_tiles,
                                                              s);
 }
 
