@@ -50,6 +50,19 @@ Precision modes
                     enter their next GEMM.  Expert outputs y, the combine and
                     the layer output stay float64 (the pages keep the combine
                     and the residual stream FP32).
+``fp8_operands``  : as ``bf16_operands``, and the routed experts' GEMMs take
+                    FP8 E4M3 operands ("The Training and RL Infrastructure
+                    Behind MAI-Thinking-1", section 2, "Pre-training and
+                    mid-training precision": forward GEMMs in FP8 E4M3 with
+                    delayed per-tensor scaling).  Every operand tensor t has a
+                    scale s_t; its values enter the GEMM as
+                    e4m3(float32(v) * s_t) and the product is divided by the
+                    two scales.  Tensors: the bf16 latent z, the bf16 SwiGLU
+                    activation h, and each expert's W_g, W_u, W_d.  Readings:
+                    the conversion rounds to nearest, ties to even, and
+                    saturates at +-448; the latent projections, the shared
+                    expert and the router are not FP8 in this build (the
+                    router is FP32 on the pages).
 
 Parity pins: see ``tests/test_oracle.py`` (closed forms, brute force over all
 experts, invariants, special cases).  No function here is "parity unpinned".
@@ -58,7 +71,8 @@ from __future__ import annotations
 
 import numpy as np
 
-MODES = ("exact", "bf16_operands")
+MODES = ("exact", "bf16_operands", "fp8_operands")
+E4M3_MAX = 448.0
 
 
 # ---------------------------------------------------------------------------
@@ -78,7 +92,49 @@ def round_bf16(v: np.ndarray) -> np.ndarray:
 def _maybe_bf16(v, mode):
     if mode not in MODES:
         raise ValueError(f"unknown mode {mode!r}")
-    return round_bf16(v) if mode == "bf16_operands" else v
+    return v if mode == "exact" else round_bf16(v)
+
+
+def round_e4m3(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to FP8 E4M3 (OCP "E4M3FN": 4 exponent bits with
+    bias 7, 3 fraction bits, subnormals below 2**-6, largest finite 448),
+    round to nearest with ties to even, saturating: magnitudes above 448
+    become 448.  Written from the format: the spacing of representable values
+    is 2**(e - 3) in the binade [2**e, 2**(e+1)) for e >= -6, and 2**-9 below
+    2**-6."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    quantum = np.exp2(np.maximum(e, -6.0) - 3.0)
+    r = np.minimum(np.rint(a / quantum) * quantum, E4M3_MAX)   # np.rint: half to even
+    return np.copysign(r, v)
+
+
+def quantize_e4m3(v, scale) -> np.ndarray:
+    """FP8 operand of a tensor with scale s: e4m3(float32(v) * float32(s)),
+    the product taken in float32 as the kernels take it.  Returned as the
+    float64 values of the E4M3 codes."""
+    p = np.asarray(v, np.float32) * np.float32(scale)
+    return round_e4m3(p.astype(np.float64))
+
+
+def fp8_matmul(a, b, scale_a, scale_b):
+    """a b^T with both operands in FP8: (Q(a, s_a) Q(b, s_b)^T) / (s_a s_b)."""
+    qa = quantize_e4m3(a, scale_a)
+    qb = quantize_e4m3(b, scale_b)
+    return (qa @ qb.T) / (float(np.float32(scale_a)) * float(np.float32(scale_b)))
+
+
+def fp8_scale_from_history(history) -> np.ndarray:
+    """Delayed scaling: the scale of a tensor is 448 / (largest absolute value
+    in its amax history), in float32; 1 when the history holds only zeros.
+    ``history`` is [..., H]; returns the scales of the leading axes."""
+    h = np.asarray(history, np.float32)
+    m = h.max(axis=-1)
+    with np.errstate(divide="ignore"):
+        s = np.where(m > 0, np.float32(E4M3_MAX) / np.where(m > 0, m, np.float32(1)),
+                     np.float32(1))
+    return s.astype(np.float32)
 
 
 # ---------------------------------------------------------------------------
@@ -188,15 +244,31 @@ def latent_down(x, w_dn, mode="exact"):
     return _maybe_bf16(np.asarray(x, np.float64) @ np.asarray(w_dn, np.float64).T, mode)
 
 
-def swiglu_expert(z_rows, w_gate, w_up, w_down, mode="exact"):
-    """y = (silu(z W_g^T) * (z W_u^T)) W_d^T for the rows routed to one expert."""
+def swiglu_expert(z_rows, w_gate, w_up, w_down, mode="exact", fp8=None):
+    """y = (silu(z W_g^T) * (z W_u^T)) W_d^T for the rows routed to one expert.
+    fp8_operands mode: ``fp8`` = (s_z, s_gate, s_up, s_h, s_down), the scales
+    of the latent, of this expert's three weights and of the activation h."""
+    if mode == "fp8_operands":
+        s_z, s_g, s_u, s_h, s_d = fp8
+        g = fp8_matmul(z_rows, w_gate, s_z, s_g)
+        u = fp8_matmul(z_rows, w_up, s_z, s_u)
+        h = round_bf16(silu(g) * u)
+        return fp8_matmul(h, w_down, s_h, s_d)
     g = z_rows @ np.asarray(w_gate, np.float64).T
     u = z_rows @ np.asarray(w_up, np.float64).T
     h = _maybe_bf16(silu(g) * u, mode)
     return h @ np.asarray(w_down, np.float64).T
 
 
-def expert_rows(z, perm, experts, mode="exact", expert_fn=None):
+def expert_fp8_scales(fp8, e):
+    """(s_z, s_gate, s_up, s_h, s_down) of expert e from a scale dict with keys
+    z, h (floats) and w_gate, w_up, w_down (per expert)."""
+    if fp8 is None:
+        return None
+    return (fp8["z"], fp8["w_gate"][e], fp8["w_up"][e], fp8["h"], fp8["w_down"][e])
+
+
+def expert_rows(z, perm, experts, mode="exact", expert_fn=None, fp8=None):
     """Expert outputs y[T*k, L] in expert order: for every expert e, the rows
     offsets[e] .. offsets[e+1] are its tokens' latents through its FFN.
     ``experts[e]`` yields (W_gate[e], W_up[e], W_down[e]); ``expert_fn`` may
@@ -211,7 +283,7 @@ def expert_rows(z, perm, experts, mode="exact", expert_fn=None):
             continue
         zr = z[row_token[a:b]]
         y[a:b] = expert_fn(e, zr) if expert_fn is not None else \
-            swiglu_expert(zr, *experts[e], mode=mode)
+            swiglu_expert(zr, *experts[e], mode=mode, fp8=expert_fp8_scales(fp8, e))
     return y
 
 
@@ -247,13 +319,15 @@ def shared_expert(x, ws_gate, ws_up, ws_down, mode="exact"):
 # ---------------------------------------------------------------------------
 
 def forward(x, w_router, b_router, k, w_dn, experts, w_lat_up, shared=None,
-            mode="exact", routing=None, expert_fn=None):
+            mode="exact", routing=None, expert_fn=None, fp8=None):
     """LatentMoE forward: route -> permute -> z = x W_dn^T -> experts on the
     latent -> weighted combine -> up-projection (+ shared expert).
 
     ``experts[e]`` -> (W_gate[e], W_up[e], W_down[e]); ``shared`` is None or
     (Ws_gate, Ws_up, Ws_down); ``routing`` optionally replaces the router with
-    given (topk_idx, topk_w).  Returns a dict of every stage's result."""
+    given (topk_idx, topk_w); ``fp8`` holds the FP8 scales for the
+    fp8_operands mode (see ``expert_fp8_scales``).  Returns a dict of every
+    stage's result."""
     x = np.asarray(x, np.float64)
     E = int(np.asarray(w_router).shape[0]) if w_router is not None else len(experts)
     if routing is None:
@@ -263,7 +337,7 @@ def forward(x, w_router, b_router, k, w_dn, experts, w_lat_up, shared=None,
              "topk_w": np.asarray(routing[1], np.float64)}
     p = permute(r["topk_idx"], E)
     z = latent_down(x, w_dn, mode)
-    y = expert_rows(z, p, experts, mode, expert_fn)
+    y = expert_rows(z, p, experts, mode, expert_fn, fp8)
     c = combine(y, r["topk_w"], p["assign_row"])
     out = latent_up(c, w_lat_up, mode)
     if shared is not None:
@@ -275,7 +349,7 @@ def forward(x, w_router, b_router, k, w_dn, experts, w_lat_up, shared=None,
 
 
 def forward_tokens(x_rows, topk_idx, topk_w, w_dn, experts, w_lat_up, shared=None,
-                   mode="exact"):
+                   mode="exact", fp8=None):
     """Per-token definition of the layer output, with no permutation: for each
     token t, out[t] = (sum_j w[t,j] * expert_{idx[t,j]}(z_t)) W_up^T (+ shared).
     Used for sampled tokens of shapes too large for ``forward``."""
@@ -285,7 +359,8 @@ def forward_tokens(x_rows, topk_idx, topk_w, w_dn, experts, w_lat_up, shared=Non
     for t in range(x_rows.shape[0]):
         for j in range(topk_idx.shape[1]):
             e = int(topk_idx[t, j])
-            c[t] += float(topk_w[t, j]) * swiglu_expert(z[t:t + 1], *experts[e], mode=mode)[0]
+            c[t] += float(topk_w[t, j]) * swiglu_expert(
+                z[t:t + 1], *experts[e], mode=mode, fp8=expert_fp8_scales(fp8, e))[0]
     out = latent_up(c, w_lat_up, mode)
     if shared is not None:
         out = out + shared_expert(x_rows, *shared, mode=mode)
@@ -293,7 +368,7 @@ def forward_tokens(x_rows, topk_idx, topk_w, w_dn, experts, w_lat_up, shared=Non
 
 
 def forward_dense_bruteforce(x, w_router, b_router, k, w_dn, experts, w_lat_up,
-                             shared=None, mode="exact", expert_fn=None):
+                             shared=None, mode="exact", expert_fn=None, fp8=None):
     """Brute force: evaluate every expert on every token, then keep the top-k
     by a mask (no permutation, no gather).  For tiny inputs only."""
     x = np.asarray(x, np.float64)
@@ -307,7 +382,8 @@ def forward_dense_bruteforce(x, w_router, b_router, k, w_dn, experts, w_lat_up,
     z = latent_down(x, w_dn, mode)
     c = np.zeros_like(z)
     for e in range(E):
-        ye = expert_fn(e, z) if expert_fn is not None else swiglu_expert(z, *experts[e], mode=mode)
+        ye = expert_fn(e, z) if expert_fn is not None else \
+            swiglu_expert(z, *experts[e], mode=mode, fp8=expert_fp8_scales(fp8, e))
         c += (mask[:, e] * r["probs"][:, e])[:, None] * ye
     out = latent_up(c, w_lat_up, mode)
     if shared is not None:

@@ -30,7 +30,7 @@ def main():
     inp = gen.host_inputs_f64(cfg)
     experts = [(inp["w_gate"][e], inp["w_up"][e], inp["w_down"][e]) for e in range(cfg.E)]
     out = {"config": cfg.name, "seed": cfg.seed}
-    for mode in oracle.MODES:
+    for mode in ("exact", "bf16_operands"):
         r = oracle.forward(inp["x"], inp["w_router"], inp["b_router"], cfg.k, inp["w_dn"], experts,
                            inp["w_lat_up"], mode=mode)
         out[mode] = {

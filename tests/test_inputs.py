@@ -87,7 +87,7 @@ def test_oracle_golden_values_tiny():
     inp = gen.host_inputs_f64(cfg)
     experts = [(inp["w_gate"][e], inp["w_up"][e], inp["w_down"][e]) for e in range(cfg.E)]
     crc = lambda a: zlib.crc32(np.ascontiguousarray(a, dtype=np.int32).tobytes())  # noqa: E731
-    for mode in oracle.MODES:
+    for mode in ("exact", "bf16_operands"):
         r = oracle.forward(inp["x"], inp["w_router"], inp["b_router"], cfg.k, inp["w_dn"], experts,
                            inp["w_lat_up"], mode=mode)
         w = want[mode]

@@ -39,6 +39,21 @@ def _random_layer(seed, T=37, d=24, L=16, E=8, k=3, F=20, Fs=0, bias=False):
                 shared=shared)
 
 
+def _fp8_scales(lay):
+    """Per-tensor FP8 scales for a random layer: 448 / amax of z and of each
+    expert weight; a fixed scale for h (any positive scale is valid)."""
+    z = om.latent_down(lay["x"], lay["w_dn"], "bf16_operands")
+    amax = lambda a: float(np.max(np.abs(a)))  # noqa: E731
+    return {"z": np.float32(448.0 / amax(z)), "h": np.float32(64.0),
+            "w_gate": [np.float32(448.0 / amax(g)) for g, _, _ in lay["experts"]],
+            "w_up": [np.float32(448.0 / amax(u)) for _, u, _ in lay["experts"]],
+            "w_down": [np.float32(448.0 / amax(d)) for _, _, d in lay["experts"]]}
+
+
+def _fp8_for(lay, mode):
+    return _fp8_scales(lay) if mode == "fp8_operands" else None
+
+
 # ---------------------------------------------------------------------------
 # bf16 rounding
 # ---------------------------------------------------------------------------
@@ -337,8 +352,8 @@ def test_combine_fixed_order_weighted_sum():
 def test_permuted_path_equals_dense_bruteforce(seed, k, bias, Fs):
     lay = _random_layer(seed, k=k, bias=bias, Fs=Fs)
     for mode in oracle.MODES:
-        a = om.forward(**lay, mode=mode)
-        b = om.forward_dense_bruteforce(**lay, mode=mode)
+        a = om.forward(**lay, mode=mode, fp8=_fp8_for(lay, mode))
+        b = om.forward_dense_bruteforce(**lay, mode=mode, fp8=_fp8_for(lay, mode))
         np.testing.assert_array_equal(a["topk_idx"], b["topk_idx"])
         scale = np.sqrt(np.mean(b["out"] ** 2))
         assert np.max(np.abs(a["out"] - b["out"])) <= 1e-12 * scale
@@ -347,9 +362,10 @@ def test_permuted_path_equals_dense_bruteforce(seed, k, bias, Fs):
 def test_per_token_definition_equals_permuted_path():
     lay = _random_layer(7, k=3, Fs=8)
     for mode in oracle.MODES:
-        a = om.forward(**lay, mode=mode)
+        a = om.forward(**lay, mode=mode, fp8=_fp8_for(lay, mode))
         b = om.forward_tokens(lay["x"], a["topk_idx"], a["topk_w"], lay["w_dn"], lay["experts"],
-                              lay["w_lat_up"], shared=lay["shared"], mode=mode)
+                              lay["w_lat_up"], shared=lay["shared"], mode=mode,
+                              fp8=_fp8_for(lay, mode))
         np.testing.assert_allclose(b["out"], a["out"], rtol=1e-12, atol=1e-12)
 
 
@@ -408,3 +424,94 @@ def test_bf16_mode_rounds_only_gemm_operands():
     np.testing.assert_array_equal(bf["z"], om.round_bf16(ex["z"]))
     rel = np.max(np.abs(bf["out"] - ex["out"])) / np.sqrt(np.mean(ex["out"] ** 2))
     assert 1e-5 < rel < 5e-2
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 operands (forward GEMMs in FP8 with per-tensor scales)
+# ---------------------------------------------------------------------------
+
+def _e4m3_values():
+    """Every finite non-negative E4M3FN value in code order, decoded from the
+    bit fields (exponent bias 7, 3 fraction bits; code 0x7F is NaN)."""
+    vals = []
+    for code in range(0x7F):
+        e, m = code >> 3, code & 7
+        vals.append((m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+def test_e4m3_table_landmarks():
+    tab = _e4m3_values()
+    assert tab[-1] == 448.0 and tab[1] == 2.0 ** -9 and tab[8] == 2.0 ** -6 and tab[0x38] == 1.0
+    assert np.all(np.diff(tab) > 0)
+
+
+def test_round_e4m3_exact_values():
+    cases = [(1.0, 1.0), (1.0625, 1.0), (1.1875, 1.25), (1.125, 1.125), (3 * 2.0 ** -10, 2.0 ** -8),
+             (2.0 ** -10, 0.0), (2.0 ** -9, 2.0 ** -9), (464.0, 448.0), (479.0, 448.0),
+             (500.0, 448.0), (1e9, 448.0), (-1.0625, -1.0), (0.0146484375, 0.015625), (3.3, 3.25),
+             (-3.3, -3.25), (240.0, 240.0), (256.0, 256.0), (0.0, 0.0), (1e-8, 0.0)]
+    for v, want in cases:
+        assert om.round_e4m3(np.array([v]))[0] == want, v
+
+
+def test_round_e4m3_is_the_nearest_value_ties_to_even_code():
+    tab = _e4m3_values()
+    r = _rng(21)
+    mags = np.exp(r.uniform(np.log(2.0 ** -12), np.log(600.0), 20000))
+    mids = (tab[:-1] + tab[1:]) / 2                      # every tie
+    v = np.concatenate([mags, -mags, mids, -mids, tab, [600.0, 1e6]])
+    got = om.round_e4m3(v)
+    a = np.minimum(np.abs(v), 448.0)                     # saturating conversion
+    dist = np.abs(tab[None, :] - a[:, None])
+    cand = dist == dist.min(axis=1, keepdims=True)
+    even = (np.arange(tab.size) % 2 == 0)[None, :]
+    pick = np.where(cand.sum(axis=1) > 1, np.argmax(cand & even, axis=1), np.argmax(cand, axis=1))
+    np.testing.assert_array_equal(got, np.copysign(tab[pick], v))
+
+
+def test_quantize_e4m3_saturates_and_scales():
+    np.testing.assert_array_equal(om.quantize_e4m3(np.array([1000.0, -1000.0, 3.0]), 1.0),
+                                  [448.0, -448.0, 3.0])
+    # 0.75 * 2**-3 = 0.09375 = 1.5 * 2**-4 (exact); with scale 8 it is 0.75
+    np.testing.assert_array_equal(om.quantize_e4m3(np.array([0.09375]), 8.0), [0.75])
+
+
+def test_fp8_matmul_exact_for_representable_operands_and_power_of_two_scales():
+    tab = _e4m3_values()
+    r = _rng(22)
+    # normal values 2**-5 .. 7.5: times 4 or halved they stay normal and below 448
+    a = np.copysign(r.choice(tab[16:80], (5, 16)), r.standard_normal((5, 16)))
+    b = np.copysign(r.choice(tab[16:80], (7, 16)), r.standard_normal((7, 16)))
+    np.testing.assert_array_equal(om.fp8_matmul(a, b, 1.0, 1.0), a @ b.T)
+    # power-of-two scales shift whole binades (no saturation, no underflow here)
+    np.testing.assert_array_equal(om.fp8_matmul(a, b, 4.0, 0.5), a @ b.T)
+    # and the division by the scales is not dropped: one operand is scaled 2x
+    np.testing.assert_array_equal(om.fp8_matmul(a, 2 * b, 1.0, 0.5), 2 * (a @ b.T))
+
+
+def test_fp8_scale_from_history():
+    h = np.array([[0.5, 2.0, 1.0], [0.0, 0.0, 0.0], [448.0, 1.0, 3.0], [0.0, 7.0, 0.0]], np.float32)
+    np.testing.assert_array_equal(om.fp8_scale_from_history(h),
+                                  np.array([224.0, 1.0, 1.0, 64.0], np.float32))
+
+
+def test_fp8_mode_quantizes_expert_operands_only():
+    lay = _random_layer(23, k=2, Fs=8)
+    sc = _fp8_scales(lay)
+    bf = om.forward(**lay, mode="bf16_operands")
+    f8 = om.forward(**lay, mode="fp8_operands", fp8=sc)
+    np.testing.assert_array_equal(f8["z"], bf["z"])           # z itself stays bf16
+    # one expert by hand: every operand through e4m3 with its scale
+    e, zr = 0, bf["z"][:3]
+    wg, wu, wd = lay["experts"][e]
+    qz = om.round_e4m3(np.float32(zr) * sc["z"])
+    g = (qz @ om.round_e4m3(np.float32(wg) * sc["w_gate"][e]).T) / (float(sc["z"]) * float(sc["w_gate"][e]))
+    u = (qz @ om.round_e4m3(np.float32(wu) * sc["w_up"][e]).T) / (float(sc["z"]) * float(sc["w_up"][e]))
+    h = om.round_bf16(g / (1 + np.exp(-g)) * u)
+    y = (om.round_e4m3(np.float32(h) * sc["h"]) @ om.round_e4m3(np.float32(wd) * sc["w_down"][e]).T) \
+        / (float(sc["h"]) * float(sc["w_down"][e]))
+    got = om.swiglu_expert(zr, wg, wu, wd, mode="fp8_operands", fp8=om.expert_fp8_scales(sc, e))
+    np.testing.assert_allclose(got, y, rtol=1e-12, atol=1e-15)
+    rel = np.max(np.abs(f8["out"] - bf["out"])) / np.sqrt(np.mean(bf["out"] ** 2))
+    assert 1e-3 < rel < 0.3
