@@ -40,11 +40,13 @@ def _random_layer(seed, T=37, d=24, L=16, E=8, k=3, F=20, Fs=0, bias=False):
 
 
 def _fp8_scales(lay):
-    """Per-tensor FP8 scales for a random layer: 448 / amax of z and of each
-    expert weight; a fixed scale for h (any positive scale is valid)."""
+    """Per-tensor FP8 scales for a random layer: 448 / amax of z, of h (over
+    every expert applied to every token, a bound of the routed rows' amax)
+    and of each expert weight."""
     z = om.latent_down(lay["x"], lay["w_dn"], "bf16_operands")
     amax = lambda a: float(np.max(np.abs(a)))  # noqa: E731
-    return {"z": np.float32(448.0 / amax(z)), "h": np.float32(64.0),
+    h_amax = max(amax(om.silu(z @ g.T) * (z @ u.T)) for g, u, _ in lay["experts"])
+    return {"z": np.float32(448.0 / amax(z)), "h": np.float32(448.0 / h_amax),
             "w_gate": [np.float32(448.0 / amax(g)) for g, _, _ in lay["experts"]],
             "w_up": [np.float32(448.0 / amax(u)) for _, u, _ in lay["experts"]],
             "w_down": [np.float32(448.0 / amax(d)) for _, _, d in lay["experts"]]}
