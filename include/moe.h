@@ -73,6 +73,7 @@ extern "C" {
 #define MOE_OP_PERMUTE     1
 #define MOE_OP_LATENT_FFN  2
 #define MOE_OP_COMBINE     3
+#define MOE_OP_LATENT_FFN_FP8 4
 
 /*
  * Bytes of device workspace that the entry point `op` needs for these shapes
@@ -84,6 +85,8 @@ extern "C" {
  *   LATENT_FFN : z (T*L*2) + SwiGLU activations H (T*k*F*2) + tile tables
  *                (2 * (E+1) + 2 * ceil-bound of 128-row M tiles + 16, int32)
  *   COMBINE    : combined latent c in bf16 (T*L*2)
+ *   LATENT_FFN_FP8 : z in E4M3 (T*L) + H in E4M3 (T*k*F) + the same tile
+ *                tables as LATENT_FFN
  */
 size_t moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t L, int32_t E,
                            int32_t k, int32_t F, int32_t Fs);
@@ -216,6 +219,65 @@ int moe_combine(const float* y_rows, const float* topk_w, const int32_t* assign_
                 const uint16_t* w_lat_up, const uint16_t* hs, const uint16_t* ws_down,
                 int64_t T, int32_t d, int32_t L, int32_t k, int32_t Fs,
                 float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- FP8 E4M3 forward expert GEMMs ----------------------------------------
+ * "The Training and RL Infrastructure Behind MAI-Thinking-1", section 2,
+ * "Pre-training and mid-training precision": the forward GEMMs take FP8 E4M3
+ * operands, with delayed scaling over a 1,024-step history of each tensor's
+ * absolute maximum.  Format: OCP E4M3FN bytes (bias 7, 3 fraction bits,
+ * largest finite 448).  A tensor t with scale s_t enters a GEMM as
+ * e4m3(float32(v) * s_t), rounded to nearest even and saturated at +-448;
+ * the product of two such operands is divided by both scales.  Scales and
+ * maxima are fp32 device values; maxima are non-negative.
+ */
+
+/* amax[t] = max |src[t][i]| over i, for ntensor bf16 tensors of numel values
+ * each, stored back to back.  numel must be a multiple of 8 and src 16-byte
+ * aligned (MOE_ERR_UNSUPPORTED), ntensor <= 65535.  Order-independent,
+ * deterministic.  ntensor == 0 is a no-op. */
+int moe_fp8_amax(const uint16_t* src, int64_t ntensor, int64_t numel, float* amax,
+                 void* stream);
+
+/* dst[t][i] = e4m3(float32(src[t][i]) * scale[t]) (one byte each), for
+ * ntensor bf16 tensors of numel values; the weights of the FP8 experts are
+ * quantized with this once (e.g. 512 experts of F*L values, scale 448 /
+ * amax per expert).  numel a multiple of 8; src and dst 16-byte aligned. */
+int moe_fp8_quantize(const uint16_t* src, int64_t ntensor, int64_t numel, const float* scale,
+                     uint8_t* dst, void* stream);
+
+/* Delayed scaling, one step for ntensor tensors: history[t][slot] = amax[t],
+ * then scale[t] = 448 / max_i history[t][i] (1 if that maximum is 0).
+ * history is [ntensor][hist_len] fp32 (hist_len 1,024 on the pages), owned
+ * and zero-initialised by the caller; the caller advances slot modulo
+ * hist_len.  MOE_ERR_INVALID_ARG for slot outside [0, hist_len). */
+int moe_fp8_scale_update(float* history, const float* amax, int64_t ntensor, int32_t hist_len,
+                         int32_t slot, float* scale, void* stream);
+
+/*
+ * moe_latent_ffn_forward with the routed experts' GEMMs in FP8 E4M3.
+ *   w_gate, w_up   : [E, F, L] E4M3 bytes;  w_down : [E, L, F] E4M3 bytes
+ *   w_scale        : [3*E] fp32, the quantization scales of W_g[e] (first
+ *                    E), W_u[e] (next E), W_d[e] (last E)
+ *   act_scale      : [2] fp32, the scales of the latent z and of the SwiGLU
+ *                    activation h for this step (from their amax histories)
+ *   act_amax (out) : [2] fp32, max |z| and max |h| of this step (of the bf16
+ *                    values before quantization), for the histories
+ * z = bf16(x W_dn^T) and h = bf16(silu(g) u) are computed as in the bf16
+ * path and quantized in the epilogues that produce them; each expert GEMM
+ * dequantizes in its epilogue; y_rows is fp32.  The latent down-projection
+ * and the shared expert stay bf16.  L and F must be multiples of 128
+ * (MOE_ERR_UNSUPPORTED).  Other arguments, limits and errors as for
+ * moe_latent_ffn_forward; workspace op MOE_OP_LATENT_FFN_FP8.  Finish with
+ * moe_combine as usual.
+ */
+int moe_latent_ffn_forward_fp8(const uint16_t* x, const uint16_t* w_lat_down,
+                               const int32_t* expert_offsets, const int32_t* row_token,
+                               const uint8_t* w_gate, const uint8_t* w_up, const uint8_t* w_down,
+                               const float* w_scale, const float* act_scale,
+                               const uint16_t* ws_gate, const uint16_t* ws_up, int64_t T,
+                               int32_t d, int32_t L, int32_t E, int32_t k, int32_t F, int32_t Fs,
+                               float* y_rows, uint16_t* hs, float* act_amax, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /* ---- profiling hook ------------------------------------------------------
  * Register two hipEvent_t (created by the caller) that the library records on

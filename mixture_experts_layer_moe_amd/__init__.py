@@ -5,6 +5,8 @@ include/moe.h); this package is its Python binding.  Importing the package
 does not load the library; the first call does, and raises if it is missing.
 """
 from ._lib import (MOE_BIAS_LOGITS, MOE_BIAS_SELECTION, MoEError, load,  # noqa: F401
-                   moe_combine, moe_latent_ffn_forward, moe_permute, moe_route, moe_route_ex,
-                   moe_set_kernel_events, moe_status_string, moe_workspace_bytes)
-from .layer import LatentMoEBuffers, LatentMoEWeights, forward  # noqa: F401
+                   moe_combine, moe_fp8_amax, moe_fp8_quantize, moe_fp8_scale_update,
+                   moe_latent_ffn_forward, moe_latent_ffn_forward_fp8, moe_permute, moe_route,
+                   moe_route_ex, moe_set_kernel_events, moe_status_string, moe_workspace_bytes)
+from .layer import (Fp8Scaling, LatentMoEBuffers, LatentMoEFp8Experts,  # noqa: F401
+                    LatentMoEWeights, forward, forward_fp8, quantize_experts)

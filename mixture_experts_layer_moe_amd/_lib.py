@@ -19,6 +19,7 @@ _lib = None
 MOE_OK = 0
 MOE_BIAS_LOGITS, MOE_BIAS_SELECTION = 0, 1
 MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_LATENT_FFN, MOE_OP_COMBINE = 0, 1, 2, 3
+MOE_OP_LATENT_FFN_FP8 = 4
 KERNELS = {"router_gemm": 0, "router_topk": 1, "permute": 2, "latent_down": 3, "gate_up": 4,
            "expert_down": 5, "combine": 6, "latent_up": 7}
 
@@ -57,6 +58,16 @@ def load():
     lib.moe_combine.restype = ctypes.c_int
     lib.moe_combine.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp,
                                 _vp, _sz, _vp]
+    lib.moe_fp8_amax.restype = ctypes.c_int
+    lib.moe_fp8_amax.argtypes = [_vp, _i64, _i64, _vp, _vp]
+    lib.moe_fp8_quantize.restype = ctypes.c_int
+    lib.moe_fp8_quantize.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
+    lib.moe_fp8_scale_update.restype = ctypes.c_int
+    lib.moe_fp8_scale_update.argtypes = [_vp, _vp, _i64, _i32, _i32, _vp, _vp]
+    lib.moe_latent_ffn_forward_fp8.restype = ctypes.c_int
+    lib.moe_latent_ffn_forward_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                               _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32,
+                                               _vp, _vp, _vp, _vp, _sz, _vp]
     lib.moe_set_kernel_events.restype = ctypes.c_int
     lib.moe_set_kernel_events.argtypes = [ctypes.c_int, _vp, _vp]
     _lib = lib
@@ -189,3 +200,59 @@ def moe_combine(y_rows, topk_w, assign_row, w_lat_up, hs, ws_down, out, ws, stre
                                              _ptr(w_lat_up), _ptr(hs), _ptr(ws_down), T, d, L, k,
                                              Fs, _ptr(out), _ptr(ws), _nbytes(ws),
                                              _stream(stream)))
+
+
+def moe_fp8_amax(src, ntensor, amax, stream=None):
+    """amax[t] = max |src_t| for ntensor equal bf16 tensors stored back to back in src."""
+    _need(src, "src", torch.bfloat16)
+    _need(amax, "amax", torch.float32, 1)
+    _check("moe_fp8_amax", load().moe_fp8_amax(_ptr(src), int(ntensor), src.numel() // max(ntensor, 1),
+                                               _ptr(amax), _stream(stream)))
+
+
+def moe_fp8_quantize(src, ntensor, scale, dst, stream=None):
+    """dst = e4m3(src_t * scale[t]) bytes (uint8) for ntensor equal bf16 tensors."""
+    _need(src, "src", torch.bfloat16)
+    _need(scale, "scale", torch.float32, 1)
+    _need(dst, "dst", torch.uint8)
+    if dst.numel() != src.numel():
+        raise ValueError("dst must have one byte per src value")
+    _check("moe_fp8_quantize", load().moe_fp8_quantize(
+        _ptr(src), int(ntensor), src.numel() // max(ntensor, 1), _ptr(scale), _ptr(dst),
+        _stream(stream)))
+
+
+def moe_fp8_scale_update(history, amax, slot, scale, stream=None):
+    """history [n, H] fp32: history[:, slot] = amax; scale = 448 / max over the history."""
+    _need(history, "history", torch.float32, 2)
+    _need(amax, "amax", torch.float32, 1)
+    _need(scale, "scale", torch.float32, 1)
+    n, H = history.shape
+    _check("moe_fp8_scale_update", load().moe_fp8_scale_update(
+        _ptr(history), _ptr(amax), n, H, int(slot), _ptr(scale), _stream(stream)))
+
+
+def moe_latent_ffn_forward_fp8(x, w_lat_down, expert_offsets, row_token, w_gate, w_up, w_down,
+                               w_scale, act_scale, ws_gate, ws_up, k, y_rows, hs, act_amax, ws,
+                               stream=None):
+    for n, t in (("x", x), ("w_lat_down", w_lat_down), ("ws_gate", ws_gate), ("ws_up", ws_up),
+                 ("hs", hs)):
+        _need(t, n, torch.bfloat16)
+    for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(t, n, torch.uint8, 3)
+    _need(w_scale, "w_scale", torch.float32, 1)
+    _need(act_scale, "act_scale", torch.float32, 1)
+    _need(act_amax, "act_amax", torch.float32, 1)
+    _need(expert_offsets, "expert_offsets", torch.int32, 1)
+    _need(row_token, "row_token", torch.int32, 1)
+    _need(y_rows, "y_rows", torch.float32, 2)
+    _need(ws, "ws", torch.uint8, 1)
+    T, d = x.shape
+    L = w_lat_down.shape[0]
+    E, F = w_gate.shape[0], w_gate.shape[1]
+    Fs = 0 if ws_gate is None else ws_gate.shape[0]
+    _check("moe_latent_ffn_forward_fp8", load().moe_latent_ffn_forward_fp8(
+        _ptr(x), _ptr(w_lat_down), _ptr(expert_offsets), _ptr(row_token), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), _ptr(w_scale), _ptr(act_scale), _ptr(ws_gate), _ptr(ws_up), T,
+        d, L, E, k, F, Fs, _ptr(y_rows), _ptr(hs), _ptr(act_amax), _ptr(ws), _nbytes(ws),
+        _stream(stream)))

@@ -34,13 +34,13 @@ template <class C, int EPI, int NSEG>
 static hipError_t dense_gemm(GemmArgs a, int64_t M, hipStream_t s) {
   a.M = (int)M;
   a.m_tiles = (int)ceil_div(M, C::bm);
-  a.n_tiles = (int)ceil_div(EPI == EPI_SWIGLU ? 2 * (int64_t)a.N : a.N, C::bn);
+  a.n_tiles = (int)ceil_div(epi_swiglu(EPI) ? 2 * (int64_t)a.N : a.N, C::bn);
   return launch_gemm<C, false, false, EPI, NSEG>(a, (int64_t)a.m_tiles * a.n_tiles, s);
 }
 
 template <int EPI, int NSEG>
 hipError_t dense_gemm_auto(GemmArgs a, int64_t M, hipStream_t s) {
-  const int64_t ncols = EPI == EPI_SWIGLU ? 2 * (int64_t)a.N : a.N;
+  const int64_t ncols = epi_swiglu(EPI) ? 2 * (int64_t)a.N : a.N;
   if (big_dense(M, ncols)) return dense_gemm<TileBig, EPI, NSEG>(a, M, s);
   return dense_gemm<TileMid, EPI, NSEG>(a, M, s);
 }
@@ -56,6 +56,22 @@ hipError_t launch_latent_down(const uint16_t* x, const uint16_t* w_dn, int64_t T
   a.C = z;
   a.ldc = L;
   return dense_gemm_auto<EPI_BF16, 1>(a, T, s);
+}
+
+// FP8 path: z = bf16(x W_dn^T) quantized to E4M3 with the scale z_scale in
+// the epilogue; the largest |z| goes to amax (one uint32 holding float bits).
+hipError_t launch_latent_down_q8(const uint16_t* x, const uint16_t* w_dn, int64_t T, int d,
+                                 int L, const float* z_scale, uint32_t* amax, uint8_t* z8,
+                                 hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = x; a.seg[0].lda = d; a.seg[0].B = w_dn; a.seg[0].ldb = d; a.seg[0].K = d;
+  a.nseg = 1;
+  a.N = L;
+  a.C = z8;
+  a.ldc = L;
+  a.out_scale = z_scale;
+  a.amax = amax;
+  return dense_gemm_auto<EPI_Q8, 1>(a, T, s);
 }
 
 hipError_t launch_shared_gate_up(const uint16_t* x, const uint16_t* wsg, const uint16_t* wsu,
@@ -108,13 +124,13 @@ hipError_t launch_tile_prefix(const int32_t* offsets, int E, int bm_a, int bm_b,
   return hipGetLastError();
 }
 
-template <int BM, bool GATHER, int EPI>
+template <int BM, bool GATHER, int EPI, bool F8 = false>
 static hipError_t grouped_gemm(GemmArgs a, int64_t rows, hipStream_t s) {
   using C = std::conditional_t<BM == 128, TileStream, TileBig>;
   static_assert(C::bm == BM, "tile height");
-  a.n_tiles = (int)ceil_div(EPI == EPI_SWIGLU ? 2 * (int64_t)a.N : a.N, C::bn);
+  a.n_tiles = (int)ceil_div(epi_swiglu(EPI) ? 2 * (int64_t)a.N : a.N, C::bn);
   const int64_t bound = grouped_mtile_bound(rows, a.E, BM) * a.n_tiles;
-  return launch_gemm<C, true, GATHER, EPI>(a, bound, s);
+  return launch_gemm<C, true, GATHER, EPI, 1, F8>(a, bound, s);
 }
 
 hipError_t launch_gate_up(const uint16_t* z, const int32_t* offsets, const int32_t* row_token,
@@ -158,6 +174,62 @@ hipError_t launch_expert_down(const uint16_t* H, const int32_t* offsets,
   a.ldc = L;
   if (bm == 128) return grouped_gemm<128, false, EPI_F32>(a, rows, s);
   return grouped_gemm<256, false, EPI_F32>(a, rows, s);
+}
+
+// FP8 experts: z8 and the weights are E4M3 with scales (z: one, weights: one
+// per expert); h = bf16(silu(g) u) is written as E4M3 with h_scale and its
+// largest |h| goes to amax.
+hipError_t launch_gate_up_fp8(const uint8_t* z8, const int32_t* offsets, const int32_t* row_token,
+                              const int32_t* tile_prefix, const int32_t* tile_expert,
+                              int32_t* queue, const uint8_t* w_gate, const uint8_t* w_up,
+                              const float* z_scale, const float* wg_scale, const float* wu_scale,
+                              const float* h_scale, uint32_t* amax, int64_t T, int64_t rows,
+                              int E, int L, int F, int bm, uint8_t* H8, hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = z8; a.seg[0].lda = L; a.seg[0].B = w_gate; a.seg[0].B2 = w_up; a.seg[0].ldb = L;
+  a.seg[0].K = L;
+  a.nseg = 1;
+  a.N = F;
+  a.offsets = offsets;
+  a.tile_prefix = tile_prefix;
+  a.tile_expert = tile_expert;
+  a.E = E;
+  a.b_expert_stride = (int64_t)F * L;
+  a.row_token = row_token;
+  a.queue = queue;
+  a.M = (int)T;
+  a.C = H8;
+  a.ldc = F;
+  a.a_scale = z_scale;
+  a.b_scale = wg_scale;
+  a.b2_scale = wu_scale;
+  a.out_scale = h_scale;
+  a.amax = amax;
+  if (bm == 128) return grouped_gemm<128, true, EPI_SWIGLU_Q8, true>(a, rows, s);
+  return grouped_gemm<256, true, EPI_SWIGLU_Q8, true>(a, rows, s);
+}
+
+hipError_t launch_expert_down_fp8(const uint8_t* H8, const int32_t* offsets,
+                                  const int32_t* tile_prefix, const int32_t* tile_expert,
+                                  int32_t* queue, const uint8_t* w_down, const float* h_scale,
+                                  const float* wd_scale, int64_t rows, int E, int L, int F,
+                                  int bm, float* Y, hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = H8; a.seg[0].lda = F; a.seg[0].B = w_down; a.seg[0].ldb = F; a.seg[0].K = F;
+  a.nseg = 1;
+  a.N = L;
+  a.offsets = offsets;
+  a.tile_prefix = tile_prefix;
+  a.tile_expert = tile_expert;
+  a.queue = queue;
+  a.E = E;
+  a.b_expert_stride = (int64_t)L * F;
+  a.C = Y;
+  a.ldc = L;
+  a.a_scale = h_scale;
+  a.b_scale = wd_scale;
+  if (bm == 128) return grouped_gemm<128, false, EPI_F32, true>(a, rows, s);
+  return grouped_gemm<256, false, EPI_F32, true>(a, rows, s);
 }
 
 int device_cu_count() {

@@ -46,6 +46,18 @@
 //   * EPI_SWIGLU: the B tile interleaves 32-row blocks of W_g and W_u for the
 //     same output columns, so each lane holds the gate and up values of the
 //     same (row, column) and applies silu(g) * u before one bf16 store.
+//   * F8: both operands are FP8 E4M3 bytes with per-tensor scales (A: one
+//     activation scale; B: one scale per expert).  A stage row is still 128
+//     (or 64) bytes, now 128 (64) K values, consumed by
+//     v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales (a lane takes
+//     32 contiguous bytes of its row, the same assignment for A and B); the
+//     epilogue multiplies by 1 / (s_A s_B).  EPI_Q8 / EPI_SWIGLU_Q8 write the
+//     bf16-rounded result as FP8 instead (quantized with an output scale, the
+//     conversion clamped to +-448, because the hardware conversion does not
+//     saturate) and record the largest |bf16 value| for delayed scaling: a
+//     running maximum per wave, one integer atomic max per wave at the end
+//     (the bit patterns of non-negative floats order like unsigned integers,
+//     so the result does not depend on the order).
 #pragma once
 
 #include <type_traits>
@@ -57,13 +69,17 @@ namespace moe {
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9)
 constexpr int DENSE_GM = 4;                     // M panels per tile group (dense GEMMs)
 
-enum GemmEpi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_BIAS = 2, EPI_SWIGLU = 3 };
+enum GemmEpi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_BIAS = 2, EPI_SWIGLU = 3, EPI_Q8 = 4,
+               EPI_SWIGLU_Q8 = 5 };
+
+constexpr bool epi_swiglu(int epi) { return epi == EPI_SWIGLU || epi == EPI_SWIGLU_Q8; }
+constexpr float E4M3_MAX = 448.0f;
 
 struct GemmSeg {
-  const uint16_t* A;    // row r at A + arow(r) * lda
-  const uint16_t* B;    // row n at B + n * ldb (+ expert * b_expert_stride)
-  const uint16_t* B2;   // EPI_SWIGLU: the up matrix (B holds the gate matrix)
-  int64_t lda, ldb;
+  const void* A;        // row r at A + arow(r) * lda elements
+  const void* B;        // row n at B + n * ldb (+ expert * b_expert_stride) elements
+  const void* B2;       // SwiGLU: the up matrix (B holds the gate matrix)
+  int64_t lda, ldb;     // in elements (bf16 or fp8)
   int K;
 };
 
@@ -84,7 +100,20 @@ struct GemmArgs {
   const float* bias;           // EPI_F32_BIAS
   int n_tiles;
   int m_tiles;                 // dense
+  // FP8 operands: quantization scales of A (1 value) and of B / B2 (one per
+  // expert; dense: one); EPI_Q8 / EPI_SWIGLU_Q8: output scale and amax slot
+  const float* a_scale;
+  const float* b_scale;
+  const float* b2_scale;
+  const float* out_scale;
+  uint32_t* amax;
 };
+
+// fp32 -> FP8 E4M3 byte, round to nearest even, saturating at +-448
+__device__ __forceinline__ uint8_t f32_to_e4m3_sat(float v) {
+  v = fminf(fmaxf(v, -E4M3_MAX), E4M3_MAX);
+  return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xff);
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -133,8 +162,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool GROUPED, bool GATHER, int EPI,
-          bool BNT, int NSEG>
+          bool BNT, int NSEG, bool F8>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
+  constexpr int ES = F8 ? 1 : 2;                   // operand bytes per element
+  constexpr int KE = BK * 2 / ES;                  // K values per stage (BK * 2 bytes per row)
+  constexpr bool SWG = epi_swiglu(EPI);
+  constexpr bool Q8 = EPI == EPI_Q8 || EPI == EPI_SWIGLU_Q8;
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -148,7 +181,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile / waves");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   (void)WTM;
-  static_assert(EPI != EPI_SWIGLU || WTN % 64 == 0, "swiglu pairs");
+  static_assert(!SWG || WTN % 64 == 0, "swiglu pairs");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4 && LPS * (NSTAGE - 2) < 64, "stages");
   static_assert(NSEG >= 1 && NSEG <= 3 && (!GATHER || NSEG == 1), "K segments");
   __shared__ uint4 smem[NSTAGE * STAGE + 1];
@@ -164,7 +197,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   const int lrow = lane / KCH;                     // row inside a DMA row group
   const int lchunk = (lane % KCH) ^ swz<KCH>(lrow);   // chunk this lane fetches
   const int fr = lane & 31;                        // fragment row inside a 32-row block
-  const int fq = lane >> 5;                        // 8-wide k group inside a 16-wide step
+  const int fq = lane >> 5;                        // which half of a sub-step's K this lane holds
 
   int total;
   if constexpr (GROUPED) total = a.tile_prefix[a.E] * a.n_tiles;
@@ -182,11 +215,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   static_for<0, NSEG>([&](auto sc) {
     constexpr int S = decltype(sc)::value;
     kseg[S] = a.seg[S].K;
-    lda2[S] = (uint32_t)(a.seg[S].lda * 2);
-    ldb2[S] = (uint32_t)(a.seg[S].ldb * 2);
+    lda2[S] = (uint32_t)(a.seg[S].lda * ES);
+    ldb2[S] = (uint32_t)(a.seg[S].ldb * ES);
     ktotal += kseg[S];
   });
-  const int nk = ktotal / BK;
+  const int nk = ktotal / KE;
+  float amax_run = 0.f;     // Q8: largest |bf16 output| this lane wrote
 
   // The queue's tile index is broadcast through the last 16-byte slot of the
   // LDS array (one LDS object only, so the compiler's LDS-DMA alias tracking
@@ -205,6 +239,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
     // ---- decode the tile ----
     int r0, mrows, n_tile;
     int64_t b_off = 0;
+    float dq_b = 1.f, dq_b2 = 1.f;     // F8: 1 / (s_A s_B), 1 / (s_A s_B2)
     if constexpr (GROUPED) {
       // table reads at a uniform address: every lane gets the same value
       const int e = __builtin_amdgcn_readfirstlane(a.tile_expert[t / a.n_tiles]);
@@ -215,7 +250,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       const int m_local = rem - n_tile * mt;
       r0 = __builtin_amdgcn_readfirstlane(a.offsets[e]) + m_local * BM;
       mrows = min(BM, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - r0);
-      b_off = (int64_t)e * a.b_expert_stride;
+      b_off = (int64_t)e * a.b_expert_stride * ES;
+      if constexpr (F8) {
+        dq_b = 1.0f / (a.a_scale[0] * a.b_scale[e]);
+        if constexpr (SWG) dq_b2 = 1.0f / (a.a_scale[0] * a.b2_scale[e]);
+      }
     } else {
       // Groups of DENSE_GM M panels: inside a group the tiles go N tile by N
       // tile with the M panel fastest, so a window of concurrent tiles spans a
@@ -226,9 +265,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       n_tile = r / gm;
       r0 = (g * DENSE_GM + (r - n_tile * gm)) * BM;
       mrows = min(BM, a.M - r0);
+      if constexpr (F8) {
+        dq_b = 1.0f / (a.a_scale[0] * a.b_scale[0]);
+        if constexpr (SWG) dq_b2 = 1.0f / (a.a_scale[0] * a.b2_scale[0]);
+      }
     }
-    const int n0 = EPI == EPI_SWIGLU ? n_tile * (BN / 2) : n_tile * BN;   // first output col
-    const int nrows = min(EPI == EPI_SWIGLU ? BN / 2 : BN, a.N - n0);     // valid B rows per matrix
+    const int n0 = SWG ? n_tile * (BN / 2) : n_tile * BN;   // first output col
+    const int nrows = min(SWG ? BN / 2 : BN, a.N - n0);     // valid B rows per matrix
 
     // per-lane A row byte offsets for GATHER (fixed over the K loop)
     uint32_t a_goff[A_INS];
@@ -240,7 +283,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
         if (rl < mrows) {
           int src = a.row_token[r0 + rl];
           if ((unsigned)src >= (unsigned)a.M) src = 0;   // malformed metadata: row 0
-          off = (uint32_t)((int64_t)src * a.seg[0].lda * 2);
+          off = (uint32_t)((int64_t)src * a.seg[0].lda * ES);
         }
         a_goff[i] = off;
       }
@@ -251,24 +294,27 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
     static_for<0, NSEG>([&](auto sc) {
       constexpr int S = decltype(sc)::value;
       const GemmSeg& g = a.seg[S];
-      if constexpr (GATHER) rA[S] = make_rsrc(g.A, (int64_t)a.M * g.lda * 2);
-      else rA[S] = make_rsrc(g.A + (int64_t)r0 * g.lda, (int64_t)mrows * g.lda * 2);
-      rB[S] = make_rsrc(g.B + b_off + (int64_t)n0 * g.ldb, (int64_t)nrows * g.ldb * 2);
-      if constexpr (EPI == EPI_SWIGLU)
-        rU[S] = make_rsrc(g.B2 + b_off + (int64_t)n0 * g.ldb, (int64_t)nrows * g.ldb * 2);
+      const char* A = (const char*)g.A;
+      const char* B = (const char*)g.B;
+      if constexpr (GATHER) rA[S] = make_rsrc(A, (int64_t)a.M * g.lda * ES);
+      else rA[S] = make_rsrc(A + (int64_t)r0 * g.lda * ES, (int64_t)mrows * g.lda * ES);
+      rB[S] = make_rsrc(B + b_off + (int64_t)n0 * g.ldb * ES, (int64_t)nrows * g.ldb * ES);
+      if constexpr (SWG)
+        rU[S] = make_rsrc((const char*)g.B2 + b_off + (int64_t)n0 * g.ldb * ES,
+                          (int64_t)nrows * g.ldb * ES);
     });
 
     // DMA loads of stage kt.  A stage's instructions are split into NPART
     // parts (instruction i belongs to part i % NPART; PART < 0 = all) so that
     // the loads of a prefetched stage can be spread between the MFMA
     // sub-steps of the stage being computed instead of stalling in one block.
-    constexpr int NPART = BK / 16;
+    constexpr int NPART = F8 ? BK / 32 : BK / 16;   // MFMA sub-steps per stage
     auto issue_seg = [&](auto seg_c, int kt, int k0, auto part_c) {
       constexpr int S = decltype(seg_c)::value;
       constexpr int PART = decltype(part_c)::value;
       uint4* sa = smem + (kt % NSTAGE) * STAGE;
       uint4* sb = sa + BM * KCH;
-      const uint32_t kbytes = (uint32_t)(k0 + lchunk * 8) * 2;
+      const uint32_t kbytes = (uint32_t)k0 * ES + (uint32_t)lchunk * 16;
 #pragma unroll
       for (int i = 0; i < A_INS; ++i) {
         if (!(PART < 0 || i % NPART == PART)) continue;
@@ -283,7 +329,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       for (int i = 0; i < B_INS; ++i) {
         if (!(PART < 0 || (A_INS + i) % NPART == PART)) continue;
         const int rho0 = (wave + i * NW) * RPI;     // a DMA group never straddles a 32-row block
-        if constexpr (EPI == EPI_SWIGLU) {
+        if constexpr (SWG) {
           const int hrow = (rho0 >> 6) * 32 + (rho0 & 31) + lrow;
           const uint32_t off = (uint32_t)hrow * ldb2[S] + kbytes;
           if ((rho0 >> 5) & 1) dma16<BNT>(rU[S], sb + rho0 * KCH, off);
@@ -294,7 +340,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       }
     };
     auto issue = [&](int kt, auto part_c) {
-      int k0 = kt * BK;
+      int k0 = kt * KE;
       if constexpr (NSEG == 1) {
         issue_seg(std::integral_constant<int, 0>{}, kt, k0, part_c);
       } else {
@@ -348,7 +394,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
         static_for<0, NPART>([&](auto kk_c) {
           constexpr int kk = decltype(kk_c)::value;
           if (prefetch) issue(kt + NSTAGE - 1, kk_c);
-          if constexpr (NACT > 0) {
+          if constexpr (NACT > 0 && !F8) {
             // rows 32 (i WM + wrow) + fr all have the same swizzle as row fr
             const int ch = (kk * 2 + fq) ^ swz<KCH>(fr);
             bf16x8 bfr[TN], afr[NACT];
@@ -364,6 +410,32 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
               for (int j = 0; j < TN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[i], bfr[j], acc[i][j],
                                                                     0, 0, 0);
+          } else if constexpr (NACT > 0) {
+            // FP8: a sub-step is 64 K values = 4 chunks; lane half fq takes
+            // chunks 2 fq and 2 fq + 1 (32 contiguous bytes of its row)
+            const int c0 = (kk * 4 + fq * 2) ^ swz<KCH>(fr);
+            const int c1 = (kk * 4 + fq * 2 + 1) ^ swz<KCH>(fr);
+            i32x8 bfr[TN], afr[NACT];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              const uint4 lo = sb[(wn0 + j * 32 + fr) * KCH + c0];
+              const uint4 hi = sb[(wn0 + j * 32 + fr) * KCH + c1];
+              bfr[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+#pragma unroll
+            for (int i = 0; i < NACT; ++i) {
+              const uint4 lo = sa[((i * WM + wrow) * 32 + fr) * KCH + c0];
+              const uint4 hi = sa[((i * WM + wrow) * 32 + fr) * KCH + c1];
+              afr[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+#pragma unroll
+            for (int i = 0; i < NACT; ++i)
+#pragma unroll
+              for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    afr[i], bfr[j], acc[i][j], 0, 0, 0, 127, 0, 127);   // E4M3 x E4M3, scale 2^0
           }
         });
       }
@@ -384,6 +456,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
 
     // ---- epilogue: in a 32x32 block, lane l holds column l & 31 and, in
     // register r, row 8 * (r / 4) + 4 * (l / 32) + r % 4 ----
+    const float oscale = Q8 ? a.out_scale[0] : 1.f;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -391,14 +464,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
         const int rl = (i * WM + wrow) * 32 + 8 * (r >> 2) + 4 * fq + (r & 3);
         if (rl >= mrows) continue;
         const int64_t row = r0 + rl;
-        if constexpr (EPI == EPI_SWIGLU) {
-          uint16_t* out = (uint16_t*)a.C + row * a.ldc;
+        if constexpr (SWG) {
 #pragma unroll
           for (int j = 0; j < TN; j += 2) {
             const int cl = ((wn0 + j * 32) >> 6) * 32 + fr;
             if (cl < nrows) {
-              const float g = acc[i][j][r], u = acc[i][j + 1][r];
-              out[n0 + cl] = f32_to_bf16_rne(g / (1.0f + __expf(-g)) * u);
+              const float g = acc[i][j][r] * dq_b, u = acc[i][j + 1][r] * dq_b2;
+              const uint16_t hb = f32_to_bf16_rne(g / (1.0f + __expf(-g)) * u);
+              if constexpr (EPI == EPI_SWIGLU_Q8) {
+                const float hv = bf16_to_f32(hb);
+                amax_run = fmaxf(amax_run, fabsf(hv));
+                ((uint8_t*)a.C)[row * a.ldc + n0 + cl] = f32_to_e4m3_sat(hv * oscale);
+              } else {
+                ((uint16_t*)a.C)[row * a.ldc + n0 + cl] = hb;
+              }
             }
           }
         } else {
@@ -407,9 +486,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
             const int cl = wn0 + j * 32 + fr;
             if (cl >= nrows) continue;
             const int col = n0 + cl;
-            const float val = acc[i][j][r];
+            const float val = acc[i][j][r] * dq_b;
             if constexpr (EPI == EPI_BF16) {
               ((uint16_t*)a.C)[row * a.ldc + col] = f32_to_bf16_rne(val);
+            } else if constexpr (EPI == EPI_Q8) {
+              const float zv = bf16_to_f32(f32_to_bf16_rne(val));
+              amax_run = fmaxf(amax_run, fabsf(zv));
+              ((uint8_t*)a.C)[row * a.ldc + col] = f32_to_e4m3_sat(zv * oscale);
             } else if constexpr (EPI == EPI_F32_BIAS) {
               ((float*)a.C)[row * a.ldc + col] = val + (a.bias ? a.bias[col] : 0.f);
             } else {
@@ -420,6 +503,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       }
     }
     lds_barrier();     // LDS ring is reused by the next tile's first stages
+  }
+  if constexpr (Q8) {
+    // wave maximum, then one atomic per wave (order-independent: max)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax_run = fmaxf(amax_run, __shfl_xor(amax_run, o));
+    if (lane == 0 && amax_run > 0.f) atomicMax(a.amax, __float_as_uint(amax_run));
   }
 }
 
@@ -453,13 +542,13 @@ using TileBig = TileCfg<256, 256, 64, 2, 4, 2, false>;
 using TileMid = TileCfg<128, 256, 64, 2, 4, 3, false>;
 using TileRouter = TileCfg<64, 128, 64, 2, 2, 4, false>;
 
-template <class C, bool GROUPED, bool GATHER, int EPI, int NSEG = 1>
+template <class C, bool GROUPED, bool GATHER, int EPI, int NSEG = 1, bool F8 = false>
 hipError_t launch_gemm(const GemmArgs& a, int64_t tiles_upper_bound, hipStream_t s) {
   if (tiles_upper_bound <= 0) return hipSuccess;
   if (a.nseg != NSEG) return hipErrorInvalidValue;
   const int grid = persistent_grid(tiles_upper_bound);
   hipLaunchKernelGGL((gemm_kernel<C::bm, C::bn, C::bk, C::wm, C::wn, C::nstage, GROUPED, GATHER,
-                                  EPI, C::bnt, NSEG>),
+                                  EPI, C::bnt, NSEG, F8>),
                      dim3(grid), dim3(64 * C::wm * C::wn), 0, s, a);
   return hipGetLastError();
 }

@@ -50,7 +50,34 @@ hipError_t launch_expert_down(const uint16_t* H, const int32_t* offsets,
                               int32_t* queue, const uint16_t* w_down, int64_t rows, int E, int L,
                               int F, int bm, float* Y, hipStream_t s);
 
+// FP8 experts (expert.hip)
+hipError_t launch_latent_down_q8(const uint16_t* x, const uint16_t* w_dn, int64_t T, int d,
+                                 int L, const float* z_scale, uint32_t* amax, uint8_t* z8,
+                                 hipStream_t s);
+hipError_t launch_gate_up_fp8(const uint8_t* z8, const int32_t* offsets, const int32_t* row_token,
+                              const int32_t* tile_prefix, const int32_t* tile_expert,
+                              int32_t* queue, const uint8_t* w_gate, const uint8_t* w_up,
+                              const float* z_scale, const float* wg_scale, const float* wu_scale,
+                              const float* h_scale, uint32_t* amax, int64_t T, int64_t rows,
+                              int E, int L, int F, int bm, uint8_t* H8, hipStream_t s);
+hipError_t launch_expert_down_fp8(const uint8_t* H8, const int32_t* offsets,
+                                  const int32_t* tile_prefix, const int32_t* tile_expert,
+                                  int32_t* queue, const uint8_t* w_down, const float* h_scale,
+                                  const float* wd_scale, int64_t rows, int E, int L, int F,
+                                  int bm, float* Y, hipStream_t s);
+
 int device_cu_count();
+
+// fp8.hip: per-tensor amax of bf16 tensors (ntensor tensors of numel values,
+// numel a multiple of 8; amax holds float bits), E4M3 quantization with one
+// scale per tensor, delayed-scaling update, and a zero fill
+hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
+hipError_t launch_amax_bf16(const uint16_t* src, int64_t ntensor, int64_t numel, uint32_t* amax,
+                            hipStream_t s);
+hipError_t launch_quantize_e4m3(const uint16_t* src, int64_t ntensor, int64_t numel,
+                                const float* scale, uint8_t* dst, hipStream_t s);
+hipError_t launch_scale_update(float* history, const float* amax, int64_t n, int H, int slot,
+                               float* scale, hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(const float* y_rows, const float* topk_w, const int32_t* assign_row,

@@ -63,6 +63,20 @@ FfnWs ffn_ws(int64_t T, int L, int E, int k, int F) {
   w.total = w.queues + align_up(16 * 4);
   return w;
 }
+// FP8 experts: z and H as E4M3 bytes, then the same tile tables
+FfnWs ffn8_ws(int64_t T, int L, int E, int k, int F) {
+  const size_t mt = (size_t)grouped_mtile_bound(T * k, E, 128);
+  FfnWs w;
+  w.z = 0;
+  w.h = align_up((size_t)T * L);
+  w.pre_a = w.h + align_up((size_t)T * k * F);
+  w.pre_b = w.pre_a + align_up((size_t)(E + 1) * 4);
+  w.exp_a = w.pre_b + align_up((size_t)(E + 1) * 4);
+  w.exp_b = w.exp_a + align_up(mt * 4);
+  w.queues = w.exp_b + align_up(mt * 4);
+  w.total = w.queues + align_up(16 * 4);
+  return w;
+}
 size_t combine_ws(int64_t T, int L) { return align_up((size_t)T * L * 2); }
 
 int check_route_dims(int64_t T, int d, int E, int k) {
@@ -95,6 +109,7 @@ size_t moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t L, int32_t E, i
     case MOE_OP_PERMUTE: return perm_ws(T, E).total;
     case MOE_OP_LATENT_FFN: return (L > 0 && F > 0) ? ffn_ws(T, L, E, k, F).total : 0;
     case MOE_OP_COMBINE: return L > 0 ? combine_ws(T, L) : 0;
+    case MOE_OP_LATENT_FFN_FP8: return (L > 0 && F > 0) ? ffn8_ws(T, L, E, k, F).total : 0;
     default: return 0;
   }
 }
@@ -104,8 +119,8 @@ const char* moe_status_string(int status) {
     case MOE_OK: return "ok";
     case MOE_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size, k < 1 or k > E)";
     case MOE_ERR_UNSUPPORTED:
-      return "unsupported (k > 16, E > 1024, a width not a positive multiple of 64, "
-             "T*k >= 2^31, or a pointer not 16-byte aligned)";
+      return "unsupported (k > 16, E > 1024, a width not a positive multiple of 64 (128 for "
+             "the FP8 expert widths), T*k >= 2^31, or a pointer not 16-byte aligned)";
     case MOE_ERR_WORKSPACE: return "workspace too small (see moe_workspace_bytes)";
     case MOE_ERR_HIP:
       snprintf(g_msg, sizeof g_msg, "HIP error: %s", hipGetErrorString(g_last_hip));
@@ -265,6 +280,98 @@ int moe_combine(const float* y_rows, const float* topk_w, const int32_t* assign_
   if (st) return st;
   EventScope ev(K_LATENT_UP, s);
   return hip_status(launch_latent_up(c, w_lat_up, hs, ws_down, T, d, L, Fs, out, s));
+}
+
+int moe_fp8_amax(const uint16_t* src, int64_t ntensor, int64_t numel, float* amax,
+                 void* stream) {
+  if (ntensor < 0 || numel < 0) return MOE_ERR_INVALID_ARG;
+  if (ntensor == 0) return MOE_OK;
+  if (!amax || (numel > 0 && !src)) return MOE_ERR_INVALID_ARG;
+  if (numel % 8 != 0 || ntensor > 65535 || !aligned16(src)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_amax_bf16(src, ntensor, numel, (uint32_t*)amax, (hipStream_t)stream));
+}
+
+int moe_fp8_quantize(const uint16_t* src, int64_t ntensor, int64_t numel, const float* scale,
+                     uint8_t* dst, void* stream) {
+  if (ntensor < 0 || numel < 0) return MOE_ERR_INVALID_ARG;
+  if (ntensor == 0 || numel == 0) return MOE_OK;
+  if (!src || !scale || !dst) return MOE_ERR_INVALID_ARG;
+  if (numel % 8 != 0 || ntensor > 65535 || !aligned16(src) || !aligned16(dst))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_quantize_e4m3(src, ntensor, numel, scale, dst, (hipStream_t)stream));
+}
+
+int moe_fp8_scale_update(float* history, const float* amax, int64_t ntensor, int32_t hist_len,
+                         int32_t slot, float* scale, void* stream) {
+  if (ntensor < 0 || hist_len < 1 || slot < 0 || slot >= hist_len) return MOE_ERR_INVALID_ARG;
+  if (ntensor == 0) return MOE_OK;
+  if (!history || !amax || !scale) return MOE_ERR_INVALID_ARG;
+  return hip_status(
+      launch_scale_update(history, amax, ntensor, hist_len, slot, scale, (hipStream_t)stream));
+}
+
+int moe_latent_ffn_forward_fp8(const uint16_t* x, const uint16_t* w_lat_down,
+                               const int32_t* expert_offsets, const int32_t* row_token,
+                               const uint8_t* w_gate, const uint8_t* w_up, const uint8_t* w_down,
+                               const float* w_scale, const float* act_scale,
+                               const uint16_t* ws_gate, const uint16_t* ws_up, int64_t T,
+                               int32_t d, int32_t L, int32_t E, int32_t k, int32_t F, int32_t Fs,
+                               float* y_rows, uint16_t* hs, float* act_amax, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (T < 0 || E <= 0 || k < 1 || k > E || Fs < 0) return MOE_ERR_INVALID_ARG;
+  if (k > 16 || E > 1024 || !dims_ok(d) || !dims_ok(L) || !dims_ok(F) ||
+      (Fs > 0 && !dims_ok(Fs)) || T * (int64_t)k >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
+  // one K stage of an FP8 GEMM is 128 values
+  if (L % 128 != 0 || F % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * L >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_lat_down || !expert_offsets || !row_token || !w_gate || !w_up || !w_down ||
+      !w_scale || !act_scale || !y_rows || !act_amax || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (Fs > 0 && (!ws_gate || !ws_up || !hs)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, w_lat_down, w_gate, w_up, w_down, y_rows, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  if (Fs > 0 && (!aligned16(ws_gate) || !aligned16(ws_up) || !aligned16(hs)))
+    return MOE_ERR_UNSUPPORTED;
+  const FfnWs w = ffn8_ws(T, L, E, k, F);
+  if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  uint8_t* z8 = (uint8_t*)(base + w.z);
+  uint8_t* H8 = (uint8_t*)(base + w.h);
+  int32_t* pre_a = (int32_t*)(base + w.pre_a);
+  int32_t* pre_b = (int32_t*)(base + w.pre_b);
+  int32_t* exp_a = (int32_t*)(base + w.exp_a);
+  int32_t* exp_b = (int32_t*)(base + w.exp_b);
+  int32_t* queues = (int32_t*)(base + w.queues);
+  uint32_t* amax = (uint32_t*)act_amax;
+  const int64_t rows = T * k;
+  const ExpertGemmPlan plan = plan_expert_gemms(rows, E);
+  int st = hip_status(launch_zero_u32(amax, 2, s));
+  if (st) return st;
+  {
+    EventScope ev(K_LATENT_DOWN, s);
+    st = hip_status(launch_latent_down_q8(x, w_lat_down, T, d, L, act_scale, amax, z8, s));
+    if (!st && Fs > 0) st = hip_status(launch_shared_gate_up(x, ws_gate, ws_up, T, d, Fs, hs, s));
+  }
+  if (st) return st;
+  st = hip_status(launch_tile_prefix(expert_offsets, E, plan.bm_gate_up, plan.bm_down, pre_a,
+                                     pre_b, exp_a, exp_b, queues, s));
+  if (st) return st;
+  {
+    EventScope ev(K_GATE_UP, s);
+    st = hip_status(launch_gate_up_fp8(z8, expert_offsets, row_token, pre_a, exp_a, queues,
+                                       w_gate, w_up, act_scale, w_scale, w_scale + E,
+                                       act_scale + 1, amax + 1, T, rows, E, L, F,
+                                       plan.bm_gate_up, H8, s));
+  }
+  if (st) return st;
+  EventScope ev(K_EXPERT_DOWN, s);
+  return hip_status(launch_expert_down_fp8(H8, expert_offsets, pre_b, exp_b, queues + 8, w_down,
+                                           act_scale + 1, w_scale + 2 * E, rows, E, L, F,
+                                           plan.bm_down, y_rows, s));
 }
 
 }  // extern "C"

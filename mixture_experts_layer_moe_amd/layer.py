@@ -49,7 +49,7 @@ class LatentMoEBuffers:
         self.y_rows = torch.empty((T * k, L), dtype=f32, device=dev)
         self.hs = torch.empty((T, Fs), dtype=torch.bfloat16, device=dev) if Fs else None
         self.out = torch.empty((T, d), dtype=f32, device=dev)
-        nb = max(_lib.moe_workspace_bytes(op, T, d, L, E, k, F, Fs) for op in range(4))
+        nb = max(_lib.moe_workspace_bytes(op, T, d, L, E, k, F, Fs) for op in range(5))
         # one workspace reused by the four calls (they run in order on one stream)
         self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
 
@@ -67,4 +67,79 @@ def forward(x, w: LatentMoEWeights, k, buf: LatentMoEBuffers, stream=None, route
                                 buf.ws, stream=stream)
     _lib.moe_combine(buf.y_rows, buf.topk_w, buf.assign_row, w.w_lat_up, buf.hs, w.ws_down,
                      buf.out, buf.ws, stream=stream)
+    return buf.out
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 experts with delayed scaling
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+@dataclasses.dataclass
+class LatentMoEFp8Experts:
+    """The routed experts' weights as E4M3 bytes with one scale per expert
+    matrix: w_scale = [s(W_g[0..E)), s(W_u[0..E)), s(W_d[0..E))]."""
+    w_gate: torch.Tensor      # [E, F, L] uint8
+    w_up: torch.Tensor        # [E, F, L] uint8
+    w_down: torch.Tensor      # [E, L, F] uint8
+    w_scale: torch.Tensor     # [3E] fp32
+
+
+def quantize_experts(w: LatentMoEWeights, stream=None) -> LatentMoEFp8Experts:
+    """Quantize each expert matrix with scale 448 / its own amax (all in libmoe
+    kernels: amax, the one-slot scale update, quantization)."""
+    E = w.w_gate.shape[0]
+    dev = w.w_gate.device
+    amax = torch.empty(3 * E, dtype=torch.float32, device=dev)
+    scale = torch.empty(3 * E, dtype=torch.float32, device=dev)
+    for i, t in enumerate((w.w_gate, w.w_up, w.w_down)):
+        _lib.moe_fp8_amax(t, E, amax[i * E:(i + 1) * E], stream=stream)
+    hist = torch.zeros((3 * E, 1), dtype=torch.float32, device=dev)
+    _lib.moe_fp8_scale_update(hist, amax, 0, scale, stream=stream)
+    q = []
+    for i, t in enumerate((w.w_gate, w.w_up, w.w_down)):
+        dst = torch.empty(t.shape, dtype=torch.uint8, device=dev)
+        _lib.moe_fp8_quantize(t, E, scale[i * E:(i + 1) * E], dst, stream=stream)
+        q.append(dst)
+    return LatentMoEFp8Experts(q[0], q[1], q[2], scale)
+
+
+class Fp8Scaling:
+    """Delayed scaling state of the two activation tensors (z, h): an amax
+    history of hist_len steps each, the scales for the next step, and this
+    step's amax.  Scales start at 1 until the first step is recorded."""
+
+    def __init__(self, hist_len=1024, device="cuda"):
+        dev = torch.device(device)
+        self.history = torch.zeros((2, hist_len), dtype=torch.float32, device=dev)
+        self.scale = torch.ones(2, dtype=torch.float32, device=dev)
+        self.amax = torch.zeros(2, dtype=torch.float32, device=dev)
+        self.step = 0
+
+    def update(self, stream=None):
+        _lib.moe_fp8_scale_update(self.history, self.amax, self.step % self.history.shape[1],
+                                  self.scale, stream=stream)
+        self.step += 1
+
+
+def forward_fp8(x, w: LatentMoEWeights, w8: LatentMoEFp8Experts, k, buf: LatentMoEBuffers,
+                scaling: Fp8Scaling, stream=None, route=True, update_scaling=True):
+    """One forward pass with FP8 expert GEMMs: the step uses scaling.scale
+    (from earlier steps' maxima), records this step's maxima and, with
+    update_scaling, folds them into the history for the next step."""
+    if route:
+        _lib.moe_route(x, w.w_router, w.b_router, k, buf.topk_idx, buf.topk_w, ws=buf.ws,
+                       stream=stream)
+    _lib.moe_permute(buf.topk_idx, buf.E, buf.expert_counts, buf.expert_offsets, buf.row_token,
+                     buf.assign_row, buf.ws, stream=stream)
+    _lib.moe_latent_ffn_forward_fp8(x, w.w_lat_down, buf.expert_offsets, buf.row_token, w8.w_gate,
+                                    w8.w_up, w8.w_down, w8.w_scale, scaling.scale, w.ws_gate,
+                                    w.ws_up, k, buf.y_rows, buf.hs, scaling.amax, buf.ws,
+                                    stream=stream)
+    _lib.moe_combine(buf.y_rows, buf.topk_w, buf.assign_row, w.w_lat_up, buf.hs, w.ws_down,
+                     buf.out, buf.ws, stream=stream)
+    if update_scaling:
+        scaling.update(stream=stream)
     return buf.out

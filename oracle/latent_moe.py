@@ -244,19 +244,26 @@ def latent_down(x, w_dn, mode="exact"):
     return _maybe_bf16(np.asarray(x, np.float64) @ np.asarray(w_dn, np.float64).T, mode)
 
 
+def swiglu_activation(z_rows, w_gate, w_up, mode="exact", fp8=None):
+    """h = silu(z W_g^T) * (z W_u^T), as it enters the down projection (bf16 in
+    the bf16_operands and fp8_operands modes)."""
+    if mode == "fp8_operands":
+        s_z, s_g, s_u, _, _ = fp8
+        g = fp8_matmul(z_rows, w_gate, s_z, s_g)
+        u = fp8_matmul(z_rows, w_up, s_z, s_u)
+        return round_bf16(silu(g) * u)
+    g = z_rows @ np.asarray(w_gate, np.float64).T
+    u = z_rows @ np.asarray(w_up, np.float64).T
+    return _maybe_bf16(silu(g) * u, mode)
+
+
 def swiglu_expert(z_rows, w_gate, w_up, w_down, mode="exact", fp8=None):
     """y = (silu(z W_g^T) * (z W_u^T)) W_d^T for the rows routed to one expert.
     fp8_operands mode: ``fp8`` = (s_z, s_gate, s_up, s_h, s_down), the scales
     of the latent, of this expert's three weights and of the activation h."""
+    h = swiglu_activation(z_rows, w_gate, w_up, mode, fp8)
     if mode == "fp8_operands":
-        s_z, s_g, s_u, s_h, s_d = fp8
-        g = fp8_matmul(z_rows, w_gate, s_z, s_g)
-        u = fp8_matmul(z_rows, w_up, s_z, s_u)
-        h = round_bf16(silu(g) * u)
-        return fp8_matmul(h, w_down, s_h, s_d)
-    g = z_rows @ np.asarray(w_gate, np.float64).T
-    u = z_rows @ np.asarray(w_up, np.float64).T
-    h = _maybe_bf16(silu(g) * u, mode)
+        return fp8_matmul(h, w_down, fp8[3], fp8[4])
     return h @ np.asarray(w_down, np.float64).T
 
 

@@ -51,13 +51,13 @@ def experts_of(inp):
     return [(inp["w_gate"][e], inp["w_up"][e], inp["w_down"][e]) for e in range(inp["w_gate"].shape[0])]
 
 
-def oracle_forward(cfg, inp, mode, routing=None):
+def oracle_forward(cfg, inp, mode, routing=None, fp8=None):
     shared = None
     if cfg.Fs:
         shared = (inp["ws_gate"], inp["ws_up"], inp["ws_down"])
     return oracle.forward(inp["x"], inp["w_router"], inp["b_router"], cfg.k, inp["w_dn"],
                           experts_of(inp), inp["w_lat_up"], shared=shared, mode=mode,
-                          routing=routing)
+                          routing=routing, fp8=fp8)
 
 
 def routing_swaps(gpu_idx, ora_idx, logits, gap=ROUTE_GAP):

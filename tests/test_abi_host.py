@@ -23,7 +23,8 @@ def test_library_exports_every_declared_function():
     lib = _lib.load()
     names = declared_functions()
     assert {"moe_route", "moe_route_ex", "moe_permute", "moe_latent_ffn_forward", "moe_combine",
-            "moe_workspace_bytes", "moe_status_string", "moe_set_kernel_events"} <= set(names)
+            "moe_workspace_bytes", "moe_status_string", "moe_set_kernel_events", "moe_fp8_amax",
+            "moe_fp8_quantize", "moe_fp8_scale_update", "moe_latent_ffn_forward_fp8"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -45,6 +46,8 @@ def test_workspace_sizes():
     assert _lib.moe_workspace_bytes(2, T, d, L, E, k, F) == \
         a(T * L * 2) + a(T * k * F * 2) + 2 * a((E + 1) * 4) + 2 * a(mt * 4) + a(16 * 4)
     assert _lib.moe_workspace_bytes(3, T, d, L, E, k, F) == a(T * L * 2)
+    assert _lib.moe_workspace_bytes(4, T, d, L, E, k, F) == \
+        a(T * L) + a(T * k * F) + 2 * a((E + 1) * 4) + 2 * a(mt * 4) + a(16 * 4)
     assert _lib.moe_workspace_bytes(9, T, d, L, E, k, F) == 0
     assert _lib.moe_workspace_bytes(0, -1, d, L, E, k, F) == 0
 
@@ -133,3 +136,41 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_fp8_support_calls_reject_bad_args():
+    lib = _lib.load()
+    # amax: negative sizes, numel not a multiple of 8, misaligned source
+    assert lib.moe_fp8_amax(P, -1, 64, P, None) == -1
+    assert lib.moe_fp8_amax(P, 2, 60, P, None) == -2
+    assert lib.moe_fp8_amax(P + 2, 2, 64, P, None) == -2
+    assert lib.moe_fp8_amax(None, 2, 64, P, None) == -1
+    assert lib.moe_fp8_amax(P, 0, 64, P, None) == 0
+    # quantize
+    assert lib.moe_fp8_quantize(P, 2, 64, None, P, None) == -1
+    assert lib.moe_fp8_quantize(P, 2, 64, P, P + 8, None) == -2
+    assert lib.moe_fp8_quantize(P, 70000, 64, P, P, None) == -2
+    assert lib.moe_fp8_quantize(P, 2, 0, P, P, None) == 0
+    # scale update: slot outside the history
+    assert lib.moe_fp8_scale_update(P, P, 2, 1024, 1024, P, None) == -1
+    assert lib.moe_fp8_scale_update(P, P, 2, 0, 0, P, None) == -1
+    assert lib.moe_fp8_scale_update(P, P, 2, 1024, -1, P, None) == -1
+    assert lib.moe_fp8_scale_update(P, None, 2, 1024, 3, P, None) == -1
+    assert lib.moe_fp8_scale_update(P, P, 0, 1024, 3, P, None) == 0
+
+
+def _ffn8(lib, T=8, d=512, L=256, E=16, k=2, F=512, Fs=0, wsc=P, amax=P, wsb=1 << 40):
+    return lib.moe_latent_ffn_forward_fp8(P, P, P, P, P, P, P, wsc, P, None, None, T, d, L, E, k,
+                                          F, Fs, P, None, amax, P, wsb, None)
+
+
+def test_latent_ffn_fp8_rejects_bad_args():
+    lib = _lib.load()
+    assert _ffn8(lib, L=192) == -2            # FP8 expert widths are multiples of 128
+    assert _ffn8(lib, F=320) == -2
+    assert _ffn8(lib, wsc=None) == -1         # weight scales required
+    assert _ffn8(lib, amax=None) == -1        # amax output required
+    assert _ffn8(lib, k=0) == -1
+    need = _lib.moe_workspace_bytes(4, 8, 512, 256, 16, 2, 512)
+    assert _ffn8(lib, wsb=need - 1) == -3
+    assert _ffn8(lib, T=0) == 0

@@ -1,0 +1,324 @@
+"""GPU parity of the FP8 E4M3 path (delayed-scaled expert GEMMs) against the
+oracle's fp8_operands mode.
+
+* quantization, amax and the delayed-scaling update: bit-exact (bytes and
+  fp32 values) against the oracle's definitions on seeded inputs that include
+  exact ties, values past the saturation point and zeros;
+* the layer on the oracle's routing (router replay): permutation bit-exact;
+  the E4M3 codes of z and h equal the oracle's except where they are the
+  rounding of another value within the error interval of the oracle's exact
+  value (2**-7 relative plus 2**-14 of the tensor's range); y and out
+  within 2e-2 of RMS of the fp8_operands oracle beyond a bound of what the
+  flipped h codes carry (computed from the flips, the weights and the
+  routing); tokens with a flipped z code <= 0.3 of RMS; activation scales are chosen on
+  the host from the oracle's own z and h ranges; the step's recorded maxima
+  of z and h within one bf16 ulp of the oracle's;
+* two identical steps give bitwise identical outputs and maxima.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_moe_amd as moe
+import oracle
+from moe_synth import MoEConfig, device, gen
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny": MoEConfig("tiny8", T=256, d=512, L=256, E=16, k=2, F=512, seed=21),
+    # ragged T and E, F a multiple of 128 but not of the 256-wide weight tile
+    "ragged": MoEConfig("ragged8", T=300, d=320, L=256, E=24, k=3, F=384, seed=23),
+    "shared": MoEConfig("shared8", T=200, d=512, L=256, E=32, k=7, F=384, Fs=640, seed=25),
+    "wide": MoEConfig("wide8", T=130, d=256, L=128, E=1024, k=16, F=128, seed=27),
+    "deep": MoEConfig("deep8", T=2048, d=256, L=256, E=8, k=2, F=512, seed=29),
+    "zipf": MoEConfig("zipf8", T=1024, d=256, L=128, E=64, k=4, F=256, zipf_bias=True, seed=31),
+}
+
+
+@pytest.fixture(scope="module")
+def cuda():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.load()
+    return torch.device("cuda:0")
+
+
+def _e4m3_table():
+    vals = []
+    for code in range(0x7F):
+        e, m = code >> 3, code & 7
+        vals.append((m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+def _encode_e4m3(v):
+    """Bytes of E4M3 values (exact members of the format)."""
+    tab = _e4m3_table()
+    a = np.abs(v)
+    idx = np.searchsorted(tab, a)
+    assert np.all(tab[np.minimum(idx, tab.size - 1)] == a), "not an E4M3 value"
+    return (idx | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def _bf16_tensor(vals, dev):
+    bits = (np.asarray(vals, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    back = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16), back
+
+
+def test_quantize_amax_scale_update_bit_exact(cuda):
+    r = np.random.default_rng(5)
+    n = 3 * 4096
+    raw = r.standard_normal(n) * np.exp(r.uniform(-6, 6, n))
+    tab = _e4m3_table()
+    # exact ties between E4M3 values (at scale 1), zeros, values past 448
+    raw[:126] = (tab[:-1] + tab[1:]) / 2
+    raw[126:130] = [0.0, -0.0, 1000.0, -3e5]
+    src, vals = _bf16_tensor(raw, cuda)           # bf16-exact values on both sides
+    vals = vals.reshape(3, -1)
+    amax = torch.empty(3, dtype=torch.float32, device=cuda)
+    moe.moe_fp8_amax(src, 3, amax)
+    torch.cuda.synchronize()
+    want_amax = np.abs(vals).max(axis=1).astype(np.float32)
+    np.testing.assert_array_equal(amax.cpu().numpy(), want_amax)
+    # scales: 1 (ties land exactly), 448 / amax (the weight recipe), a small one
+    scale_np = np.array([1.0, 448.0 / want_amax[1], 0.37], np.float32)
+    scale = torch.from_numpy(scale_np).to(cuda)
+    dst = torch.empty(src.shape, dtype=torch.uint8, device=cuda)
+    moe.moe_fp8_quantize(src, 3, scale, dst)
+    torch.cuda.synchronize()
+    want = np.concatenate([_encode_e4m3(oracle.quantize_e4m3(vals[t], scale_np[t]))
+                           for t in range(3)])
+    got = dst.cpu().numpy()
+    U.log(f"[fp8 quantize] {int((got != want).sum())} of {got.size} bytes differ")
+    np.testing.assert_array_equal(got, want)
+    # delayed scaling: three steps into a 4-long history
+    H = 4
+    hist = torch.zeros((2, H), dtype=torch.float32, device=cuda)
+    hist_np = np.zeros((2, H), np.float32)
+    sc = torch.empty(2, dtype=torch.float32, device=cuda)
+    for step, am in enumerate([[2.0, 0.0], [0.5, 0.0], [7.0, 3.0]]):
+        a_t = torch.tensor(am, dtype=torch.float32, device=cuda)
+        moe.moe_fp8_scale_update(hist, a_t, step % H, sc)
+        hist_np[:, step % H] = am
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(sc.cpu().numpy(), oracle.fp8_scale_from_history(hist_np))
+    np.testing.assert_array_equal(hist.cpu().numpy(), hist_np)
+
+
+def _weight_scales(host):
+    """Oracle side: 448 / amax of every expert matrix, in float32."""
+    out = {}
+    for n in ("w_gate", "w_up", "w_down"):
+        am = np.abs(host[n]).reshape(host[n].shape[0], -1).max(axis=1).astype(np.float32)
+        out[n] = np.float32(448.0) / am
+    return out
+
+
+def _act_scales(cfg, host, ws, routing):
+    """Oracle side: s_z = 448 / amax(z), s_h = 448 / amax(h) of the routed rows
+    (h computed in fp8_operands mode with s_z), and those maxima."""
+    z = oracle.latent_down(host["x"], host["w_dn"], "bf16_operands")
+    amax_z = float(np.abs(z).max())
+    s_z = np.float32(448.0) / np.float32(amax_z)
+    p = oracle.permute(routing[0], cfg.E)
+    amax_h = 0.0
+    for e in range(cfg.E):
+        a, b = int(p["expert_offsets"][e]), int(p["expert_offsets"][e + 1])
+        if a == b:
+            continue
+        h = oracle.swiglu_activation(z[p["row_token"][a:b]], host["w_gate"][e], host["w_up"][e],
+                                     "fp8_operands", (s_z, ws["w_gate"][e], ws["w_up"][e], 1, 1))
+        amax_h = max(amax_h, float(np.abs(h).max()))
+    s_h = np.float32(448.0) / np.float32(amax_h)
+    return s_z, s_h, amax_z, amax_h
+
+
+_cache = {}
+
+
+def _setup(name, cuda):
+    if name in _cache:
+        return _cache[name]
+    cfg = CASES[name]
+    U.log(f"[fp8 case {name}] {cfg}")
+    host = gen.host_inputs_f64(cfg)
+    dv = device.device_inputs(cfg, cuda)
+    w = moe.LatentMoEWeights(dv["w_router"], dv["b_router"], dv["w_dn"], dv["w_gate"], dv["w_up"],
+                             dv["w_down"], dv["w_lat_up"], dv.get("ws_gate"), dv.get("ws_up"),
+                             dv.get("ws_down"))
+    w8 = moe.quantize_experts(w)
+    torch.cuda.synchronize()
+    ro = oracle.route(host["x"], host["w_router"], host["b_router"], cfg.k)
+    routing = (ro["topk_idx"], np.asarray(ro["topk_w"], np.float32).astype(np.float64))
+    _cache[name] = (cfg, host, dv, w, w8, routing)
+    return _cache[name]
+
+
+def _code_flips(gpu_bytes, oracle_vals, exact_scaled, rel=2.0 ** -7, abs_tol=448.0 * 2.0 ** -14):
+    """Positions where the GPU's E4M3 code differs from the oracle's (+0 and
+    -0 count as equal).  Each must be a valid rounding of a value within the
+    error interval of the oracle's exact (unrounded, scaled) value x:
+    e4m3(x - tol) <= gpu <= e4m3(x + tol), tol = rel * |x| + abs_tol.  The
+    relative part covers one bf16 step (2**-8) of the operand, which both
+    sides round before quantizing; the absolute part covers the
+    accumulation-order difference (fp32 vs float64) of the GEMM sums the
+    operand comes from, which does not shrink with the operand: 2**-14 of
+    the tensor's full range (its scale maps the largest |value| to 448).
+    Raises otherwise; returns the flat indices of the flips."""
+    tab = _e4m3_table()
+    g = gpu_bytes.ravel().astype(np.int64)
+    o = _encode_e4m3(oracle_vals.ravel()).astype(np.int64)
+    g = np.where(g == 0x80, 0, g)      # -0 == +0
+    o = np.where(o == 0x80, 0, o)
+    bad = np.nonzero(g != o)[0]
+    if bad.size == 0:
+        return bad
+    gm = g[bad] & 0x7F
+    gv = np.where(g[bad] & 0x80, -1.0, 1.0) * tab[np.minimum(gm, tab.size - 1)]
+    ov = oracle_vals.ravel()[bad]
+    x = exact_scaled.ravel()[bad]
+    tol = rel * np.abs(x) + abs_tol
+    lo, hi = oracle.round_e4m3(x - tol), oracle.round_e4m3(x + tol)
+    ok = (gm < 0x7F) & (lo <= gv) & (gv <= hi)
+    if not np.all(ok):
+        w = np.nonzero(~ok)[0][:6]
+        detail = "; ".join(f"i={int(bad[q])} gpu={gv[q]:.6g} oracle={ov[q]:.6g} exact={x[q]:.8g}"
+                           for q in w)
+        raise AssertionError(f"{int((~ok).sum())} E4M3 codes are not a rounding of a value "
+                             f"within the error interval: {detail}")
+    return bad
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layer_fp8_with_oracle_routing(cuda, name):
+    """Experts in FP8 on the oracle's routing (router replay).
+
+    Quantized operands: the GPU's E4M3 codes of z and h (read from the
+    workspace) equal the oracle's except for valid roundings within the
+    error interval (see _code_flips).
+    Outputs: within 2e-2 of RMS of the fp8_operands oracle beyond the bound
+    of what the flipped h codes carry; tokens with a flipped z code (whose
+    effect runs through the nonlinearity) are held to 0.3 of RMS."""
+    cfg, host, dv, w, w8, routing = _setup(name, cuda)
+    ws = _weight_scales(host)
+    got_ws = w8.w_scale.cpu().numpy().reshape(3, cfg.E)
+    for i, n in enumerate(("w_gate", "w_up", "w_down")):
+        np.testing.assert_array_equal(got_ws[i], ws[n], err_msg=n)
+    s_z, s_h, amax_z, amax_h = _act_scales(cfg, host, ws, routing)
+    fp8 = {"z": s_z, "h": s_h, "w_gate": ws["w_gate"], "w_up": ws["w_up"], "w_down": ws["w_down"]}
+    ro = U.oracle_forward(cfg, host, "fp8_operands", routing=routing, fp8=fp8)
+    rb = U.oracle_forward(cfg, host, "bf16_operands", routing=routing)
+
+    buf = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, cfg.Fs, device=cuda)
+    buf.topk_idx.copy_(torch.from_numpy(np.asarray(routing[0], np.int32)))
+    buf.topk_w.copy_(torch.from_numpy(np.asarray(routing[1], np.float32)))
+    sc = moe.Fp8Scaling(hist_len=1024, device=cuda)
+    sc.scale.copy_(torch.tensor([s_z, s_h], dtype=torch.float32))
+    moe.moe_permute(buf.topk_idx, cfg.E, buf.expert_counts, buf.expert_offsets, buf.row_token,
+                    buf.assign_row, buf.ws)
+    moe.moe_latent_ffn_forward_fp8(dv["x"], w.w_lat_down, buf.expert_offsets, buf.row_token,
+                                   w8.w_gate, w8.w_up, w8.w_down, w8.w_scale, sc.scale, w.ws_gate,
+                                   w.ws_up, cfg.k, buf.y_rows, buf.hs, sc.amax, buf.ws)
+    torch.cuda.synchronize()
+    # the workspace holds z (E4M3, [T, L]) then H (E4M3, [T*k, F], expert order)
+    wsb = buf.ws.cpu().numpy()
+    h_off = (cfg.T * cfg.L + 255) // 256 * 256
+    z8 = wsb[:cfg.T * cfg.L].reshape(cfg.T, cfg.L)
+    h8 = wsb[h_off:h_off + cfg.T * cfg.k * cfg.F].reshape(cfg.T * cfg.k, cfg.F)
+    moe.moe_combine(buf.y_rows, buf.topk_w, buf.assign_row, w.w_lat_up, buf.hs, w.ws_down,
+                    buf.out, buf.ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(U.to_np(buf.row_token), ro["row_token"])
+    np.testing.assert_array_equal(U.to_np(buf.assign_row), ro["assign_row"])
+
+    # codes of z
+    z_exact = oracle.latent_down(host["x"], host["w_dn"], "exact")
+    zq = oracle.quantize_e4m3(ro["z"], s_z)
+    zf = _code_flips(z8, zq, z_exact * float(s_z))
+    flipped = set((zf // cfg.L).tolist())
+    # codes of h, rows of tokens whose z codes all agree
+    rt = ro["row_token"]
+    offs = ro["expert_offsets"]
+    hq = np.zeros((cfg.T * cfg.k, cfg.F))
+    h_exact = np.zeros((cfg.T * cfg.k, cfg.F))
+    for e in range(cfg.E):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if a == b:
+            continue
+        zr = ro["z"][rt[a:b]]
+        g = oracle.fp8_matmul(zr, host["w_gate"][e], s_z, ws["w_gate"][e])
+        u = oracle.fp8_matmul(zr, host["w_up"][e], s_z, ws["w_up"][e])
+        h_exact[a:b] = oracle.silu(g) * u
+        hq[a:b] = oracle.quantize_e4m3(oracle.round_bf16(h_exact[a:b]), s_h)
+    keep = np.array([t not in flipped for t in rt])
+    kept_rows = np.nonzero(keep)[0]
+    hf = _code_flips(h8[keep], hq[keep], h_exact[keep] * float(s_h))
+    # Where a code of h flipped, the oracle's y and out may legitimately
+    # differ from the GPU's by what that one E4M3 step carries through the
+    # down projection, the combine and the up projection.  Bound it (triangle
+    # inequality): dy[r] <= sum over flipped f of |step| * |Wd_q[e](:, f)|;
+    # dc[t] <= sum_j w[t,j] dy[row(t,j)], plus one bf16 step of c (the
+    # perturbed c may round the other way); dout[t] <= |W_up| dc[t].
+    tab = _e4m3_table()
+    dy = np.zeros((cfg.T * cfg.k, cfg.L))
+    if hf.size:
+        rows = kept_rows[hf // cfg.F]
+        cols = hf % cfg.F
+        g8 = h8[keep].ravel()[hf].astype(np.int64) & 0x7F
+        o8 = _encode_e4m3(hq[keep].ravel()[hf]).astype(np.int64) & 0x7F
+        step = np.abs(tab[np.minimum(g8, 126)] - tab[np.minimum(o8, 126)]) / float(s_h)
+        exp_of_row = np.searchsorted(offs, rows, side="right") - 1
+        for r_, c_, st_, e_ in zip(rows, cols, step, exp_of_row):
+            wd = oracle.quantize_e4m3(host["w_down"][e_][:, c_], ws["w_down"][e_]) / \
+                float(ws["w_down"][e_])
+            dy[r_] += st_ * np.abs(wd)
+    w_t = np.asarray(routing[1])
+    dc = np.zeros((cfg.T, cfg.L))
+    for j in range(cfg.k):
+        dc += w_t[:, j:j + 1] * dy[ro["assign_row"][:, j]]
+    dc += np.where(dc > 0, np.abs(ro["c"]) * 2.0 ** -8, 0.0)
+    dout = dc @ np.abs(host["w_lat_up"]).T
+    clean = np.array([t not in flipped for t in range(cfg.T)])
+
+    am = sc.amax.cpu().numpy().astype(np.float64)
+    out = U.to_np(buf.out)
+    y = U.to_np(buf.y_rows)
+    rms_out = np.sqrt(np.mean(ro["out"] ** 2))
+    rms_y = np.sqrt(np.mean(ro["y_rows"] ** 2))
+    excess_y = np.abs(y - ro["y_rows"]) - dy
+    excess_o = np.abs(out - ro["out"]) - dout
+    ea = U.rel_err(out, ro["out"])
+    eb = U.rel_err(out, rb["out"])
+    U.log(f"[fp8 {name}] code flips: z {zf.size} of {z8.size}, h {hf.size} of {int(keep.sum()) * cfg.F}"
+          f"; out vs fp8 oracle max/rms {ea[0]:.2e}/{ea[1]:.2e}, beyond the flip bound "
+          f"{excess_o.max() / rms_out:.2e} (y {excess_y.max() / rms_y:.2e}); vs bf16 oracle "
+          f"{eb[0]:.2e}/{eb[1]:.2e}; amax z {am[0]:.5g} (oracle {amax_z:.5g}), h {am[1]:.5g} "
+          f"(oracle {amax_h:.5g})")
+    assert excess_y[keep].max() <= U.OUT_TOL * rms_y
+    assert excess_o[clean].max() <= U.OUT_TOL * rms_out
+    # tokens with a flipped z code: validity only
+    if (~clean).any():
+        assert np.abs(out - ro["out"])[~clean].max() <= 0.3 * rms_out
+    # maxima of bf16 values: equal up to one bf16 rounding step of the largest element
+    assert abs(am[0] - amax_z) <= amax_z * 2.0 ** -8
+    assert abs(am[1] - amax_h) <= amax_h * 2.0 ** -7
+
+
+def test_fp8_steps_are_deterministic_and_history_advances(cuda):
+    cfg, host, dv, w, w8, routing = _setup("zipf", cuda)
+    buf = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, cfg.Fs, device=cuda)
+    sc = moe.Fp8Scaling(hist_len=8, device=cuda)
+    outs, maxima = [], []
+    for _ in range(3):
+        moe.forward_fp8(dv["x"], w, w8, cfg.k, buf, sc)
+        torch.cuda.synchronize()
+        outs.append(buf.out.clone())
+        maxima.append(sc.amax.clone())
+    # step 0 ran with unit scales; steps 1 and 2 with the same history maxima
+    assert torch.equal(outs[1], outs[2]) and torch.equal(maxima[1], maxima[2])
+    hist = sc.history.cpu().numpy()
+    np.testing.assert_array_equal(hist[:, 3:], 0.0)
+    np.testing.assert_array_equal(sc.scale.cpu().numpy(), oracle.fp8_scale_from_history(hist))
+    U.log(f"[fp8 steps] scales after 3 steps {sc.scale.cpu().numpy()}")
