@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
 MFMA_BF16_PEAK = 2.5e15    # MI355X dense bf16 MFMA, FLOP/s
+MFMA_FP8_PEAK = 5.0e15     # MI355X dense fp8 MFMA, FLOP/s
 METRIC = "LatentMoE layer fwd tokens/sec on 1 MI355X; % bf16 MFMA peak / % HBM BW"
 KERNEL_NAMES = ["router_gemm", "router_topk", "permute", "latent_down", "gate_up",
                 "expert_down", "combine", "latent_up"]
@@ -46,6 +47,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="base1_small_batch")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--fp8", action="store_true",
+                   help="routed experts' GEMMs in FP8 E4M3 with delayed scaling (not the headline "
+                        "configuration, which is bf16)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain device copy of known size (for HBM counter scaling)")
     return p.parse_args()
@@ -97,33 +101,35 @@ def stored_traffic(config_name):
     return rec.get("traffic_bytes_per_launch")
 
 
-def dominant_work(cfg, counts):
+def dominant_work(cfg, counts, esize=2):
     """Algorithmic FLOPs and bytes of one launch of the grouped gate/up GEMM:
     2 GEMMs of 2*rows*L*F FLOPs; bytes = gate+up weights of every expert that
-    received a row (each read once) + the gathered latent rows (bf16) + H out."""
+    received a row (each read once) + the gathered latent rows + H out, all
+    of esize bytes per value (2: bf16, 1: FP8 E4M3)."""
     import numpy as np
     touched = int(np.count_nonzero(counts))
     rows = cfg.T * cfg.k
     flops = 4.0 * rows * cfg.L * cfg.F
-    nbytes = touched * 2.0 * cfg.F * cfg.L * 2 + rows * cfg.L * 2.0 + rows * cfg.F * 2.0
+    nbytes = (touched * 2.0 * cfg.F * cfg.L + rows * cfg.L + rows * cfg.F) * esize
     return flops, nbytes, touched
 
 
-def layer_bytes(cfg, touched):
-    """Algorithmic HBM bytes of the whole layer: weights touched once, x in,
-    fp32 out (intermediates excluded)."""
+def layer_bytes(cfg, touched, esize=2):
+    """Algorithmic HBM bytes of the whole layer: weights touched once (expert
+    weights esize bytes per value), x in, fp32 out (intermediates excluded)."""
     T, d, L, E, F, Fs = cfg.T, cfg.d, cfg.L, cfg.E, cfg.F, cfg.Fs
-    w = touched * 3.0 * F * L * 2 + 2.0 * d * L * 2 + E * d * 4.0 + 3.0 * d * Fs * 2
+    w = touched * 3.0 * F * L * esize + 2.0 * d * L * 2 + E * d * 4.0 + 3.0 * d * Fs * 2
     return w + T * d * 2.0 + T * d * 4.0
 
 
-def cpu_baseline(cfg, n_tok=256, n_exp=8, seed=0):
+def cpu_baseline(cfg, n_tok=256, n_exp=8, seed=0, fp8=False):
     """The oracle (float64 numpy, as it stands) on a bounded sample of the
     workload, extrapolated to tokens/s of the whole layer:
       router + permutation over all T tokens (timed in full),
       latent down, combine and up-projection on n_tok tokens (x T/n_tok),
       n_exp experts' SwiGLU FFNs on their routed rows (x E/n_exp).
-    Input generation is not timed."""
+    Input generation is not timed.  fp8: the experts in the oracle's
+    fp8_operands mode (scales from the sample's own ranges)."""
     import numpy as np
     import oracle
     from moe_synth import gen
@@ -165,8 +171,15 @@ def cpu_baseline(cfg, n_tok=256, n_exp=8, seed=0):
         wts = gen.expert_weights_f64(cfg, int(e))
         a, bnd = int(p["expert_offsets"][e]), int(p["expert_offsets"][e + 1])
         zr = oracle.latent_down(x[p["row_token"][a:bnd]], w_dn, "bf16_operands")
+        sc = None
+        if fp8:
+            s_w = [np.float32(448.0) / np.float32(np.abs(wt).max()) for wt in wts]
+            s_z = np.float32(448.0) / np.float32(np.abs(zr).max())
+            sc = (s_z, s_w[0], s_w[1], np.float32(1.0), s_w[2])
+            h = oracle.swiglu_activation(zr, wts[0], wts[1], "fp8_operands", sc)
+            sc = (s_z, s_w[0], s_w[1], np.float32(448.0) / np.float32(np.abs(h).max()), s_w[2])
         t0 = time.perf_counter()
-        oracle.swiglu_expert(zr, *wts, mode="bf16_operands")
+        oracle.swiglu_expert(zr, *wts, mode="fp8_operands" if fp8 else "bf16_operands", fp8=sc)
         t_exp += time.perf_counter() - t0
         rows_done += bnd - a
         del wts
@@ -175,7 +188,8 @@ def cpu_baseline(cfg, n_tok=256, n_exp=8, seed=0):
     total = t_route + t_tok * cfg.T / len(toks) + t_exp_total
     return {
         "value": cfg.T / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"float64 numpy oracle: router + permutation over all {cfg.T} tokens "
+        "sample": (f"float64 numpy oracle{' (experts in fp8_operands mode)' if fp8 else ''}: "
+                   f"router + permutation over all {cfg.T} tokens "
                    f"({t_route:.2f} s), latent down/combine/up on {len(toks)} tokens "
                    f"({t_tok:.2f} s, scaled x{cfg.T / len(toks):.0f}), SwiGLU experts on "
                    f"{len(sample)} sampled experts = {rows_done} routed rows ({t_exp:.2f} s, "
@@ -205,6 +219,19 @@ def main():
                              dv.get("ws_down"))
     buf = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, cfg.Fs, device=dev)
     x = dv["x"]
+    step = lambda: moe.forward(x, w, cfg.k, buf)  # noqa: E731
+    if args.fp8:
+        # weights quantized once (448 / amax per expert matrix); the bf16
+        # expert weights are then dropped; activation scales are delayed:
+        # each step uses the history of the previous steps' maxima
+        w8 = moe.quantize_experts(w)
+        torch.cuda.synchronize()
+        w.w_gate = w.w_up = w.w_down = None
+        for n in ("w_gate", "w_up", "w_down"):
+            del dv[n]
+        torch.cuda.empty_cache()
+        scaling = moe.Fp8Scaling(hist_len=1024, device=dev)
+        step = lambda: moe.forward_fp8(x, w, w8, cfg.k, buf, scaling)  # noqa: E731
     torch.cuda.synchronize()
 
     if args.copy_calibration:
@@ -217,7 +244,7 @@ def main():
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        moe.forward(x, w, cfg.k, buf)
+        step()
     torch.cuda.synchronize()
 
     hip = HipEvents()
@@ -228,7 +255,7 @@ def main():
     for i in range(args.steps):
         for name in KERNEL_NAMES:
             moe.moe_set_kernel_events(name, *ev[name][i])
-        moe.forward(x, w, cfg.k, buf)
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for name in KERNEL_NAMES:
@@ -244,36 +271,41 @@ def main():
     ms_per_step = elapsed / args.steps * 1e3
     value = cfg.T * args.steps / elapsed
     counts = buf.expert_counts.cpu().numpy()
-    flops, nbytes, touched = dominant_work(cfg, counts)
+    esize = 1 if args.fp8 else 2
+    mfma_peak = MFMA_FP8_PEAK if args.fp8 else MFMA_BF16_PEAK
+    flops, nbytes, touched = dominant_work(cfg, counts, esize)
     dom_s = kern_ms[DOMINANT] * 1e-3
     ai = flops / nbytes
-    if ai < MFMA_BF16_PEAK / HBM_PEAK:
+    if ai < mfma_peak / HBM_PEAK:
         roof = {"bound": "hbm", "achieved": nbytes / dom_s / 1e9, "peak": HBM_PEAK / 1e9,
                 "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": flops / dom_s / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
+        roof = {"bound": "mfma", "achieved": flops / dom_s / 1e12, "peak": mfma_peak / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = stored_traffic(cfg.name)
-    roof["kernel"] = "grouped gate/up GEMM + SwiGLU (gemm_kernel GROUPED GATHER EPI_SWIGLU)"
+    roof["traffic"] = stored_traffic(cfg.name + ("_fp8" if args.fp8 else ""))
+    roof["kernel"] = ("grouped gate/up GEMM + SwiGLU (gemm_kernel GROUPED GATHER EPI_SWIGLU"
+                      + (" FP8 E4M3, E4M3 output)" if args.fp8 else ")"))
     roof["algorithmic_per_launch"] = {"flops": flops, "bytes": nbytes, "experts_touched": touched}
 
     step_s = ms_per_step * 1e-3
     layer = {
-        "mfma_frac": cfg.flops() / step_s / MFMA_BF16_PEAK,
-        "hbm_frac": layer_bytes(cfg, touched) / step_s / HBM_PEAK,
+        "mfma_frac": cfg.flops() / step_s / mfma_peak,
+        "hbm_frac": layer_bytes(cfg, touched, esize) / step_s / HBM_PEAK,
         "kernels_ms": {k: round(v, 4) for k, v in kern_ms.items()},
     }
 
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg)
+        cpu = cpu_baseline(cfg, fp8=args.fp8)
 
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3 (expert GEMMs; bf16 latent projections)" if args.fp8 else "bf16",
+        "data": "synthetic",
         "config": {"workload": cfg.description, "T": cfg.T, "d": cfg.d, "latent": cfg.L,
                    "experts": cfg.E, "top_k": cfg.k, "ffn": cfg.F, "shared_ffn": cfg.Fs,
                    "seed": cfg.seed},
