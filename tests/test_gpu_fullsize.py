@@ -120,3 +120,124 @@ def test_full_size_parity(cuda, name):
     eo = U.rel_err(out_rows, ref["out"])
     U.log(f"[full {name}] sampled out err max/rms {eo[0]:.2e}/{eo[1]:.2e}")
     assert eo[0] <= U.OUT_TOL
+
+
+FULL_FP8 = {"base1_small_batch": 2, "base1_compute": 2}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(FULL_FP8))
+def test_full_size_fp8_parity(cuda, name):
+    """The FP8 expert path at full size (bench.py --fp8's launch configuration:
+    quantized weights, the bf16 copies dropped), on sampled tokens: their
+    E4M3 codes of z and h must equal the oracle's except for valid roundings
+    within the accumulation-error interval, and their outputs must match the
+    fp8_operands oracle to 2e-2 of RMS beyond the bound of what the flipped h
+    codes carry (as in the small-shape FP8 tests).  Activation scales are
+    chosen on the host: s_z = 448 / amax of the oracle's z, s_h = 448 / 16."""
+    from tests.test_gpu_fp8 import _code_flips, _e4m3_table, _encode_e4m3
+    cfg = CONFIGS[name]
+    U.log(f"[full fp8 {name}] T={cfg.T}: generating inputs and quantizing experts on the GPU")
+    dv = device.device_inputs(cfg, cuda)
+    w = moe.LatentMoEWeights(dv["w_router"], dv["b_router"], dv["w_dn"], dv["w_gate"], dv["w_up"],
+                             dv["w_down"], dv["w_lat_up"], dv.get("ws_gate"), dv.get("ws_up"),
+                             dv.get("ws_down"))
+    w8 = moe.quantize_experts(w)
+    torch.cuda.synchronize()
+    w.w_gate = w.w_up = w.w_down = None
+    for n in ("w_gate", "w_up", "w_down"):
+        del dv[n]
+    torch.cuda.empty_cache()
+
+    U.log(f"[full fp8 {name}] oracle routing and latent over all tokens")
+    x = gen.host_tensor_f64(cfg, "x")
+    b = gen.router_bias(cfg)
+    ro = oracle.route(x, gen.router_weights(cfg).astype(np.float64),
+                      None if b is None else b.astype(np.float64), cfg.k)
+    w_dn = gen.host_tensor_f64(cfg, "w_dn")
+    z_exact = oracle.latent_down(x, w_dn, "exact")
+    z_bf = oracle.round_bf16(z_exact)
+    s_z = np.float32(448.0) / np.float32(np.abs(z_bf).max())
+    s_h = np.float32(448.0 / 16.0)
+
+    buf = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, cfg.Fs, device=cuda)
+    sc = moe.Fp8Scaling(hist_len=1024, device=cuda)
+    sc.scale.copy_(torch.tensor([s_z, s_h], dtype=torch.float32))
+    U.log(f"[full fp8 {name}] forward pass")
+    moe.moe_route(dv["x"], w.w_router, w.b_router, cfg.k, buf.topk_idx, buf.topk_w, ws=buf.ws)
+    moe.moe_permute(buf.topk_idx, cfg.E, buf.expert_counts, buf.expert_offsets, buf.row_token,
+                    buf.assign_row, buf.ws)
+    moe.moe_latent_ffn_forward_fp8(dv["x"], w.w_lat_down, buf.expert_offsets, buf.row_token,
+                                   w8.w_gate, w8.w_up, w8.w_down, w8.w_scale, sc.scale, w.ws_gate,
+                                   w.ws_up, cfg.k, buf.y_rows, buf.hs, sc.amax, buf.ws)
+    torch.cuda.synchronize()
+    gidx = buf.topk_idx.cpu().numpy()
+    swaps = U.routing_swaps(gidx, ro["topk_idx"], ro["logits"])
+    rng = np.random.default_rng(4321)
+    toks, need = _choose_tokens(ro["topk_idx"], FULL_FP8[name], swaps, rng)
+    ar = buf.assign_row.cpu().numpy()
+    h_off = (cfg.T * cfg.L + 255) // 256 * 256
+    z8 = buf.ws[:cfg.T * cfg.L].view(cfg.T, cfg.L)[torch.from_numpy(toks).to(cuda)].cpu().numpy()
+    h8_all = buf.ws[h_off:h_off + cfg.T * cfg.k * cfg.F].view(cfg.T * cfg.k, cfg.F)
+    rows = ar[toks].ravel()
+    h8 = h8_all[torch.from_numpy(rows.astype(np.int64)).to(cuda)].cpu().numpy()
+    ws_all = w8.w_scale.cpu().numpy().reshape(3, cfg.E)
+    moe.moe_combine(buf.y_rows, buf.topk_w, buf.assign_row, w.w_lat_up, buf.hs, w.ws_down,
+                    buf.out, buf.ws)
+    torch.cuda.synchronize()
+    out_rows = buf.out[torch.from_numpy(toks).to(cuda)].cpu().numpy()
+    del buf, dv, w, w8
+    torch.cuda.empty_cache()
+
+    U.log(f"[full fp8 {name}] oracle on sampled tokens {toks.tolist()} ({len(need)} experts)")
+    experts = gen.LazyExperts(cfg, cache=len(need) + 1)
+    amax = lambda a: np.float32(np.abs(a).max())  # noqa: E731
+    scales = {}
+    for e in sorted(need):
+        wg, wu, wd = experts[e]
+        scales[e] = (np.float32(448.0) / amax(wg), np.float32(448.0) / amax(wu),
+                     np.float32(448.0) / amax(wd))
+        np.testing.assert_array_equal(ws_all[:, e], np.array(scales[e], np.float32))
+    zf = _code_flips(z8, oracle.quantize_e4m3(z_bf[toks], s_z), z_exact[toks] * float(s_z))
+    tab = _e4m3_table()
+    w_up = gen.host_tensor_f64(cfg, "w_lat_up")
+    hf_total, worst = 0, 0.0
+    c = np.zeros((len(toks), cfg.L))
+    dc = np.zeros((len(toks), cfg.L))
+    for i, t in enumerate(toks):
+        for j in range(cfg.k):
+            e = int(ro["topk_idx"][t, j])
+            wg, wu, wd = experts[e]
+            sg, su, sd = scales[e]
+            zr = z_bf[t:t + 1]
+            g = oracle.fp8_matmul(zr, wg, s_z, sg)
+            u = oracle.fp8_matmul(zr, wu, s_z, su)
+            h_ex = oracle.silu(g) * u
+            h_bf = oracle.round_bf16(h_ex)
+            hq = oracle.quantize_e4m3(h_bf, s_h)
+            hrow = h8[i * cfg.k + j:i * cfg.k + j + 1]
+            hf = _code_flips(hrow, hq, h_ex * float(s_h))
+            hf_total += hf.size
+            y = oracle.fp8_matmul(h_bf, wd, s_h, sd)[0]
+            wt = float(np.float32(ro["topk_w"][t, j]))
+            c[i] += wt * y
+            if hf.size:
+                g8 = hrow.ravel()[hf].astype(np.int64) & 0x7F
+                o8 = _encode_e4m3(hq.ravel()[hf]).astype(np.int64) & 0x7F
+                step = np.abs(tab[np.minimum(g8, 126)] - tab[np.minimum(o8, 126)]) / float(s_h)
+                wdq = oracle.quantize_e4m3(wd[:, hf], sd) / float(sd)
+                dc[i] += wt * (np.abs(wdq) @ step)
+    dc += np.where(dc > 0, np.abs(c) * 2.0 ** -8, 0.0)
+    ref = oracle.latent_up(c, w_up, "bf16_operands")
+    if cfg.Fs:
+        shared = tuple(gen.host_tensor_f64(cfg, n) for n in ("ws_gate", "ws_up", "ws_down"))
+        ref = ref + oracle.shared_expert(x[toks], *shared, mode="bf16_operands")
+    dout = dc @ np.abs(w_up).T
+    rms = np.sqrt(np.mean(ref ** 2))
+    excess = (np.abs(out_rows - ref) - dout).max() / rms
+    U.log(f"[full fp8 {name}] code flips z {zf.size} of {z8.size}, h {hf_total} of "
+          f"{len(toks) * cfg.k * cfg.F}; out err max/rms {U.rel_err(out_rows, ref)[0]:.2e}, beyond "
+          f"the flip bound {excess:.2e}")
+    assert zf.size == 0 or np.abs(out_rows - ref).max() <= 0.3 * rms
+    if zf.size == 0:
+        assert excess <= U.OUT_TOL
