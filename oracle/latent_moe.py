@@ -294,6 +294,47 @@ def expert_rows(z, perm, experts, mode="exact", expert_fn=None, fp8=None):
     return y
 
 
+def round_schedule(expert_offsets, capacity, group_size):
+    """Multi-round dropless schedule with a fixed per-expert token capacity
+    ("Frontier Pre-training at Microsoft AI", "Dropless MoE with tunable,
+    fixed-size memory usage"; "MAI-Base-2 ...", the multi-round dropless
+    figure): experts form groups of ``group_size`` consecutive experts (the
+    last group may be smaller); in every round a group of n experts has
+    n * capacity slots, which its experts share (an overloaded expert uses
+    the slots its quieter neighbours leave free); rows overflowing a round go
+    to the next; the round count is global (the largest any group needs).
+
+    Reading: a group's rows are taken in expert order, then token order (the
+    permutation's row order), so round r of group g is the slice
+    [start_g + r * cap_g, start_g + (r + 1) * cap_g) of its row range.  The
+    round's activation buffer has E * capacity rows; group g's slots start at
+    row first_expert(g) * capacity.
+
+    Returns (rounds, plan) with plan[r] = list over experts e of
+    (row_begin, row_end, buffer_row_of_row_begin); empty ranges have
+    row_begin == row_end."""
+    off = np.asarray(expert_offsets, np.int64)
+    E = off.size - 1
+    groups = [(g0, min(g0 + group_size, E)) for g0 in range(0, E, group_size)]
+    rounds = 0
+    for g0, g1 in groups:
+        load = int(off[g1] - off[g0])
+        rounds = max(rounds, -(-load // ((g1 - g0) * capacity)))
+    plan = []
+    for r in range(rounds):
+        rr = []
+        for g0, g1 in groups:
+            cap = (g1 - g0) * capacity
+            w0 = min(int(off[g0]) + r * cap, int(off[g1]))      # the group's window
+            w1 = min(int(off[g1]), w0 + cap)
+            for e in range(g0, g1):
+                b = min(max(int(off[e]), w0), int(off[e + 1]))   # the expert's rows in it
+                en = max(min(int(off[e + 1]), w1), b)
+                rr.append((b, en, g0 * capacity + min(max(b - w0, 0), cap)))
+        plan.append(rr)
+    return rounds, plan
+
+
 # ---------------------------------------------------------------------------
 # A7, A8, A9: combine, up-projection, shared expert
 # ---------------------------------------------------------------------------

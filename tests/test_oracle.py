@@ -517,3 +517,52 @@ def test_fp8_mode_quantizes_expert_operands_only():
     np.testing.assert_allclose(got, y, rtol=1e-12, atol=1e-15)
     rel = np.max(np.abs(f8["out"] - bf["out"])) / np.sqrt(np.mean(bf["out"] ** 2))
     assert 1e-3 < rel < 0.3
+
+
+# ---------------------------------------------------------------------------
+# multi-round dropless schedule (fixed per-expert capacity, borrowing inside
+# expert groups)
+# ---------------------------------------------------------------------------
+
+def test_round_schedule_hand_worked():
+    # 4 experts in groups of 2, capacity 2: group 0 holds 5 + 0 rows (4 slots
+    # per round: expert 0 borrows expert 1's two slots, then overflows into a
+    # second round), group 1 holds 1 + 1 rows (one round)
+    offsets = np.array([0, 5, 5, 6, 7])
+    rounds, plan = om.round_schedule(offsets, capacity=2, group_size=2)
+    assert rounds == 2
+    assert plan[0] == [(0, 4, 0), (5, 5, 4), (5, 6, 4), (6, 7, 5)]
+    assert plan[1] == [(4, 5, 0), (5, 5, 1), (6, 6, 4), (7, 7, 4)]
+
+
+def test_round_schedule_without_borrowing_or_with_one_group():
+    offsets = np.array([0, 5, 5, 6, 7])
+    # groups of one expert: no borrowing, expert 0 needs ceil(5 / 2) = 3 rounds
+    assert om.round_schedule(offsets, 2, 1)[0] == 3
+    # one group of all four: 8 slots per round hold all 7 rows
+    assert om.round_schedule(offsets, 2, 4)[0] == 1
+    # nothing routed: no round
+    assert om.round_schedule(np.zeros(5, np.int64), 2, 2)[0] == 0
+
+
+@pytest.mark.parametrize("capacity,group", [(3, 2), (8, 4), (1, 3), (50, 8)])
+def test_round_schedule_invariants(capacity, group):
+    r = _rng(capacity * 10 + group)
+    counts = r.poisson(r.uniform(0, 20, 13))
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    rounds, plan = om.round_schedule(offsets, capacity, group)
+    E = counts.size
+    seen = np.zeros(offsets[-1], np.int64)
+    for rr in plan:
+        used = np.zeros(E * capacity, np.int64)
+        for e, (b, en, h) in enumerate(rr):
+            assert offsets[e] <= b <= en <= offsets[e + 1]
+            seen[b:en] += 1
+            used[h:h + (en - b)] += 1
+            g0 = e // group * group
+            assert g0 * capacity <= h and h + (en - b) <= min(g0 + group, E) * capacity
+        assert used.max(initial=0) <= 1          # slots of one round never overlap
+    np.testing.assert_array_equal(seen, 1)       # every row in exactly one round
+    loads = [offsets[min(g + group, E)] - offsets[g] for g in range(0, E, group)]
+    caps = [(min(g + group, E) - g) * capacity for g in range(0, E, group)]
+    assert rounds == max(-(-ld // c) for ld, c in zip(loads, caps))
