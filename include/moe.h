@@ -279,6 +279,38 @@ int moe_latent_ffn_forward_fp8(const uint16_t* x, const uint16_t* w_lat_down,
                                float* y_rows, uint16_t* hs, float* act_amax, void* ws,
                                size_t ws_bytes, void* stream);
 
+/* ---- multi-round dropless experts (fixed memory) ---------------------------
+ * "Frontier Pre-training at Microsoft AI", "Dropless MoE with tunable,
+ * fixed-size memory usage" (and the multi-round figure on "MAI-Base-2 ...")
+ * moe_latent_ffn_forward with a fixed per-expert token capacity: experts form
+ * groups of group_size consecutive experts (the last may be smaller); in
+ * every round a group of n experts has n * capacity slots that its experts
+ * share (an overloaded expert uses the slots its neighbours leave free);
+ * rows that do not fit run in the next round; the round count is global.
+ * A group's rows are taken in permutation order (expert, then token), so a
+ * round is a contiguous slice of the group's rows.  The SwiGLU activations
+ * live in a round buffer of E * capacity rows whatever the routing, instead
+ * of T * k rows; each row is computed exactly as by moe_latent_ffn_forward,
+ * so y_rows is bitwise the same.  The host enqueues the most rounds any
+ * routing can need (max over group sizes n of ceil(T * min(k, n) /
+ * (n * capacity))); rounds beyond the routing's own find no rows.
+ *   rounds_out (nullable): int32 on the device, the rounds this routing needs
+ * Other arguments, limits and errors as for moe_latent_ffn_forward;
+ * capacity < 1 or group_size < 1 is MOE_ERR_INVALID_ARG; workspace from
+ * moe_workspace_bytes_rounds (z, the round buffer E*capacity*F*2, row and
+ * tile tables for one round).  MOE_KERNEL_GATE_UP brackets all rounds.
+ */
+size_t moe_workspace_bytes_rounds(int64_t T, int32_t d, int32_t L, int32_t E, int32_t k,
+                                  int32_t F, int32_t Fs, int32_t capacity, int32_t group_size);
+int moe_latent_ffn_forward_rounds(const uint16_t* x, const uint16_t* w_lat_down,
+                                  const int32_t* expert_offsets, const int32_t* row_token,
+                                  const uint16_t* w_gate, const uint16_t* w_up,
+                                  const uint16_t* w_down, const uint16_t* ws_gate,
+                                  const uint16_t* ws_up, int64_t T, int32_t d, int32_t L,
+                                  int32_t E, int32_t k, int32_t F, int32_t Fs, int32_t capacity,
+                                  int32_t group_size, float* y_rows, uint16_t* hs,
+                                  int32_t* rounds_out, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- profiling hook ------------------------------------------------------
  * Register two hipEvent_t (created by the caller) that the library records on
  * the call's stream immediately before and after every launch of `kernel`

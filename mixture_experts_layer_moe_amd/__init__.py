@@ -6,7 +6,9 @@ does not load the library; the first call does, and raises if it is missing.
 """
 from ._lib import (MOE_BIAS_LOGITS, MOE_BIAS_SELECTION, MoEError, load,  # noqa: F401
                    moe_combine, moe_fp8_amax, moe_fp8_quantize, moe_fp8_scale_update,
-                   moe_latent_ffn_forward, moe_latent_ffn_forward_fp8, moe_permute, moe_route,
-                   moe_route_ex, moe_set_kernel_events, moe_status_string, moe_workspace_bytes)
+                   moe_latent_ffn_forward, moe_latent_ffn_forward_fp8,
+                   moe_latent_ffn_forward_rounds, moe_permute, moe_route, moe_route_ex,
+                   moe_set_kernel_events, moe_status_string, moe_workspace_bytes,
+                   moe_workspace_bytes_rounds)
 from .layer import (Fp8Scaling, LatentMoEBuffers, LatentMoEFp8Experts,  # noqa: F401
-                    LatentMoEWeights, forward, forward_fp8, quantize_experts)
+                    LatentMoEWeights, forward, forward_fp8, forward_rounds, quantize_experts)

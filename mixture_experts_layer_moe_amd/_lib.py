@@ -68,6 +68,13 @@ def load():
     lib.moe_latent_ffn_forward_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                _vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32,
                                                _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.moe_workspace_bytes_rounds.restype = _sz
+    lib.moe_workspace_bytes_rounds.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                               _i32]
+    lib.moe_latent_ffn_forward_rounds.restype = ctypes.c_int
+    lib.moe_latent_ffn_forward_rounds.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                  _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                  _i32, _vp, _vp, _vp, _vp, _sz, _vp]
     lib.moe_set_kernel_events.restype = ctypes.c_int
     lib.moe_set_kernel_events.argtypes = [ctypes.c_int, _vp, _vp]
     _lib = lib
@@ -256,3 +263,29 @@ def moe_latent_ffn_forward_fp8(x, w_lat_down, expert_offsets, row_token, w_gate,
         _ptr(w_up), _ptr(w_down), _ptr(w_scale), _ptr(act_scale), _ptr(ws_gate), _ptr(ws_up), T,
         d, L, E, k, F, Fs, _ptr(y_rows), _ptr(hs), _ptr(act_amax), _ptr(ws), _nbytes(ws),
         _stream(stream)))
+
+
+def moe_workspace_bytes_rounds(T, d, L, E, k, F, Fs, capacity, group_size):
+    return int(load().moe_workspace_bytes_rounds(T, d, L, E, k, F, Fs, capacity, group_size))
+
+
+def moe_latent_ffn_forward_rounds(x, w_lat_down, expert_offsets, row_token, w_gate, w_up, w_down,
+                                  ws_gate, ws_up, k, capacity, group_size, y_rows, hs, rounds_out,
+                                  ws, stream=None):
+    for n, t in (("x", x), ("w_lat_down", w_lat_down), ("w_gate", w_gate), ("w_up", w_up),
+                 ("w_down", w_down), ("ws_gate", ws_gate), ("ws_up", ws_up), ("hs", hs)):
+        _need(t, n, torch.bfloat16)
+    _need(expert_offsets, "expert_offsets", torch.int32, 1)
+    _need(row_token, "row_token", torch.int32, 1)
+    _need(y_rows, "y_rows", torch.float32, 2)
+    _need(rounds_out, "rounds_out", torch.int32)
+    _need(ws, "ws", torch.uint8, 1)
+    T, d = x.shape
+    L = w_lat_down.shape[0]
+    E, F = w_gate.shape[0], w_gate.shape[1]
+    Fs = 0 if ws_gate is None else ws_gate.shape[0]
+    _check("moe_latent_ffn_forward_rounds", load().moe_latent_ffn_forward_rounds(
+        _ptr(x), _ptr(w_lat_down), _ptr(expert_offsets), _ptr(row_token), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), T, d, L, E, k, F, Fs,
+        int(capacity), int(group_size), _ptr(y_rows), _ptr(hs), _ptr(rounds_out), _ptr(ws),
+        _nbytes(ws), _stream(stream)))

@@ -124,6 +124,73 @@ hipError_t launch_tile_prefix(const int32_t* offsets, int E, int bm_a, int bm_b,
   return hipGetLastError();
 }
 
+// One round of the multi-round dropless schedule (the schedule is described
+// with moe_latent_ffn_forward_rounds in include/moe.h): expert e's rows this
+// round, their place in the round's activation buffer, and the same tile
+// tables as tile_prefix_kernel for the clipped row ranges.  Round 0 also
+// writes the number of rounds the routing needs.
+__global__ __launch_bounds__(1024) void round_tables_kernel(
+    const int32_t* __restrict__ offsets, int E, int G, int C, int round, int bm_a, int bm_b,
+    int32_t* __restrict__ seg_start, int32_t* __restrict__ seg_end, int32_t* __restrict__ h_base,
+    int32_t* __restrict__ pre_a, int32_t* __restrict__ pre_b, int32_t* __restrict__ exp_a,
+    int32_t* __restrict__ exp_b, int32_t* __restrict__ queues, int32_t* __restrict__ rounds_out) {
+  __shared__ int red[32];
+  const int e = threadIdx.x;
+  if (e < 16) queues[e] = 0;
+  int rows = 0, need = 0;
+  if (e < E) {
+    const int g0 = e / G * G, g1 = min(g0 + G, E);
+    const int64_t cap = (int64_t)(g1 - g0) * C;
+    const int64_t lo = offsets[g0], hi = offsets[g1];
+    const int64_t w0 = min(lo + (int64_t)round * cap, hi);
+    const int64_t w1 = min(hi, w0 + cap);
+    const int64_t b = min(max((int64_t)offsets[e], w0), (int64_t)offsets[e + 1]);
+    const int64_t en = max(min((int64_t)offsets[e + 1], w1), b);
+    seg_start[e] = (int32_t)b;
+    seg_end[e] = (int32_t)en;
+    h_base[e] = (int32_t)((int64_t)g0 * C + min(max(b - w0, (int64_t)0), cap));
+    rows = (int)(en - b);
+    if (e == g0) need = (int)((hi - lo + cap - 1) / cap);   // this group's rounds
+  }
+  const int ma = e < E ? (rows + bm_a - 1) / bm_a : 0;
+  const int mb = e < E ? (rows + bm_b - 1) / bm_b : 0;
+  int ta, tb;
+  const int ea = block_exclusive_scan(ma, &ta);
+  const int eb = block_exclusive_scan(mb, &tb);
+  if (e < E) {
+    pre_a[e] = ea;
+    pre_b[e] = eb;
+    for (int i = 0; i < ma; ++i) exp_a[ea + i] = e;
+    for (int i = 0; i < mb; ++i) exp_b[eb + i] = e;
+  }
+  if (e == 0) {
+    pre_a[E] = ta;
+    pre_b[E] = tb;
+  }
+  if (round == 0 && rounds_out != nullptr) {
+    // maximum over groups (integer, order-independent)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) need = max(need, __shfl_xor(need, o));
+    if ((e & 63) == 0) red[e >> 6] = need;
+    __syncthreads();
+    if (e == 0) {
+      int m = 0;
+      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) m = max(m, red[w]);
+      rounds_out[0] = m;
+    }
+  }
+}
+
+hipError_t launch_round_tables(const int32_t* offsets, int E, int G, int C, int round, int bm_a,
+                               int bm_b, int32_t* seg_start, int32_t* seg_end, int32_t* h_base,
+                               int32_t* pre_a, int32_t* pre_b, int32_t* exp_a, int32_t* exp_b,
+                               int32_t* queues, int32_t* rounds_out, hipStream_t s) {
+  hipLaunchKernelGGL(round_tables_kernel, dim3(1), dim3(1024), 0, s, offsets, E, G, C, round, bm_a,
+                     bm_b, seg_start, seg_end, h_base, pre_a, pre_b, exp_a, exp_b, queues,
+                     rounds_out);
+  return hipGetLastError();
+}
+
 template <int BM, bool GATHER, int EPI, bool F8 = false>
 static hipError_t grouped_gemm(GemmArgs a, int64_t rows, hipStream_t s) {
   using C = std::conditional_t<BM == 128, TileStream, TileBig>;
@@ -230,6 +297,57 @@ hipError_t launch_expert_down_fp8(const uint8_t* H8, const int32_t* offsets,
   a.b_scale = wd_scale;
   if (bm == 128) return grouped_gemm<128, false, EPI_F32, true>(a, rows, s);
   return grouped_gemm<256, false, EPI_F32, true>(a, rows, s);
+}
+
+// A round of the multi-round schedule: gate/up over the round's rows of every
+// expert into the round buffer Hr, then down from Hr into y_rows (rows in
+// permutation order).  rows_bound: the most rows a round can hold.
+hipError_t launch_round_experts(const uint16_t* z, const int32_t* seg_start,
+                                const int32_t* seg_end, const int32_t* h_base,
+                                const int32_t* row_token, const int32_t* pre_a,
+                                const int32_t* exp_a, const int32_t* pre_b, const int32_t* exp_b,
+                                int32_t* queues, const uint16_t* w_gate, const uint16_t* w_up,
+                                const uint16_t* w_down, int64_t T, int64_t rows_bound, int E,
+                                int L, int F, int bm_a, int bm_b, uint16_t* Hr, float* Y,
+                                hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = z; a.seg[0].lda = L; a.seg[0].B = w_gate; a.seg[0].B2 = w_up; a.seg[0].ldb = L;
+  a.seg[0].K = L;
+  a.nseg = 1;
+  a.N = F;
+  a.offsets = seg_start;
+  a.seg_end = seg_end;
+  a.h_base = h_base;
+  a.h_side = 1;
+  a.tile_prefix = pre_a;
+  a.tile_expert = exp_a;
+  a.E = E;
+  a.b_expert_stride = (int64_t)F * L;
+  a.row_token = row_token;
+  a.queue = queues;
+  a.M = (int)T;
+  a.C = Hr;
+  a.ldc = F;
+  hipError_t err = bm_a == 128 ? grouped_gemm<128, true, EPI_SWIGLU>(a, rows_bound, s)
+                               : grouped_gemm<256, true, EPI_SWIGLU>(a, rows_bound, s);
+  if (err != hipSuccess) return err;
+  GemmArgs b = {};
+  b.seg[0].A = Hr; b.seg[0].lda = F; b.seg[0].B = w_down; b.seg[0].ldb = F; b.seg[0].K = F;
+  b.nseg = 1;
+  b.N = L;
+  b.offsets = seg_start;
+  b.seg_end = seg_end;
+  b.h_base = h_base;
+  b.h_side = 2;
+  b.tile_prefix = pre_b;
+  b.tile_expert = exp_b;
+  b.queue = queues + 8;
+  b.E = E;
+  b.b_expert_stride = (int64_t)L * F;
+  b.C = Y;
+  b.ldc = L;
+  return bm_b == 128 ? grouped_gemm<128, false, EPI_F32>(b, rows_bound, s)
+                     : grouped_gemm<256, false, EPI_F32>(b, rows_bound, s);
 }
 
 int device_cu_count() {

@@ -107,6 +107,13 @@ struct GemmArgs {
   const float* b2_scale;
   const float* out_scale;
   uint32_t* amax;
+  // grouped, multi-round schedule: expert e's rows this round are
+  // [offsets[e], seg_end[e]) (seg_end null: offsets[e + 1]); with h_base,
+  // row r of expert e sits at row h_base[e] + (r - offsets[e]) of the round's
+  // activation buffer, which is C (h_side 1: gate/up) or A (h_side 2: down)
+  const int32_t* seg_end;
+  const int32_t* h_base;
+  int h_side;
 };
 
 // fp32 -> FP8 E4M3 byte, round to nearest even, saturating at +-448
@@ -238,6 +245,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   for (int t = next_tile(-1); t < t_end; t = next_tile(t)) {
     // ---- decode the tile ----
     int r0, mrows, n_tile;
+    int a_r0, c_r0;                    // first row of the tile in A (no gather) and in C
     int64_t b_off = 0;
     float dq_b = 1.f, dq_b2 = 1.f;     // F8: 1 / (s_A s_B), 1 / (s_A s_B2)
     if constexpr (GROUPED) {
@@ -248,8 +256,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       const int rem = t - p0 * a.n_tiles;
       n_tile = rem / mt;
       const int m_local = rem - n_tile * mt;
-      r0 = __builtin_amdgcn_readfirstlane(a.offsets[e]) + m_local * BM;
-      mrows = min(BM, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - r0);
+      const int rs = __builtin_amdgcn_readfirstlane(a.offsets[e]);
+      const int re = __builtin_amdgcn_readfirstlane(a.seg_end ? a.seg_end[e] : a.offsets[e + 1]);
+      r0 = rs + m_local * BM;
+      mrows = min(BM, re - r0);
+      const int hr0 = a.h_base ? __builtin_amdgcn_readfirstlane(a.h_base[e]) + (r0 - rs) : r0;
+      a_r0 = a.h_side == 2 ? hr0 : r0;
+      c_r0 = a.h_side == 1 ? hr0 : r0;
       b_off = (int64_t)e * a.b_expert_stride * ES;
       if constexpr (F8) {
         dq_b = 1.0f / (a.a_scale[0] * a.b_scale[e]);
@@ -265,6 +278,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       n_tile = r / gm;
       r0 = (g * DENSE_GM + (r - n_tile * gm)) * BM;
       mrows = min(BM, a.M - r0);
+      a_r0 = c_r0 = r0;
       if constexpr (F8) {
         dq_b = 1.0f / (a.a_scale[0] * a.b_scale[0]);
         if constexpr (SWG) dq_b2 = 1.0f / (a.a_scale[0] * a.b2_scale[0]);
@@ -297,7 +311,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       const char* A = (const char*)g.A;
       const char* B = (const char*)g.B;
       if constexpr (GATHER) rA[S] = make_rsrc(A, (int64_t)a.M * g.lda * ES);
-      else rA[S] = make_rsrc(A + (int64_t)r0 * g.lda * ES, (int64_t)mrows * g.lda * ES);
+      else rA[S] = make_rsrc(A + (int64_t)a_r0 * g.lda * ES, (int64_t)mrows * g.lda * ES);
       rB[S] = make_rsrc(B + b_off + (int64_t)n0 * g.ldb * ES, (int64_t)nrows * g.ldb * ES);
       if constexpr (SWG)
         rU[S] = make_rsrc((const char*)g.B2 + b_off + (int64_t)n0 * g.ldb * ES,
@@ -463,7 +477,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int rl = (i * WM + wrow) * 32 + 8 * (r >> 2) + 4 * fq + (r & 3);
         if (rl >= mrows) continue;
-        const int64_t row = r0 + rl;
+        const int64_t row = c_r0 + rl;
         if constexpr (SWG) {
 #pragma unroll
           for (int j = 0; j < TN; j += 2) {

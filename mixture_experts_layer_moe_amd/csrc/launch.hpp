@@ -66,6 +66,20 @@ hipError_t launch_expert_down_fp8(const uint8_t* H8, const int32_t* offsets,
                                   const float* wd_scale, int64_t rows, int E, int L, int F,
                                   int bm, float* Y, hipStream_t s);
 
+// multi-round dropless schedule (expert.hip)
+hipError_t launch_round_tables(const int32_t* offsets, int E, int G, int C, int round, int bm_a,
+                               int bm_b, int32_t* seg_start, int32_t* seg_end, int32_t* h_base,
+                               int32_t* pre_a, int32_t* pre_b, int32_t* exp_a, int32_t* exp_b,
+                               int32_t* queues, int32_t* rounds_out, hipStream_t s);
+hipError_t launch_round_experts(const uint16_t* z, const int32_t* seg_start,
+                                const int32_t* seg_end, const int32_t* h_base,
+                                const int32_t* row_token, const int32_t* pre_a,
+                                const int32_t* exp_a, const int32_t* pre_b, const int32_t* exp_b,
+                                int32_t* queues, const uint16_t* w_gate, const uint16_t* w_up,
+                                const uint16_t* w_down, int64_t T, int64_t rows_bound, int E,
+                                int L, int F, int bm_a, int bm_b, uint16_t* Hr, float* Y,
+                                hipStream_t s);
+
 int device_cu_count();
 
 // fp8.hip: per-tensor amax of bf16 tensors (ntensor tensors of numel values,

@@ -79,6 +79,44 @@ FfnWs ffn8_ws(int64_t T, int L, int E, int k, int F) {
 }
 size_t combine_ws(int64_t T, int L) { return align_up((size_t)T * L * 2); }
 
+// multi-round dropless: z, the round buffer (E * C rows of H), the round's
+// row tables, tile tables sized for a round's rows, queue counters
+struct RoundsWs { size_t z, h, seg_start, seg_end, h_base, pre_a, pre_b, exp_a, exp_b, queues, total; };
+int64_t round_rows_bound(int64_t T, int E, int k, int C) {
+  const int64_t cap = (int64_t)E * C;
+  return T * k < cap ? T * k : cap;
+}
+RoundsWs rounds_ws(int64_t T, int L, int E, int k, int F, int C) {
+  const int64_t rb = round_rows_bound(T, E, k, C);
+  const size_t mt = (size_t)grouped_mtile_bound(rb, E, 128);
+  RoundsWs w;
+  w.z = 0;
+  w.h = align_up((size_t)T * L * 2);
+  w.seg_start = w.h + align_up((size_t)E * C * F * 2);
+  w.seg_end = w.seg_start + align_up((size_t)E * 4);
+  w.h_base = w.seg_end + align_up((size_t)E * 4);
+  w.pre_a = w.h_base + align_up((size_t)E * 4);
+  w.pre_b = w.pre_a + align_up((size_t)(E + 1) * 4);
+  w.exp_a = w.pre_b + align_up((size_t)(E + 1) * 4);
+  w.exp_b = w.exp_a + align_up(mt * 4);
+  w.queues = w.exp_b + align_up(mt * 4);
+  w.total = w.queues + align_up(16 * 4);
+  return w;
+}
+// Rounds any routing can need: a group of n experts holds at most
+// T * min(k, n) rows and n * C slots per round.
+int64_t max_rounds(int64_t T, int E, int k, int G, int C) {
+  int64_t m = 0;
+  const int sizes[2] = {G < E ? G : E, E % G ? E % G : (G < E ? G : E)};
+  for (int n : sizes) {
+    const int64_t load = T * (k < n ? k : n);
+    const int64_t cap = (int64_t)n * C;
+    const int64_t r = (load + cap - 1) / cap;
+    if (r > m) m = r;
+  }
+  return m;
+}
+
 int check_route_dims(int64_t T, int d, int E, int k) {
   if (T < 0 || d <= 0 || E <= 0 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
   if (k > 16 || E > 1024 || !dims_ok(d)) return MOE_ERR_UNSUPPORTED;
@@ -372,6 +410,81 @@ int moe_latent_ffn_forward_fp8(const uint16_t* x, const uint16_t* w_lat_down,
   return hip_status(launch_expert_down_fp8(H8, expert_offsets, pre_b, exp_b, queues + 8, w_down,
                                            act_scale + 1, w_scale + 2 * E, rows, E, L, F,
                                            plan.bm_down, y_rows, s));
+}
+
+size_t moe_workspace_bytes_rounds(int64_t T, int32_t d, int32_t L, int32_t E, int32_t k,
+                                  int32_t F, int32_t Fs, int32_t capacity, int32_t group_size) {
+  (void)d;
+  (void)Fs;
+  if (T < 0 || E <= 0 || k < 1 || L <= 0 || F <= 0 || capacity < 1 || group_size < 1) return 0;
+  return rounds_ws(T, L, E, k, F, capacity).total;
+}
+
+int moe_latent_ffn_forward_rounds(const uint16_t* x, const uint16_t* w_lat_down,
+                                  const int32_t* expert_offsets, const int32_t* row_token,
+                                  const uint16_t* w_gate, const uint16_t* w_up,
+                                  const uint16_t* w_down, const uint16_t* ws_gate,
+                                  const uint16_t* ws_up, int64_t T, int32_t d, int32_t L,
+                                  int32_t E, int32_t k, int32_t F, int32_t Fs, int32_t capacity,
+                                  int32_t group_size, float* y_rows, uint16_t* hs,
+                                  int32_t* rounds_out, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || E <= 0 || k < 1 || k > E || Fs < 0 || capacity < 1 || group_size < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (k > 16 || E > 1024 || !dims_ok(d) || !dims_ok(L) || !dims_ok(F) ||
+      (Fs > 0 && !dims_ok(Fs)) || T * (int64_t)k >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * L * 2 >= (int64_t(1) << 31) ||
+      (int64_t)E * capacity >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_lat_down || !expert_offsets || !row_token || !w_gate || !w_up || !w_down ||
+      !y_rows || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (Fs > 0 && (!ws_gate || !ws_up || !hs)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, w_lat_down, w_gate, w_up, w_down, y_rows, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  if (Fs > 0 && (!aligned16(ws_gate) || !aligned16(ws_up) || !aligned16(hs)))
+    return MOE_ERR_UNSUPPORTED;
+  const RoundsWs w = rounds_ws(T, L, E, k, F, capacity);
+  if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  uint16_t* z = (uint16_t*)(base + w.z);
+  uint16_t* Hr = (uint16_t*)(base + w.h);
+  int32_t* seg_start = (int32_t*)(base + w.seg_start);
+  int32_t* seg_end = (int32_t*)(base + w.seg_end);
+  int32_t* h_base = (int32_t*)(base + w.h_base);
+  int32_t* pre_a = (int32_t*)(base + w.pre_a);
+  int32_t* pre_b = (int32_t*)(base + w.pre_b);
+  int32_t* exp_a = (int32_t*)(base + w.exp_a);
+  int32_t* exp_b = (int32_t*)(base + w.exp_b);
+  int32_t* queues = (int32_t*)(base + w.queues);
+  const int64_t rb = round_rows_bound(T, E, k, capacity);
+  const ExpertGemmPlan plan = plan_expert_gemms(rb, E);
+  int st;
+  {
+    EventScope ev(K_LATENT_DOWN, s);
+    st = hip_status(launch_latent_down(x, w_lat_down, T, d, L, z, s));
+    if (!st && Fs > 0) st = hip_status(launch_shared_gate_up(x, ws_gate, ws_up, T, d, Fs, hs, s));
+  }
+  if (st) return st;
+  // The host does not know the routing, so it enqueues the most rounds any
+  // routing can need; rounds past the ones this routing needs find no rows
+  // and their GEMMs exit at once.
+  const int64_t R = max_rounds(T, E, k, group_size, capacity);
+  EventScope ev(K_GATE_UP, s);   // brackets every round (gate/up and down)
+  for (int64_t r = 0; r < R; ++r) {
+    st = hip_status(launch_round_tables(expert_offsets, E, group_size, capacity, (int)r,
+                                        plan.bm_gate_up, plan.bm_down, seg_start, seg_end, h_base,
+                                        pre_a, pre_b, exp_a, exp_b, queues, rounds_out, s));
+    if (st) return st;
+    st = hip_status(launch_round_experts(z, seg_start, seg_end, h_base, row_token, pre_a, exp_a,
+                                         pre_b, exp_b, queues, w_gate, w_up, w_down, T, rb, E, L,
+                                         F, plan.bm_gate_up, plan.bm_down, Hr, y_rows, s));
+    if (st) return st;
+  }
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -143,3 +143,32 @@ def forward_fp8(x, w: LatentMoEWeights, w8: LatentMoEFp8Experts, k, buf: LatentM
     if update_scaling:
         scaling.update(stream=stream)
     return buf.out
+
+
+# ---------------------------------------------------------------------------
+# multi-round dropless experts (fixed activation memory)
+# ---------------------------------------------------------------------------
+
+def forward_rounds(x, w: LatentMoEWeights, k, buf: LatentMoEBuffers, capacity, group_size,
+                   ws_rounds=None, rounds_out=None, stream=None, route=True):
+    """One forward pass whose experts run the multi-round schedule with a
+    fixed per-expert capacity (borrowing inside groups of group_size
+    experts).  ``ws_rounds``: workspace of moe_workspace_bytes_rounds bytes
+    (allocated here if None); ``rounds_out``: optional int32 device tensor
+    that receives the number of rounds the routing needed."""
+    if ws_rounds is None:
+        d, L, E, F, Fs = w.dims
+        nb = _lib.moe_workspace_bytes_rounds(buf.T, d, L, E, k, F, Fs, capacity, group_size)
+        ws_rounds = torch.empty(nb, dtype=torch.uint8, device=x.device)
+    if route:
+        _lib.moe_route(x, w.w_router, w.b_router, k, buf.topk_idx, buf.topk_w, ws=buf.ws,
+                       stream=stream)
+    _lib.moe_permute(buf.topk_idx, buf.E, buf.expert_counts, buf.expert_offsets, buf.row_token,
+                     buf.assign_row, buf.ws, stream=stream)
+    _lib.moe_latent_ffn_forward_rounds(x, w.w_lat_down, buf.expert_offsets, buf.row_token,
+                                       w.w_gate, w.w_up, w.w_down, w.ws_gate, w.ws_up, k, capacity,
+                                       group_size, buf.y_rows, buf.hs, rounds_out, ws_rounds,
+                                       stream=stream)
+    _lib.moe_combine(buf.y_rows, buf.topk_w, buf.assign_row, w.w_lat_up, buf.hs, w.ws_down,
+                     buf.out, buf.ws, stream=stream)
+    return buf.out

@@ -24,7 +24,8 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"moe_route", "moe_route_ex", "moe_permute", "moe_latent_ffn_forward", "moe_combine",
             "moe_workspace_bytes", "moe_status_string", "moe_set_kernel_events", "moe_fp8_amax",
-            "moe_fp8_quantize", "moe_fp8_scale_update", "moe_latent_ffn_forward_fp8"} <= set(names)
+            "moe_fp8_quantize", "moe_fp8_scale_update", "moe_latent_ffn_forward_fp8",
+            "moe_workspace_bytes_rounds", "moe_latent_ffn_forward_rounds"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -174,3 +175,24 @@ def test_latent_ffn_fp8_rejects_bad_args():
     need = _lib.moe_workspace_bytes(4, 8, 512, 256, 16, 2, 512)
     assert _ffn8(lib, wsb=need - 1) == -3
     assert _ffn8(lib, T=0) == 0
+
+
+def test_rounds_workspace_and_bad_args():
+    a = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    T, d, L, E, k, F, C, G = 4096, 6656, 3072, 512, 8, 10240, 96, 8
+    rb = min(T * k, E * C)
+    mt = (rb + min(E, rb) * 127) // 128
+    assert _lib.moe_workspace_bytes_rounds(T, d, L, E, k, F, 0, C, G) == \
+        a(T * L * 2) + a(E * C * F * 2) + 3 * a(E * 4) + 2 * a((E + 1) * 4) + 2 * a(mt * 4) + a(64)
+    assert _lib.moe_workspace_bytes_rounds(T, d, L, E, k, F, 0, 0, G) == 0
+    lib = _lib.load()
+
+    def call(C=64, G=8, T=8, wsb=1 << 40, E=16, k=2, L=256):
+        return lib.moe_latent_ffn_forward_rounds(P, P, P, P, P, P, P, None, None, T, 512, L, E, k,
+                                                 512, 0, C, G, P, None, None, P, wsb, None)
+    assert call(C=0) == -1
+    assert call(G=0) == -1
+    assert call(k=0) == -1
+    assert call(L=192 + 32) == -2
+    assert call(wsb=100) == -3
+    assert call(T=0) == 0
