@@ -50,6 +50,11 @@ def parse():
     p.add_argument("--fp8", action="store_true",
                    help="routed experts' GEMMs in FP8 E4M3 with delayed scaling (not the headline "
                         "configuration, which is bf16)")
+    p.add_argument("--capacity", type=float, default=0.0,
+                   help="multi-round dropless experts: per-expert capacity per round as a "
+                        "multiple of the mean rows per expert (0: single pass)")
+    p.add_argument("--group-size", type=int, default=8,
+                   help="experts sharing capacity in the multi-round schedule")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain device copy of known size (for HBM counter scaling)")
     return p.parse_args()
@@ -73,8 +78,7 @@ class HipEvents:
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
         rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
-        assert rc == 0, f"hipEventElapsedTime rc={rc}"
-        return ms.value
+        return ms.value if rc == 0 else None   # None: a kernel that this path does not launch
 
     def destroy(self, e):
         self.hip.hipEventDestroy(ctypes.c_void_p(e))
@@ -220,6 +224,20 @@ def main():
     buf = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, cfg.Fs, device=dev)
     x = dv["x"]
     step = lambda: moe.forward(x, w, cfg.k, buf)  # noqa: E731
+    rounds_info = None
+    if args.capacity > 0:
+        if args.fp8:
+            print("--capacity runs the bf16 experts only", file=sys.stderr)
+            sys.exit(2)
+        cap = max(1, int(round(args.capacity * cfg.T * cfg.k / cfg.E)))
+        gs = min(args.group_size, cfg.E)
+        nb = moe.moe_workspace_bytes_rounds(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, cfg.Fs, cap,
+                                            gs)
+        ws_r = torch.empty(nb, dtype=torch.uint8, device=dev)
+        rounds_t = torch.zeros(1, dtype=torch.int32, device=dev)
+        rounds_info = {"capacity": cap, "group_size": gs, "workspace_bytes": nb}
+        step = lambda: moe.forward_rounds(x, w, cfg.k, buf, cap, gs, ws_rounds=ws_r,  # noqa: E731
+                                          rounds_out=rounds_t)
     if args.fp8:
         # weights quantized once (448 / amax per expert matrix); the bf16
         # expert weights are then dropped; activation scales are delayed:
@@ -260,8 +278,10 @@ def main():
     t1 = time.perf_counter()
     for name in KERNEL_NAMES:
         moe.moe_set_kernel_events(name, None, None)
-    kern_ms = {name: float(np.mean([hip.elapsed_ms(a, b) for a, b in ev[name]]))
-               for name in KERNEL_NAMES}
+    kern_ms = {}
+    for name in KERNEL_NAMES:
+        t = [hip.elapsed_ms(a, b) for a, b in ev[name]]
+        kern_ms[name] = None if any(v is None for v in t) else float(np.mean(t))
     for pairs in ev.values():
         for a, b in pairs:
             hip.destroy(a)
@@ -292,7 +312,7 @@ def main():
     layer = {
         "mfma_frac": cfg.flops() / step_s / mfma_peak,
         "hbm_frac": layer_bytes(cfg, touched, esize) / step_s / HBM_PEAK,
-        "kernels_ms": {k: round(v, 4) for k, v in kern_ms.items()},
+        "kernels_ms": {k: (None if v is None else round(v, 4)) for k, v in kern_ms.items()},
     }
 
     cpu = None
@@ -311,6 +331,10 @@ def main():
                    "seed": cfg.seed},
         "roofline": roof, "layer": layer, "cpu_baseline": cpu,
     }
+    if rounds_info is not None:
+        rounds_info["rounds"] = int(rounds_t.item())
+        line["config"]["multi_round"] = rounds_info
+        line["roofline"] = None   # the gate/up events bracket every round of both GEMMs
     print(json.dumps(line), flush=True)
 
 
