@@ -39,7 +39,8 @@
 //   * GROUPED: M is the expert-ordered row list; tiles never straddle two
 //     experts.  Device tables (prefix of per-expert M-tile counts and the
 //     expert of every M-tile) map a tile index to (expert, M-tile, N-tile)
-//     with no host sync.  Order: expert, then N tile, then M tile, so M tiles
+//     with no host sync; an expert's rows are split into its M tiles evenly
+//     (heights a multiple of 32 rows).  Order: expert, then N tile, then M tile, so M tiles
 //     of one expert that read the same weight tile run side by side.
 //     GATHER: A row r is row row_token[r] of the activations (the token
 //     permutation is fused into the A load).
@@ -258,8 +259,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       const int m_local = rem - n_tile * mt;
       const int rs = __builtin_amdgcn_readfirstlane(a.offsets[e]);
       const int re = __builtin_amdgcn_readfirstlane(a.seg_end ? a.seg_end[e] : a.offsets[e + 1]);
-      r0 = rs + m_local * BM;
-      mrows = min(BM, re - r0);
+      // the expert's rows split into mt tiles of equal height (a multiple of
+      // 32, at most BM): no tile is mostly empty, e.g. 574 rows -> 3 x 192
+      const int th = ((re - rs + mt - 1) / mt + 31) / 32 * 32;
+      r0 = rs + m_local * th;
+      mrows = min(th, re - r0);
       const int hr0 = a.h_base ? __builtin_amdgcn_readfirstlane(a.h_base[e]) + (r0 - rs) : r0;
       a_r0 = a.h_side == 2 ? hr0 : r0;
       c_r0 = a.h_side == 1 ? hr0 : r0;
