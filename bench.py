@@ -126,7 +126,7 @@ def layer_bytes(cfg, touched, esize=2):
     return w + T * d * 2.0 + T * d * 4.0
 
 
-def cpu_baseline(cfg, n_tok=256, n_exp=8, seed=0, fp8=False):
+def cpu_baseline(cfg, n_tok=2048, n_exp=24, seed=0, fp8=False):
     """The oracle (float64 numpy, as it stands) on a bounded sample of the
     workload, extrapolated to tokens/s of the whole layer:
       router + permutation over all T tokens (timed in full),
@@ -170,9 +170,12 @@ def cpu_baseline(cfg, n_tok=256, n_exp=8, seed=0, fp8=False):
     nonempty = np.nonzero(counts)[0]
     sample = rng.choice(nonempty, size=min(n_exp, nonempty.size), replace=False)
     t_exp = 0.0
+    t_gen = 0.0
     rows_done = 0
     for e in sample:
+        tg = time.perf_counter()
         wts = gen.expert_weights_f64(cfg, int(e))
+        t_gen += time.perf_counter() - tg
         a, bnd = int(p["expert_offsets"][e]), int(p["expert_offsets"][e + 1])
         zr = oracle.latent_down(x[p["row_token"][a:bnd]], w_dn, "bf16_operands")
         sc = None
@@ -197,8 +200,9 @@ def cpu_baseline(cfg, n_tok=256, n_exp=8, seed=0, fp8=False):
                    f"({t_route:.2f} s), latent down/combine/up on {len(toks)} tokens "
                    f"({t_tok:.2f} s, scaled x{cfg.T / len(toks):.0f}), SwiGLU experts on "
                    f"{len(sample)} sampled experts = {rows_done} routed rows ({t_exp:.2f} s, "
-                   f"scaled by rows to all {cfg.T * cfg.k}); extrapolated {total:.1f} s per "
-                   f"forward pass"),
+                   f"scaled by rows to all {cfg.T * cfg.k}); {t_route + t_tok + t_exp:.1f} s of "
+                   f"timed oracle work, extrapolated {total:.1f} s per forward pass (weight "
+                   f"generation, {t_gen:.0f} s, not timed)"),
     }
 
 

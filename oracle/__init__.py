@@ -1,4 +1,4 @@
-"""CPU oracle of the LatentMoE layer forward pass.
+"""CPU oracle of the LatentMoE layer forward and backward passes.
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py``; never by the product path.
@@ -11,3 +11,5 @@ from .latent_moe import (BIAS_MODES, E4M3_MAX, MODES, combine, expert_fp8_scales
                          router_logits, shared_expert, silu, softmax, swiglu_activation,
                          swiglu_expert,
                          topk_stable)
+from . import latent_moe_backward  # noqa: F401,E402
+from .latent_moe_backward import backward  # noqa: F401,E402
