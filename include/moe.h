@@ -1,5 +1,5 @@
 /*
- * libmoe — forward pass of the LatentMoE feed-forward layer on one AMD
+ * libmoe — forward (and backward) pass of the LatentMoE feed-forward layer on one AMD
  * MI355X (gfx950), as a C ABI over hand-written HIP kernels.
  *
  * The layer (pages: "The Training and RL Infrastructure Behind MAI-Thinking-1",
@@ -311,6 +311,78 @@ int moe_latent_ffn_forward_rounds(const uint16_t* x, const uint16_t* w_lat_down,
                                   int32_t group_size, float* y_rows, uint16_t* hs,
                                   int32_t* rounds_out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- backward pass ---------------------------------------------------------
+ * Gradients of the forward pass above (no shared expert: Fs must be 0) for a
+ * gradient g_out = dLoss/d out [T, d] fp32.  Math, per "The Training and RL
+ * Infrastructure Behind MAI-Thinking-1", section 2 "Numerics":
+ *   dW_up = g^T c,  dc = g W_up                        (g = g_out cast to bf16)
+ *   dy_r = w[t,j] dc_t,  dw[t,j] = dc_t . y_r          (combine backward, FP32)
+ *   per expert e, rows r:  g = z W_g^T, u = z W_u^T     (recomputed, FP32)
+ *     dh = dy W_d,  dg = dh u silu'(g),  du = dh silu(g)
+ *     dz_r = dg W_g + du W_u,  dW_d = dy^T h,  dW_g = dg^T z_r,  dW_u = du^T z_r
+ *   dz_t = sum_j dz_{row(t,j)} (fixed order),  dx = dz W_dn,  dW_dn = dz^T x
+ *   router (FP32): p = softmax(router_logits), dl = p (dp - sum p dp) with dp
+ *     = dw at the selected experts, dx += dl W_r, dW_r = dl^T x, db = sum_t dl
+ * GEMM operands are bf16 with FP32 accumulation; the gradients g_out, dy, dg,
+ * du and dz are cast to bf16 where they become GEMM operands, rounded to
+ * nearest even (rounding = MOE_ROUND_NEAREST) or stochastically (rounding =
+ * MOE_ROUND_STOCHASTIC: the pages round stochastically wherever a gradient
+ * is cast to lower precision).  Stochastic rounding adds a uniform 16-bit
+ * integer to the fp32 bit pattern and drops the low 16 bits; the integer of
+ * element i (flat row-major index) of stream s (1 g_out, 2 dy with rows in
+ * expert order, 3 dg, 4 du, 5 dz) is the top 16 bits of
+ *   h = lowbias32(lowbias32((i mod 2^32) ^ key) ^ (i >> 32)),
+ *   key = lowbias32(seed + 0x9E3779B9 * s)     (uint32 arithmetic)
+ * with lowbias32 the published integer mixer x ^= x >> 16, x *= 0x7feb352d,
+ * x ^= x >> 15, x *= 0x846ca68b, x ^= x >> 16.
+ *
+ * moe_backward_prepare: the transposed weight copies the data-gradient GEMMs
+ * read (all bf16, caller-allocated): w_lat_down_t [d, L], w_gate_t and
+ * w_up_t [E, L, F], w_down_t [E, F, L], w_lat_up_t [L, d].  Call once per
+ * weight update (the pages' backward likewise needs each tensor and its
+ * transpose, "The Training and RL Infrastructure Behind MAI-Thinking-1",
+ * section 3 "Custom kernels").
+ *
+ * moe_backward inputs: the forward's x, routing (topk_idx, topk_w,
+ * router_logits = moe_route's logits_out [T, E] fp32, bias_mode as given to
+ * moe_route_ex: MOE_BIAS_LOGITS or MOE_BIAS_SELECTION), permutation
+ * (expert_offsets, row_token, assign_row), the expert rows y_rows [T*k, L]
+ * fp32 of moe_latent_ffn_forward, the weights w_lat_down, w_gate, w_up
+ * (recomputation) and w_router [E, d] fp32, the prepared transposes, and
+ * g_out.  Outputs (fp32, overwritten, caller-allocated): dx [T, d],
+ * dw_router [E, d], db_router [E] (nullable; zero in the selection bias
+ * mode), dw_lat_down [L, d], dw_gate [E, F, L], dw_up [E, F, L],
+ * dw_down [E, L, F], dw_lat_up [d, L], dtopk_w [T, k] (nullable: the
+ * gradient of the gate weights).  Workspace: MOE_OP_BACKWARD.  Limits and
+ * errors as for the forward; Fs != 0 is MOE_ERR_UNSUPPORTED.  Deterministic:
+ * every reduction has a fixed order.
+ */
+/* moe_grad_cast_bf16: dst[i] = src[i] cast to bf16 with the backward's
+ * gradient rounding (MOE_ROUND_NEAREST, or MOE_ROUND_STOCHASTIC with the
+ * element's integer from stream `stream_id` under `seed`, as above); n a
+ * multiple of 4.  The cast the backward applies to g_out (stream 1). */
+int moe_grad_cast_bf16(const float* src, int64_t n, int32_t rounding, uint32_t seed,
+                       int32_t stream_id, uint16_t* dst, void* stream);
+#define MOE_OP_BACKWARD      5
+#define MOE_ROUND_NEAREST    0
+#define MOE_ROUND_STOCHASTIC 1
+int moe_backward_prepare(const uint16_t* w_lat_down, const uint16_t* w_gate,
+                         const uint16_t* w_up, const uint16_t* w_down,
+                         const uint16_t* w_lat_up, int32_t d, int32_t L, int32_t E, int32_t F,
+                         uint16_t* w_lat_down_t, uint16_t* w_gate_t, uint16_t* w_up_t,
+                         uint16_t* w_down_t, uint16_t* w_lat_up_t, void* stream);
+int moe_backward(const uint16_t* x, const float* w_router, const float* router_logits,
+                 int32_t bias_mode, const int32_t* topk_idx, const float* topk_w,
+                 const int32_t* expert_offsets, const int32_t* row_token,
+                 const int32_t* assign_row, const float* y_rows, const uint16_t* w_lat_down,
+                 const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_lat_down_t,
+                 const uint16_t* w_gate_t, const uint16_t* w_up_t, const uint16_t* w_down_t,
+                 const uint16_t* w_lat_up_t, const float* g_out, int64_t T, int32_t d,
+                 int32_t L, int32_t E, int32_t k, int32_t F, int32_t rounding, uint32_t seed,
+                 float* dx, float* dw_router, float* db_router, float* dw_lat_down,
+                 float* dw_gate, float* dw_up, float* dw_down, float* dw_lat_up, float* dtopk_w,
+                 void* ws, size_t ws_bytes, void* stream);
+
 /* ---- profiling hook ------------------------------------------------------
  * Register two hipEvent_t (created by the caller) that the library records on
  * the call's stream immediately before and after every launch of `kernel`
@@ -325,7 +397,14 @@ int moe_latent_ffn_forward_rounds(const uint16_t* x, const uint16_t* w_lat_down,
 #define MOE_KERNEL_EXPERT_DOWN   5   /* grouped expert down GEMM                */
 #define MOE_KERNEL_COMBINE       6   /* weighted gather-combine                 */
 #define MOE_KERNEL_LATENT_UP     7   /* out = c W_up^T (+ shared down)          */
-#define MOE_KERNEL_COUNT         8
+#define MOE_KERNEL_BWD_UP        8   /* backward: g cast, dW_up, dc             */
+#define MOE_KERNEL_BWD_COMBINE   9   /* backward: combine (dy rows, dw)         */
+#define MOE_KERNEL_BWD_DGRAD    10   /* backward: gate/up recompute, dh + SwiGLU
+                                        backward, expert rows' latent gradient  */
+#define MOE_KERNEL_BWD_WGRAD    11   /* backward: padded transposes, dW_d/g/u   */
+#define MOE_KERNEL_BWD_LATENT   12   /* backward: gather dz, dx, dW_dn          */
+#define MOE_KERNEL_BWD_ROUTER   13   /* backward: softmax backward, router GEMMs */
+#define MOE_KERNEL_COUNT        14
 int moe_set_kernel_events(int kernel, void* start_event, void* stop_event);
 
 #ifdef __cplusplus

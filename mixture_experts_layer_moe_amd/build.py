@@ -26,7 +26,8 @@ COMMON_FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 
-SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "expert.hip", "combine.hip", "fp8.hip"]
+SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "expert.hip", "combine.hip", "fp8.hip",
+           "backward.hip"]
 
 
 def _compile(src: str, extra: list[str]) -> str:

@@ -14,7 +14,9 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // Kernel ids of the profiling hook (same numbering as include/moe.h).
 enum KernelId {
   K_ROUTER_GEMM = 0, K_ROUTER_TOPK = 1, K_PERMUTE = 2, K_LATENT_DOWN = 3,
-  K_GATE_UP = 4, K_EXPERT_DOWN = 5, K_COMBINE = 6, K_LATENT_UP = 7, K_COUNT = 8
+  K_GATE_UP = 4, K_EXPERT_DOWN = 5, K_COMBINE = 6, K_LATENT_UP = 7, K_BWD_UP = 8,
+  K_BWD_COMBINE = 9, K_BWD_DGRAD = 10, K_BWD_WGRAD = 11, K_BWD_LATENT = 12, K_BWD_ROUTER = 13,
+  K_COUNT = 14
 };
 
 // Records the caller's start/stop events (if registered on this thread)
@@ -31,6 +33,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// The lowbias32 integer mixer (C. Wellons, hash prospector): two
+// xorshift-multiply rounds and a final xorshift.  Host and device.
+__host__ __device__ constexpr uint32_t lowbias32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// Key of random stream `stream` under `seed` for stochastic rounding.
+__host__ __device__ constexpr uint32_t sr_stream_key(uint32_t seed, uint32_t stream) {
+  return lowbias32(seed + 0x9E3779B9u * stream);
+}
+
+// fp32 -> bf16 bits by stochastic rounding: a uniform 16-bit integer r
+// (counter-based: element index idx of the stream with key `key`) is added
+// to the bit pattern and the low 16 bits dropped, so the magnitude rounds up
+// with probability equal to the discarded fraction (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_sr(float f, uint32_t key, uint64_t idx) {
+  uint32_t h = lowbias32((uint32_t)idx ^ key);
+  h = lowbias32(h ^ (uint32_t)(idx >> 32));
+  return (uint16_t)((__float_as_uint(f) + (h >> 16)) >> 16);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -191,13 +191,13 @@ hipError_t launch_round_tables(const int32_t* offsets, int E, int G, int C, int 
   return hipGetLastError();
 }
 
-template <int BM, bool GATHER, int EPI, bool F8 = false>
+template <int BM, bool GATHER, int EPI, bool F8 = false, int NSEG = 1>
 static hipError_t grouped_gemm(GemmArgs a, int64_t rows, hipStream_t s) {
   using C = std::conditional_t<BM == 128, TileStream, TileBig>;
   static_assert(C::bm == BM, "tile height");
   a.n_tiles = (int)ceil_div(epi_swiglu(EPI) ? 2 * (int64_t)a.N : a.N, C::bn);
   const int64_t bound = grouped_mtile_bound(rows, a.E, BM) * a.n_tiles;
-  return launch_gemm<C, true, GATHER, EPI, 1, F8>(a, bound, s);
+  return launch_gemm<C, true, GATHER, EPI, NSEG, F8>(a, bound, s);
 }
 
 hipError_t launch_gate_up(const uint16_t* z, const int32_t* offsets, const int32_t* row_token,
@@ -241,6 +241,89 @@ hipError_t launch_expert_down(const uint16_t* H, const int32_t* offsets,
   a.ldc = L;
   if (bm == 128) return grouped_gemm<128, false, EPI_F32>(a, rows, s);
   return grouped_gemm<256, false, EPI_F32>(a, rows, s);
+}
+
+// Backward: the gate/up GEMM again (recomputation), keeping g and u in FP32
+// and h in bf16 (bit-identical to the forward's h: same tiles, same order).
+hipError_t launch_gate_up_recompute(const uint16_t* z, const int32_t* offsets,
+                                    const int32_t* row_token, const int32_t* tile_prefix,
+                                    const int32_t* tile_expert, int32_t* queue,
+                                    const uint16_t* w_gate, const uint16_t* w_up, int64_t T,
+                                    int64_t rows, int E, int L, int F, int bm, float* g, float* u,
+                                    uint16_t* h, hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = z; a.seg[0].lda = L; a.seg[0].B = w_gate; a.seg[0].B2 = w_up; a.seg[0].ldb = L;
+  a.seg[0].K = L;
+  a.nseg = 1;
+  a.N = F;
+  a.offsets = offsets;
+  a.tile_prefix = tile_prefix;
+  a.tile_expert = tile_expert;
+  a.E = E;
+  a.b_expert_stride = (int64_t)F * L;
+  a.row_token = row_token;
+  a.queue = queue;
+  a.M = (int)T;
+  a.C = g;
+  a.C2 = u;
+  a.C3 = h;
+  a.ldc = F;
+  if (bm == 128) return grouped_gemm<128, true, EPI_GU_F32>(a, rows, s);
+  return grouped_gemm<256, true, EPI_GU_F32>(a, rows, s);
+}
+
+// Backward: dh = dy W_d[e] per expert (B = W_d[e]^T [F, L]), and in the
+// epilogue dg = dh u silu'(g), du = dh silu(g), both cast to bf16 (RNE or
+// stochastic rounding with the stream keys).
+hipError_t launch_swiglu_bwd(const uint16_t* dy_b, const int32_t* offsets,
+                             const int32_t* tile_prefix, const int32_t* tile_expert,
+                             int32_t* queue, const uint16_t* w_down_t, const float* g,
+                             const float* u, int64_t rows, int E, int L, int F, int bm, int sr,
+                             uint32_t key_dg, uint32_t key_du, uint16_t* dg_b, uint16_t* du_b,
+                             hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = dy_b; a.seg[0].lda = L; a.seg[0].B = w_down_t; a.seg[0].ldb = L; a.seg[0].K = L;
+  a.nseg = 1;
+  a.N = F;
+  a.offsets = offsets;
+  a.tile_prefix = tile_prefix;
+  a.tile_expert = tile_expert;
+  a.queue = queue;
+  a.E = E;
+  a.b_expert_stride = (int64_t)F * L;
+  a.C = dg_b;
+  a.C2 = du_b;
+  a.aux_g = g;
+  a.aux_u = u;
+  a.sr = sr;
+  a.sr_key_c = key_dg;
+  a.sr_key_c2 = key_du;
+  a.ldc = F;
+  if (bm == 128) return grouped_gemm<128, false, EPI_SWIGLU_BWD>(a, rows, s);
+  return grouped_gemm<256, false, EPI_SWIGLU_BWD>(a, rows, s);
+}
+
+// Backward: the rows' latent gradient dzp = dg W_g[e] + du W_u[e] (fp32), one
+// accumulation over the two K segments (B = W_g[e]^T, W_u[e]^T [L, F]).
+hipError_t launch_dzp(const uint16_t* dg_b, const uint16_t* du_b, const int32_t* offsets,
+                      const int32_t* tile_prefix, const int32_t* tile_expert, int32_t* queue,
+                      const uint16_t* w_gate_t, const uint16_t* w_up_t, int64_t rows, int E,
+                      int L, int F, int bm, float* dzp, hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = dg_b; a.seg[0].lda = F; a.seg[0].B = w_gate_t; a.seg[0].ldb = F; a.seg[0].K = F;
+  a.seg[1].A = du_b; a.seg[1].lda = F; a.seg[1].B = w_up_t; a.seg[1].ldb = F; a.seg[1].K = F;
+  a.nseg = 2;
+  a.N = L;
+  a.offsets = offsets;
+  a.tile_prefix = tile_prefix;
+  a.tile_expert = tile_expert;
+  a.queue = queue;
+  a.E = E;
+  a.b_expert_stride = (int64_t)L * F;
+  a.C = dzp;
+  a.ldc = L;
+  if (bm == 128) return grouped_gemm<128, false, EPI_F32, false, 2>(a, rows, s);
+  return grouped_gemm<256, false, EPI_F32, false, 2>(a, rows, s);
 }
 
 // FP8 experts: z8 and the weights are E4M3 with scales (z: one, weights: one

@@ -71,9 +71,13 @@ constexpr uint32_t RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data format
 constexpr int DENSE_GM = 4;                     // M panels per tile group (dense GEMMs)
 
 enum GemmEpi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_BIAS = 2, EPI_SWIGLU = 3, EPI_Q8 = 4,
-               EPI_SWIGLU_Q8 = 5 };
+               EPI_SWIGLU_Q8 = 5, EPI_GU_F32 = 6, EPI_SWIGLU_BWD = 7 };
 
-constexpr bool epi_swiglu(int epi) { return epi == EPI_SWIGLU || epi == EPI_SWIGLU_Q8; }
+// B tiles that interleave the gate and up matrices (a lane holds g and u of
+// the same element)
+constexpr bool epi_swiglu(int epi) {
+  return epi == EPI_SWIGLU || epi == EPI_SWIGLU_Q8 || epi == EPI_GU_F32;
+}
 constexpr float E4M3_MAX = 448.0f;
 
 struct GemmSeg {
@@ -115,6 +119,22 @@ struct GemmArgs {
   const int32_t* seg_end;
   const int32_t* h_base;
   int h_side;
+  // backward.  EPI_GU_F32: g -> C, u -> C2 (fp32), h = bf16(silu(g) u) -> C3.
+  // EPI_SWIGLU_BWD: the accumulator is dh; with g = aux_g, u = aux_u at the
+  // same (row, column) (leading dimension ldc), dg -> C and du -> C2 as bf16,
+  // rounded to nearest even (sr == 0) or stochastically with the random
+  // stream keys sr_key_c, sr_key_c2 (element index row * ldc + column).
+  // KG (K-grouped tiles, weight gradients): tile -> (expert, M tile, N tile)
+  // with expert e's K range [kpre[e], kpre[e + 1]) of A and B (multiples of
+  // the stage width), C of expert e at C + e * c_expert_stride.
+  void* C2;
+  void* C3;
+  const float* aux_g;
+  const float* aux_u;
+  uint32_t sr_key_c, sr_key_c2;
+  int sr;
+  const int32_t* kpre;
+  int64_t c_expert_stride;
 };
 
 // fp32 -> FP8 E4M3 byte, round to nearest even, saturating at +-448
@@ -170,7 +190,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool GROUPED, bool GATHER, int EPI,
-          bool BNT, int NSEG, bool F8>
+          bool BNT, int NSEG, bool F8, bool KG>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   constexpr int ES = F8 ? 1 : 2;                   // operand bytes per element
   constexpr int KE = BK * 2 / ES;                  // K values per stage (BK * 2 bytes per row)
@@ -208,7 +228,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   const int fq = lane >> 5;                        // which half of a sub-step's K this lane holds
 
   int total;
+  static_assert(!(KG && (GROUPED || GATHER || NSEG != 1)), "K-grouped tiles: one plain segment");
   if constexpr (GROUPED) total = a.tile_prefix[a.E] * a.n_tiles;
+  else if constexpr (KG) total = a.E * a.m_tiles * a.n_tiles;
   else total = a.m_tiles * a.n_tiles;
   const int xcd = blockIdx.x & 7;
   const int nj = gridDim.x >> 3;
@@ -227,7 +249,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
     ldb2[S] = (uint32_t)(a.seg[S].ldb * ES);
     ktotal += kseg[S];
   });
-  const int nk = ktotal / KE;
+  int nk = ktotal / KE;      // K-grouped tiles: set per tile
   float amax_run = 0.f;     // Q8: largest |bf16 output| this lane wrote
 
   // The queue's tile index is broadcast through the last 16-byte slot of the
@@ -249,6 +271,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
     int a_r0, c_r0;                    // first row of the tile in A (no gather) and in C
     int64_t b_off = 0;
     float dq_b = 1.f, dq_b2 = 1.f;     // F8: 1 / (s_A s_B), 1 / (s_A s_B2)
+    int kg_e = 0, kg_k0 = 0, kg_k = 0; // KG: expert, first K column and K extent
     if constexpr (GROUPED) {
       // table reads at a uniform address: every lane gets the same value
       const int e = __builtin_amdgcn_readfirstlane(a.tile_expert[t / a.n_tiles]);
@@ -272,6 +295,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
         dq_b = 1.0f / (a.a_scale[0] * a.b_scale[e]);
         if constexpr (SWG) dq_b2 = 1.0f / (a.a_scale[0] * a.b2_scale[e]);
       }
+    } else if constexpr (KG) {
+      // expert, then N tile, then M tile (M fastest)
+      const int per = a.m_tiles * a.n_tiles;
+      kg_e = t / per;
+      const int rem = t - kg_e * per;
+      n_tile = rem / a.m_tiles;
+      r0 = (rem - n_tile * a.m_tiles) * BM;
+      mrows = min(BM, a.M - r0);
+      a_r0 = c_r0 = r0;
+      kg_k0 = __builtin_amdgcn_readfirstlane(a.kpre[kg_e]);
+      kg_k = __builtin_amdgcn_readfirstlane(a.kpre[kg_e + 1]) - kg_k0;
+      nk = kg_k / KE;
     } else {
       // Groups of DENSE_GM M panels: inside a group the tiles go N tile by N
       // tile with the M panel fastest, so a window of concurrent tiles spans a
@@ -314,9 +349,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       const GemmSeg& g = a.seg[S];
       const char* A = (const char*)g.A;
       const char* B = (const char*)g.B;
-      if constexpr (GATHER) rA[S] = make_rsrc(A, (int64_t)a.M * g.lda * ES);
-      else rA[S] = make_rsrc(A + (int64_t)a_r0 * g.lda * ES, (int64_t)mrows * g.lda * ES);
-      rB[S] = make_rsrc(B + b_off + (int64_t)n0 * g.ldb * ES, (int64_t)nrows * g.ldb * ES);
+      if constexpr (GATHER) {
+        rA[S] = make_rsrc(A, (int64_t)a.M * g.lda * ES);
+      } else if constexpr (KG) {
+        // rows of this tile, columns [kg_k0, kg_k0 + kg_k) of each
+        rA[S] = make_rsrc(A + ((int64_t)a_r0 * g.lda + kg_k0) * ES,
+                          mrows > 0 ? ((int64_t)(mrows - 1) * g.lda + kg_k) * ES : 0);
+      } else {
+        rA[S] = make_rsrc(A + (int64_t)a_r0 * g.lda * ES, (int64_t)mrows * g.lda * ES);
+      }
+      if constexpr (KG)
+        rB[S] = make_rsrc(B + ((int64_t)n0 * g.ldb + kg_k0) * ES,
+                          nrows > 0 ? ((int64_t)(nrows - 1) * g.ldb + kg_k) * ES : 0);
+      else
+        rB[S] = make_rsrc(B + b_off + (int64_t)n0 * g.ldb * ES, (int64_t)nrows * g.ldb * ES);
       if constexpr (SWG)
         rU[S] = make_rsrc((const char*)g.B2 + b_off + (int64_t)n0 * g.ldb * ES,
                           (int64_t)nrows * g.ldb * ES);
@@ -475,6 +521,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
     // ---- epilogue: in a 32x32 block, lane l holds column l & 31 and, in
     // register r, row 8 * (r / 4) + 4 * (l / 32) + r % 4 ----
     const float oscale = Q8 ? a.out_scale[0] : 1.f;
+    const int64_t c_off = KG ? (int64_t)kg_e * a.c_expert_stride : 0;   // KG: the expert's block
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -489,7 +536,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
             if (cl < nrows) {
               const float g = acc[i][j][r] * dq_b, u = acc[i][j + 1][r] * dq_b2;
               const uint16_t hb = f32_to_bf16_rne(g / (1.0f + __expf(-g)) * u);
-              if constexpr (EPI == EPI_SWIGLU_Q8) {
+              if constexpr (EPI == EPI_GU_F32) {
+                const int64_t o = row * a.ldc + n0 + cl;
+                ((float*)a.C)[o] = g;
+                ((float*)a.C2)[o] = u;
+                ((uint16_t*)a.C3)[o] = hb;
+              } else if constexpr (EPI == EPI_SWIGLU_Q8) {
                 const float hv = bf16_to_f32(hb);
                 amax_run = fmaxf(amax_run, fabsf(hv));
                 ((uint8_t*)a.C)[row * a.ldc + n0 + cl] = f32_to_e4m3_sat(hv * oscale);
@@ -507,6 +559,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
             const float val = acc[i][j][r] * dq_b;
             if constexpr (EPI == EPI_BF16) {
               ((uint16_t*)a.C)[row * a.ldc + col] = f32_to_bf16_rne(val);
+            } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+              // val = dh; h = silu(g) u with silu(g) = g s, s = sigmoid(g)
+              const int64_t o = row * a.ldc + col;
+              const float g = a.aux_g[o], u = a.aux_u[o];
+              const float sg = 1.0f / (1.0f + __expf(-g));
+              const float dg = val * u * (sg * (1.0f + g * (1.0f - sg)));
+              const float du = val * (g * sg);
+              if (a.sr) {
+                ((uint16_t*)a.C)[o] = f32_to_bf16_sr(dg, a.sr_key_c, (uint64_t)o);
+                ((uint16_t*)a.C2)[o] = f32_to_bf16_sr(du, a.sr_key_c2, (uint64_t)o);
+              } else {
+                ((uint16_t*)a.C)[o] = f32_to_bf16_rne(dg);
+                ((uint16_t*)a.C2)[o] = f32_to_bf16_rne(du);
+              }
             } else if constexpr (EPI == EPI_Q8) {
               const float zv = bf16_to_f32(f32_to_bf16_rne(val));
               amax_run = fmaxf(amax_run, fabsf(zv));
@@ -514,7 +580,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
             } else if constexpr (EPI == EPI_F32_BIAS) {
               ((float*)a.C)[row * a.ldc + col] = val + (a.bias ? a.bias[col] : 0.f);
             } else {
-              ((float*)a.C)[row * a.ldc + col] = val;
+              ((float*)a.C)[c_off + row * a.ldc + col] = val;
             }
           }
         }
@@ -560,13 +626,14 @@ using TileBig = TileCfg<256, 256, 64, 2, 4, 2, false>;
 using TileMid = TileCfg<128, 256, 64, 2, 4, 3, false>;
 using TileRouter = TileCfg<64, 128, 64, 2, 2, 4, false>;
 
-template <class C, bool GROUPED, bool GATHER, int EPI, int NSEG = 1, bool F8 = false>
+template <class C, bool GROUPED, bool GATHER, int EPI, int NSEG = 1, bool F8 = false,
+          bool KG = false>
 hipError_t launch_gemm(const GemmArgs& a, int64_t tiles_upper_bound, hipStream_t s) {
   if (tiles_upper_bound <= 0) return hipSuccess;
   if (a.nseg != NSEG) return hipErrorInvalidValue;
   const int grid = persistent_grid(tiles_upper_bound);
   hipLaunchKernelGGL((gemm_kernel<C::bm, C::bn, C::bk, C::wm, C::wn, C::nstage, GROUPED, GATHER,
-                                  EPI, C::bnt, NSEG, F8>),
+                                  EPI, C::bnt, NSEG, F8, KG>),
                      dim3(grid), dim3(64 * C::wm * C::wn), 0, s, a);
   return hipGetLastError();
 }

@@ -82,6 +82,55 @@ hipError_t launch_round_experts(const uint16_t* z, const int32_t* seg_start,
 
 int device_cu_count();
 
+// backward (expert.hip): gate/up recomputation, SwiGLU backward GEMM, latent
+// gradient of the routed rows
+hipError_t launch_gate_up_recompute(const uint16_t* z, const int32_t* offsets,
+                                    const int32_t* row_token, const int32_t* tile_prefix,
+                                    const int32_t* tile_expert, int32_t* queue,
+                                    const uint16_t* w_gate, const uint16_t* w_up, int64_t T,
+                                    int64_t rows, int E, int L, int F, int bm, float* g, float* u,
+                                    uint16_t* h, hipStream_t s);
+hipError_t launch_swiglu_bwd(const uint16_t* dy_b, const int32_t* offsets,
+                             const int32_t* tile_prefix, const int32_t* tile_expert,
+                             int32_t* queue, const uint16_t* w_down_t, const float* g,
+                             const float* u, int64_t rows, int E, int L, int F, int bm, int sr,
+                             uint32_t key_dg, uint32_t key_du, uint16_t* dg_b, uint16_t* du_b,
+                             hipStream_t s);
+hipError_t launch_dzp(const uint16_t* dg_b, const uint16_t* du_b, const int32_t* offsets,
+                      const int32_t* tile_prefix, const int32_t* tile_expert, int32_t* queue,
+                      const uint16_t* w_gate_t, const uint16_t* w_up_t, int64_t rows, int E,
+                      int L, int F, int bm, float* dzp, hipStream_t s);
+
+// backward.hip
+hipError_t launch_cvt_grad(const float* src, int64_t n, int sr, uint32_t key, uint16_t* dst,
+                           hipStream_t s);
+hipError_t launch_kpad_prefix(const int32_t* offsets, int E, int32_t* kpre, hipStream_t s);
+hipError_t launch_transpose_dense(const uint16_t* src, int64_t nrows, int C, uint16_t* dst,
+                                  int64_t ldd, int batch, int64_t src_batch, int64_t dst_batch,
+                                  hipStream_t s);
+hipError_t launch_transpose_grouped(const uint16_t* src, const int32_t* gather, int64_t gather_rows,
+                                    int C, const int32_t* offsets, const int32_t* kpre, int E,
+                                    uint16_t* dst, int64_t ldd, hipStream_t s);
+hipError_t launch_combine_bwd(const float* dc, const float* y_rows, const float* topk_w,
+                              const int32_t* assign_row, int64_t T, int L, int k, int sr,
+                              uint32_t key, uint16_t* dy_b, float* dw, hipStream_t s);
+hipError_t launch_gather_sum(const float* dzp, const int32_t* assign_row, int64_t T, int L, int k,
+                             int sr, uint32_t key, uint16_t* dz_b, hipStream_t s);
+hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const float* dw, int64_t T,
+                             int E, int k, float* dl, hipStream_t s);
+hipError_t launch_router_dx(const float* dl, const float* w_router, int64_t T, int d, int E,
+                            float* dx, hipStream_t s);
+hipError_t launch_router_dw(const float* dl, const uint16_t* x, int64_t T, int d, int E,
+                            float* dw_router, hipStream_t s);
+int64_t router_db_partial_floats(int64_t T, int E);
+hipError_t launch_router_db(const float* dl, int64_t T, int E, float* part, float* db,
+                            hipStream_t s);
+hipError_t launch_dense_f32(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                            int64_t K, int64_t M, int N, float* C, int64_t ldc, hipStream_t s);
+hipError_t launch_kgrouped_f32(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                               const int32_t* kpre, int E, int M, int N, float* C,
+                               int64_t c_expert_stride, hipStream_t s);
+
 // fp8.hip: per-tensor amax of bf16 tensors (ntensor tensors of numel values,
 // numel a multiple of 8; amax holds float bits), E4M3 quantization with one
 // scale per tensor, delayed-scaling update, and a zero fill

@@ -117,6 +117,55 @@ int64_t max_rounds(int64_t T, int E, int k, int G, int C) {
   return m;
 }
 
+// backward: gradient casts and their transposes, recomputed expert
+// activations, the padded K layout of the weight-gradient GEMMs
+struct BwdWs {
+  size_t go, goT, z, cb, cbT, dc, dyb, dtw, g, u, h, dgb, dub, dzp, dzb, dzbT, xT, kpre, dybT, hT,
+      dgbT, dubT, zpT, dl, dbp, pre_a, pre_b, exp_a, exp_b, queues, total;
+  int64_t Tp, Rp;
+};
+BwdWs bwd_ws(int64_t T, int d, int L, int E, int k, int F) {
+  BwdWs w;
+  const int64_t R = T * k;
+  w.Tp = ceil_div(T, 64) * 64;
+  w.Rp = ceil_div(R, 64) * 64 + (int64_t)64 * E;   // >= sum_e ceil64(rows_e)
+  const size_t mt = (size_t)grouped_mtile_bound(R, E, 128);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align_up(bytes); return at; };
+  w.go = take((size_t)T * d * 2);
+  w.goT = take((size_t)d * w.Tp * 2);
+  w.z = take((size_t)T * L * 2);
+  w.cb = take((size_t)T * L * 2);
+  w.cbT = take((size_t)L * w.Tp * 2);
+  w.dc = take((size_t)T * L * 4);
+  w.dyb = take((size_t)R * L * 2);
+  w.dtw = take((size_t)R * 4);
+  w.g = take((size_t)R * F * 4);
+  w.u = take((size_t)R * F * 4);
+  w.h = take((size_t)R * F * 2);
+  w.dgb = take((size_t)R * F * 2);
+  w.dub = take((size_t)R * F * 2);
+  w.dzp = take((size_t)R * L * 4);
+  w.dzb = take((size_t)T * L * 2);
+  w.dzbT = take((size_t)L * w.Tp * 2);
+  w.xT = take((size_t)d * w.Tp * 2);
+  w.kpre = take((size_t)(E + 1) * 4);
+  w.dybT = take((size_t)L * w.Rp * 2);
+  w.hT = take((size_t)F * w.Rp * 2);
+  w.dgbT = take((size_t)F * w.Rp * 2);
+  w.dubT = take((size_t)F * w.Rp * 2);
+  w.zpT = take((size_t)L * w.Rp * 2);
+  w.dl = take((size_t)T * E * 4);
+  w.dbp = take((size_t)router_db_partial_floats(T, E) * 4);
+  w.pre_a = take((size_t)(E + 1) * 4);
+  w.pre_b = take((size_t)(E + 1) * 4);
+  w.exp_a = take(mt * 4);
+  w.exp_b = take(mt * 4);
+  w.queues = take(24 * 4);
+  w.total = o;
+  return w;
+}
+
 int check_route_dims(int64_t T, int d, int E, int k) {
   if (T < 0 || d <= 0 || E <= 0 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
   if (k > 16 || E > 1024 || !dims_ok(d)) return MOE_ERR_UNSUPPORTED;
@@ -148,6 +197,8 @@ size_t moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t L, int32_t E, i
     case MOE_OP_LATENT_FFN: return (L > 0 && F > 0) ? ffn_ws(T, L, E, k, F).total : 0;
     case MOE_OP_COMBINE: return L > 0 ? combine_ws(T, L) : 0;
     case MOE_OP_LATENT_FFN_FP8: return (L > 0 && F > 0) ? ffn8_ws(T, L, E, k, F).total : 0;
+    case MOE_OP_BACKWARD:
+      return (d > 0 && L > 0 && F > 0) ? bwd_ws(T, d, L, E, k, F).total : 0;
     default: return 0;
   }
 }
@@ -485,6 +536,179 @@ int moe_latent_ffn_forward_rounds(const uint16_t* x, const uint16_t* w_lat_down,
     if (st) return st;
   }
   return MOE_OK;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int moe_grad_cast_bf16(const float* src, int64_t n, int32_t rounding, uint32_t seed,
+                       int32_t stream_id, uint16_t* dst, void* stream) {
+  if (n < 0 || (rounding != MOE_ROUND_NEAREST && rounding != MOE_ROUND_STOCHASTIC))
+    return MOE_ERR_INVALID_ARG;
+  if (n % 4 != 0) return MOE_ERR_UNSUPPORTED;
+  if (n == 0) return MOE_OK;
+  if (!src || !dst) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(src) || ((uintptr_t)dst & 7u)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_cvt_grad(src, n, rounding == MOE_ROUND_STOCHASTIC,
+                                    sr_stream_key(seed, (uint32_t)stream_id), dst,
+                                    (hipStream_t)stream));
+}
+
+int moe_backward_prepare(const uint16_t* w_lat_down, const uint16_t* w_gate,
+                         const uint16_t* w_up, const uint16_t* w_down,
+                         const uint16_t* w_lat_up, int32_t d, int32_t L, int32_t E, int32_t F,
+                         uint16_t* w_lat_down_t, uint16_t* w_gate_t, uint16_t* w_up_t,
+                         uint16_t* w_down_t, uint16_t* w_lat_up_t, void* stream) {
+  if (E <= 0) return MOE_ERR_INVALID_ARG;
+  if (E > 1024 || !dims_ok(d) || !dims_ok(L) || !dims_ok(F)) return MOE_ERR_UNSUPPORTED;
+  const void* ptrs[] = {w_lat_down, w_gate, w_up, w_down, w_lat_up,
+                        w_lat_down_t, w_gate_t, w_up_t, w_down_t, w_lat_up_t};
+  for (const void* p : ptrs) {
+    if (!p) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t eFL = (int64_t)F * L;
+  int st = hip_status(launch_transpose_dense(w_lat_down, L, d, w_lat_down_t, L, 1, 0, 0, s));
+  if (!st) st = hip_status(launch_transpose_dense(w_gate, F, L, w_gate_t, F, E, eFL, eFL, s));
+  if (!st) st = hip_status(launch_transpose_dense(w_up, F, L, w_up_t, F, E, eFL, eFL, s));
+  if (!st) st = hip_status(launch_transpose_dense(w_down, L, F, w_down_t, L, E, eFL, eFL, s));
+  if (!st) st = hip_status(launch_transpose_dense(w_lat_up, d, L, w_lat_up_t, d, 1, 0, 0, s));
+  return st;
+}
+
+int moe_backward(const uint16_t* x, const float* w_router, const float* router_logits,
+                 int32_t bias_mode, const int32_t* topk_idx, const float* topk_w,
+                 const int32_t* expert_offsets, const int32_t* row_token,
+                 const int32_t* assign_row, const float* y_rows, const uint16_t* w_lat_down,
+                 const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_lat_down_t,
+                 const uint16_t* w_gate_t, const uint16_t* w_up_t, const uint16_t* w_down_t,
+                 const uint16_t* w_lat_up_t, const float* g_out, int64_t T, int32_t d,
+                 int32_t L, int32_t E, int32_t k, int32_t F, int32_t rounding, uint32_t seed,
+                 float* dx, float* dw_router, float* db_router, float* dw_lat_down,
+                 float* dw_gate, float* dw_up, float* dw_down, float* dw_lat_up, float* dtopk_w,
+                 void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || E <= 0 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (bias_mode != MOE_BIAS_LOGITS && bias_mode != MOE_BIAS_SELECTION) return MOE_ERR_INVALID_ARG;
+  if (rounding != MOE_ROUND_NEAREST && rounding != MOE_ROUND_STOCHASTIC)
+    return MOE_ERR_INVALID_ARG;
+  if (k > 16 || E > 1024 || !dims_ok(d) || !dims_ok(L) || !dims_ok(F) ||
+      T * (int64_t)k >= (int64_t(1) << 31) || (int64_t)T * L * 2 >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  const void* req[] = {x, w_router, router_logits, topk_idx, topk_w, expert_offsets, row_token,
+                       assign_row, y_rows, w_lat_down, w_gate, w_up, w_lat_down_t, w_gate_t,
+                       w_up_t, w_down_t, w_lat_up_t, g_out, dx, dw_router, dw_lat_down,
+                       dw_gate, dw_up, dw_down, dw_lat_up, ws};
+  for (const void* p : req)
+    if (!p) return MOE_ERR_INVALID_ARG;
+  const void* al[] = {x, w_router, router_logits, y_rows, w_lat_down, w_gate, w_up,
+                      w_lat_down_t, w_gate_t, w_up_t, w_down_t, w_lat_up_t, g_out, dx,
+                      dw_router, dw_lat_down, dw_gate, dw_up, dw_down, dw_lat_up, ws};
+  for (const void* p : al)
+    if (!aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  const BwdWs w = bwd_ws(T, d, L, E, k, F);
+  if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  auto B16 = [&](size_t off) { return (uint16_t*)(base + off); };
+  auto F32 = [&](size_t off) { return (float*)(base + off); };
+  auto I32 = [&](size_t off) { return (int32_t*)(base + off); };
+  const int sr = rounding == MOE_ROUND_STOCHASTIC;
+  const int64_t R = T * k;
+  const int64_t Tp = w.Tp, Rp = w.Rp;
+  float* dtw = dtopk_w ? dtopk_w : F32(w.dtw);
+  const ExpertGemmPlan plan = plan_expert_gemms(R, E);
+  int st;
+  {
+    // up-projection: g = bf16(g_out), dW_up = g^T c, dc = g W_up
+    EventScope ev(K_BWD_UP, s);
+    st = hip_status(launch_cvt_grad(g_out, T * d, sr, sr_stream_key(seed, 1), B16(w.go), s));
+    if (!st) st = hip_status(launch_transpose_dense(B16(w.go), T, d, B16(w.goT), Tp, 1, 0, 0, s));
+    if (!st) st = hip_status(launch_combine(y_rows, topk_w, assign_row, T, L, k, B16(w.cb), s));
+    if (!st) st = hip_status(launch_transpose_dense(B16(w.cb), T, L, B16(w.cbT), Tp, 1, 0, 0, s));
+    if (!st) st = hip_status(launch_dense_f32(B16(w.goT), Tp, B16(w.cbT), Tp, Tp, d, L, dw_lat_up,
+                                              L, s));
+    if (!st) st = hip_status(launch_dense_f32(B16(w.go), d, w_lat_up_t, d, d, T, L, F32(w.dc), L,
+                                              s));
+  }
+  if (st) return st;
+  {
+    EventScope ev(K_BWD_COMBINE, s);
+    st = hip_status(launch_combine_bwd(F32(w.dc), y_rows, topk_w, assign_row, T, L, k, sr,
+                                       sr_stream_key(seed, 2), B16(w.dyb), dtw, s));
+  }
+  if (st) return st;
+  {
+    // experts: z and g, u, h recomputed; dh with the SwiGLU backward in its
+    // epilogue; the rows' latent gradient
+    EventScope ev(K_BWD_DGRAD, s);
+    st = hip_status(launch_latent_down(x, w_lat_down, T, d, L, B16(w.z), s));
+    if (!st) st = hip_status(launch_tile_prefix(expert_offsets, E, plan.bm_gate_up, plan.bm_down,
+                                                I32(w.pre_a), I32(w.pre_b), I32(w.exp_a),
+                                                I32(w.exp_b), I32(w.queues), s));
+    if (!st) st = hip_status(launch_zero_u32((uint32_t*)I32(w.queues) + 16, 8, s));
+    if (!st) st = hip_status(launch_gate_up_recompute(
+        B16(w.z), expert_offsets, row_token, I32(w.pre_a), I32(w.exp_a), I32(w.queues), w_gate,
+        w_up, T, R, E, L, F, plan.bm_gate_up, F32(w.g), F32(w.u), B16(w.h), s));
+    if (!st) st = hip_status(launch_swiglu_bwd(
+        B16(w.dyb), expert_offsets, I32(w.pre_a), I32(w.exp_a), I32(w.queues) + 8, w_down_t,
+        F32(w.g), F32(w.u), R, E, L, F, plan.bm_gate_up, sr, sr_stream_key(seed, 3),
+        sr_stream_key(seed, 4), B16(w.dgb), B16(w.dub), s));
+    if (!st) st = hip_status(launch_dzp(B16(w.dgb), B16(w.dub), expert_offsets, I32(w.pre_b),
+                                        I32(w.exp_b), I32(w.queues) + 16, w_gate_t, w_up_t, R, E,
+                                        L, F, plan.bm_down, F32(w.dzp), s));
+  }
+  if (st) return st;
+  {
+    // expert weight gradients over each expert's rows (padded K layout)
+    EventScope ev(K_BWD_WGRAD, s);
+    int32_t* kpre = I32(w.kpre);
+    st = hip_status(launch_kpad_prefix(expert_offsets, E, kpre, s));
+    if (!st) st = hip_status(launch_transpose_grouped(B16(w.dyb), nullptr, 0, L, expert_offsets,
+                                                      kpre, E, B16(w.dybT), Rp, s));
+    if (!st) st = hip_status(launch_transpose_grouped(B16(w.h), nullptr, 0, F, expert_offsets,
+                                                      kpre, E, B16(w.hT), Rp, s));
+    if (!st) st = hip_status(launch_kgrouped_f32(B16(w.dybT), Rp, B16(w.hT), Rp, kpre, E, L, F,
+                                                 dw_down, (int64_t)L * F, s));
+    if (!st) st = hip_status(launch_transpose_grouped(B16(w.dgb), nullptr, 0, F, expert_offsets,
+                                                      kpre, E, B16(w.dgbT), Rp, s));
+    if (!st) st = hip_status(launch_transpose_grouped(B16(w.dub), nullptr, 0, F, expert_offsets,
+                                                      kpre, E, B16(w.dubT), Rp, s));
+    if (!st) st = hip_status(launch_transpose_grouped(B16(w.z), row_token, T, L, expert_offsets,
+                                                      kpre, E, B16(w.zpT), Rp, s));
+    if (!st) st = hip_status(launch_kgrouped_f32(B16(w.dgbT), Rp, B16(w.zpT), Rp, kpre, E, F, L,
+                                                 dw_gate, (int64_t)F * L, s));
+    if (!st) st = hip_status(launch_kgrouped_f32(B16(w.dubT), Rp, B16(w.zpT), Rp, kpre, E, F, L,
+                                                 dw_up, (int64_t)F * L, s));
+  }
+  if (st) return st;
+  {
+    // latent: dz per token (fixed slot order), dx = dz W_dn, dW_dn = dz^T x
+    EventScope ev(K_BWD_LATENT, s);
+    st = hip_status(launch_gather_sum(F32(w.dzp), assign_row, T, L, k, sr, sr_stream_key(seed, 5),
+                                      B16(w.dzb), s));
+    if (!st) st = hip_status(launch_dense_f32(B16(w.dzb), L, w_lat_down_t, L, L, T, d, dx, d, s));
+    if (!st) st = hip_status(launch_transpose_dense(B16(w.dzb), T, L, B16(w.dzbT), Tp, 1, 0, 0,
+                                                    s));
+    if (!st) st = hip_status(launch_transpose_dense(x, T, d, B16(w.xT), Tp, 1, 0, 0, s));
+    if (!st) st = hip_status(launch_dense_f32(B16(w.dzbT), Tp, B16(w.xT), Tp, Tp, L, d,
+                                              dw_lat_down, d, s));
+  }
+  if (st) return st;
+  // router (FP32): softmax backward, dx += dl W_r, dW_r = dl^T x, db
+  EventScope ev(K_BWD_ROUTER, s);
+  st = hip_status(launch_router_bwd(router_logits, topk_idx, dtw, T, E, k, F32(w.dl), s));
+  if (!st) st = hip_status(launch_router_dx(F32(w.dl), w_router, T, d, E, dx, s));
+  if (!st) st = hip_status(launch_router_dw(F32(w.dl), x, T, d, E, dw_router, s));
+  if (!st && db_router) {
+    if (bias_mode == MOE_BIAS_LOGITS)
+      st = hip_status(launch_router_db(F32(w.dl), T, E, F32(w.dbp), db_router, s));
+    else
+      st = hip_status(launch_zero_u32((uint32_t*)db_router, E, s));
+  }
+  return st;
 }
 
 }  // extern "C"

@@ -1,4 +1,4 @@
-"""One LatentMoE forward pass through libmoe's four entry points.
+"""LatentMoE forward (and backward) passes through libmoe's entry points.
 
 ``LatentMoEBuffers`` allocates (with torch, once) every output and workspace
 buffer a forward pass of a given shape needs; ``forward`` then only enqueues
@@ -36,7 +36,10 @@ class LatentMoEWeights:
 
 
 class LatentMoEBuffers:
-    def __init__(self, T, d, L, E, k, F, Fs=0, device="cuda"):
+    """Outputs and workspace of a forward pass.  keep_logits: also keep the
+    router logits [T, E] fp32, which the backward pass needs."""
+
+    def __init__(self, T, d, L, E, k, F, Fs=0, device="cuda", keep_logits=False):
         self.T, self.d, self.L, self.E, self.k, self.F, self.Fs = T, d, L, E, k, F, Fs
         dev = torch.device(device)
         i32, f32 = torch.int32, torch.float32
@@ -49,6 +52,7 @@ class LatentMoEBuffers:
         self.y_rows = torch.empty((T * k, L), dtype=f32, device=dev)
         self.hs = torch.empty((T, Fs), dtype=torch.bfloat16, device=dev) if Fs else None
         self.out = torch.empty((T, d), dtype=f32, device=dev)
+        self.logits = torch.empty((T, E), dtype=f32, device=dev) if keep_logits else None
         nb = max(_lib.moe_workspace_bytes(op, T, d, L, E, k, F, Fs) for op in range(5))
         # one workspace reused by the four calls (they run in order on one stream)
         self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
@@ -58,8 +62,8 @@ def forward(x, w: LatentMoEWeights, k, buf: LatentMoEBuffers, stream=None, route
     """Enqueue one forward pass; results land in ``buf`` (buf.out is [T, d] fp32).
     With route=False the caller's buf.topk_idx / buf.topk_w are used (router replay)."""
     if route:
-        _lib.moe_route(x, w.w_router, w.b_router, k, buf.topk_idx, buf.topk_w, ws=buf.ws,
-                       stream=stream)
+        _lib.moe_route(x, w.w_router, w.b_router, k, buf.topk_idx, buf.topk_w,
+                       logits_out=buf.logits, ws=buf.ws, stream=stream)
     _lib.moe_permute(buf.topk_idx, buf.E, buf.expert_counts, buf.expert_offsets, buf.row_token,
                      buf.assign_row, buf.ws, stream=stream)
     _lib.moe_latent_ffn_forward(x, w.w_lat_down, buf.expert_offsets, buf.row_token, w.w_gate,
@@ -172,3 +176,68 @@ def forward_rounds(x, w: LatentMoEWeights, k, buf: LatentMoEBuffers, capacity, g
     _lib.moe_combine(buf.y_rows, buf.topk_w, buf.assign_row, w.w_lat_up, buf.hs, w.ws_down,
                      buf.out, buf.ws, stream=stream)
     return buf.out
+
+
+# ---------------------------------------------------------------------------
+# backward pass
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class LatentMoETransposed:
+    """Transposed bf16 weight copies of the backward's data-gradient GEMMs."""
+    w_lat_down_t: torch.Tensor   # [d, L]
+    w_gate_t: torch.Tensor       # [E, L, F]
+    w_up_t: torch.Tensor         # [E, L, F]
+    w_down_t: torch.Tensor       # [E, F, L]
+    w_lat_up_t: torch.Tensor     # [L, d]
+
+
+def backward_prepare(w: LatentMoEWeights, stream=None) -> LatentMoETransposed:
+    d, L, E, F, _ = w.dims
+    dev = w.w_gate.device
+    bf = torch.bfloat16
+    t = LatentMoETransposed(torch.empty((d, L), dtype=bf, device=dev),
+                            torch.empty((E, L, F), dtype=bf, device=dev),
+                            torch.empty((E, L, F), dtype=bf, device=dev),
+                            torch.empty((E, F, L), dtype=bf, device=dev),
+                            torch.empty((L, d), dtype=bf, device=dev))
+    _lib.moe_backward_prepare(w.w_lat_down, w.w_gate, w.w_up, w.w_down, w.w_lat_up,
+                              t.w_lat_down_t, t.w_gate_t, t.w_up_t, t.w_down_t, t.w_lat_up_t,
+                              stream=stream)
+    return t
+
+
+class LatentMoEGrads:
+    """fp32 gradients of every parameter and of x, the gate weights' gradient,
+    and the backward's workspace."""
+
+    def __init__(self, T, d, L, E, k, F, device="cuda", bias=True):
+        dev = torch.device(device)
+        f32 = torch.float32
+        self.dx = torch.empty((T, d), dtype=f32, device=dev)
+        self.dw_router = torch.empty((E, d), dtype=f32, device=dev)
+        self.db_router = torch.empty(E, dtype=f32, device=dev) if bias else None
+        self.dw_lat_down = torch.empty((L, d), dtype=f32, device=dev)
+        self.dw_gate = torch.empty((E, F, L), dtype=f32, device=dev)
+        self.dw_up = torch.empty((E, F, L), dtype=f32, device=dev)
+        self.dw_down = torch.empty((E, L, F), dtype=f32, device=dev)
+        self.dw_lat_up = torch.empty((d, L), dtype=f32, device=dev)
+        self.dtopk_w = torch.empty((T, k), dtype=f32, device=dev)
+        nb = _lib.moe_workspace_bytes(_lib.MOE_OP_BACKWARD, T, d, L, E, k, F, 0)
+        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+
+
+def backward(x, w: LatentMoEWeights, wt: LatentMoETransposed, buf: LatentMoEBuffers, g_out,
+             grads: LatentMoEGrads, rounding=_lib.MOE_ROUND_STOCHASTIC, seed=0,
+             bias_mode=_lib.MOE_BIAS_LOGITS, stream=None):
+    """Enqueue the backward pass of the forward held in ``buf`` (run with
+    keep_logits=True) for dLoss/d out = g_out [T, d] fp32."""
+    if buf.logits is None:
+        raise ValueError("the forward buffers must keep the router logits (keep_logits=True)")
+    _lib.moe_backward(x, w.w_router, buf.logits, bias_mode, buf.topk_idx, buf.topk_w,
+                      buf.expert_offsets, buf.row_token, buf.assign_row, buf.y_rows, w.w_lat_down,
+                      w.w_gate, w.w_up, wt.w_lat_down_t, wt.w_gate_t, wt.w_up_t, wt.w_down_t,
+                      wt.w_lat_up_t, g_out, rounding, seed, grads.dx, grads.dw_router,
+                      grads.db_router, grads.dw_lat_down, grads.dw_gate, grads.dw_up,
+                      grads.dw_down, grads.dw_lat_up, grads.dtopk_w, grads.ws, stream=stream)
+    return grads

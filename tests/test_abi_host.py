@@ -25,7 +25,8 @@ def test_library_exports_every_declared_function():
     assert {"moe_route", "moe_route_ex", "moe_permute", "moe_latent_ffn_forward", "moe_combine",
             "moe_workspace_bytes", "moe_status_string", "moe_set_kernel_events", "moe_fp8_amax",
             "moe_fp8_quantize", "moe_fp8_scale_update", "moe_latent_ffn_forward_fp8",
-            "moe_workspace_bytes_rounds", "moe_latent_ffn_forward_rounds"} <= set(names)
+            "moe_workspace_bytes_rounds", "moe_latent_ffn_forward_rounds", "moe_backward_prepare",
+            "moe_backward", "moe_grad_cast_bf16"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -55,7 +56,7 @@ def test_workspace_sizes():
 
 def test_kernel_event_ids():
     lib = _lib.load()
-    assert lib.moe_set_kernel_events(8, None, None) == -1
+    assert lib.moe_set_kernel_events(14, None, None) == -1
     assert lib.moe_set_kernel_events(-1, None, None) == -1
     assert lib.moe_set_kernel_events(4, None, None) == 0
 
@@ -196,3 +197,36 @@ def test_rounds_workspace_and_bad_args():
     assert call(L=192 + 32) == -2
     assert call(wsb=100) == -3
     assert call(T=0) == 0
+
+
+def _bwd(lib, T=8, d=512, L=256, E=16, k=2, F=512, rounding=1, bias_mode=0, x=P, dx=P, wsb=1 << 40):
+    ptrs = [P] * 15
+    outs = [dx, P, None, P, P, P, P, P, None]
+    return lib.moe_backward(x, P, P, bias_mode, *ptrs, T, d, L, E, k, F, rounding, 7, *outs, P,
+                            wsb, None)
+
+
+def test_backward_workspace_and_bad_args():
+    lib = _lib.load()
+    T, d, L, E, k, F = 4096, 6656, 3072, 64, 8, 10240
+    assert _lib.moe_workspace_bytes(5, T, d, L, E, k, F) > T * k * F * 4 * 2   # g and u in fp32
+    assert _lib.moe_workspace_bytes(5, T, 0, L, E, k, F) == 0
+    assert _bwd(lib, rounding=2) == -1
+    assert _bwd(lib, bias_mode=3) == -1
+    assert _bwd(lib, k=0) == -1
+    assert _bwd(lib, L=200) == -2
+    assert _bwd(lib, x=None) == -1
+    assert _bwd(lib, dx=None) == -1
+    assert _bwd(lib, x=P + 4) == -2
+    assert _bwd(lib, wsb=1000) == -3
+    assert _bwd(lib, T=0) == 0
+    # prepare: sizes and pointers are checked before any launch
+    assert lib.moe_backward_prepare(P, P, P, P, P, 512, 256, 0, 512, P, P, P, P, P, None) == -1
+    assert lib.moe_backward_prepare(P, P, P, P, P, 500, 256, 16, 512, P, P, P, P, P, None) == -2
+    assert lib.moe_backward_prepare(P, P, P, None, P, 512, 256, 16, 512, P, P, P, P, P, None) == -1
+
+    assert lib.moe_grad_cast_bf16(P, 64, 2, 0, 1, P, None) == -1
+    assert lib.moe_grad_cast_bf16(P, 62, 1, 0, 1, P, None) == -2
+    assert lib.moe_grad_cast_bf16(P + 4, 64, 1, 0, 1, P, None) == -2
+    assert lib.moe_grad_cast_bf16(None, 64, 1, 0, 1, P, None) == -1
+    assert lib.moe_grad_cast_bf16(P, 0, 1, 0, 1, P, None) == 0
