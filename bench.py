@@ -45,7 +45,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", default="base1_small_batch")
+    p.add_argument("--config", default=None,
+                   help="workload (default: base1_small_batch; base1_ep8 with --backward)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--fp8", action="store_true",
                    help="routed experts' GEMMs in FP8 E4M3 with delayed scaling (not the headline "
@@ -55,6 +56,11 @@ def parse():
                         "multiple of the mean rows per expert (0: single pass)")
     p.add_argument("--group-size", type=int, default=8,
                    help="experts sharing capacity in the multi-round schedule")
+    p.add_argument("--backward", action="store_true",
+                   help="time the backward pass (moe_backward) after one forward pass instead "
+                        "of the forward (default workload then: base1_ep8)")
+    p.add_argument("--rounding", choices=["sr", "rne"], default="sr",
+                   help="backward gradient casts: stochastic (the pages' choice) or nearest")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain device copy of known size (for HBM counter scaling)")
     return p.parse_args()
@@ -206,6 +212,100 @@ def cpu_baseline(cfg, n_tok=2048, n_exp=24, seed=0, fp8=False):
     }
 
 
+BWD_KERNELS = ["bwd_up", "bwd_combine", "bwd_dgrad", "bwd_wgrad", "bwd_latent", "bwd_router"]
+
+
+def backward_flops(cfg):
+    """(model, executed) FLOPs of one backward pass.  Model: twice the
+    forward's (the data and the weight gradient of every GEMM), the count MFU
+    uses on the pages (recomputation excluded).  Executed adds the
+    recomputation of z (2TdL) and of the experts' gate/up (4TkLF)."""
+    T, d, L, E, k, F = cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F
+    model = 2.0 * (2.0 * T * d * E + 4.0 * T * d * L + 6.0 * T * k * L * F)
+    return model, model + 2.0 * T * d * L + 4.0 * T * k * L * F
+
+
+def bench_backward(args, cfg, dev):
+    """Time K backward passes (after one forward pass that keeps the router
+    logits) of the layer on seeded synthetic inputs and output gradient."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_moe_amd as moe
+    from moe_synth import device
+    if cfg.Fs:
+        print("the backward pass has no shared expert", file=sys.stderr)
+        sys.exit(2)
+    print(f"[bench] backward: {cfg.description}; generating inputs on the GPU", file=sys.stderr,
+          flush=True)
+    dv = device.device_inputs(cfg, dev)
+    w = moe.LatentMoEWeights(dv["w_router"], dv["b_router"], dv["w_dn"], dv["w_gate"], dv["w_up"],
+                             dv["w_down"], dv["w_lat_up"])
+    buf = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, device=dev,
+                               keep_logits=True)
+    moe.forward(dv["x"], w, cfg.k, buf)
+    wt = moe.backward_prepare(w)
+    grads = moe.LatentMoEGrads(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, device=dev,
+                               bias=dv["b_router"] is not None)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    g_out = torch.randn((cfg.T, cfg.d), generator=g, dtype=torch.float32, device=dev)
+    rounding = moe.MOE_ROUND_STOCHASTIC if args.rounding == "sr" else moe.MOE_ROUND_NEAREST
+    step = lambda i: moe.backward(dv["x"], w, wt, buf, g_out, grads, rounding=rounding,  # noqa: E731
+                                  seed=i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} backward steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    hip = HipEvents()
+    ev = {name: [(hip.create(), hip.create()) for _ in range(args.steps)] for name in BWD_KERNELS}
+    print(f"[bench] timing {args.steps} backward steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for name in BWD_KERNELS:
+            moe.moe_set_kernel_events(name, *ev[name][i])
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for name in BWD_KERNELS:
+        moe.moe_set_kernel_events(name, None, None)
+    kern_ms = {n: float(np.mean([hip.elapsed_ms(a, b) for a, b in ev[n]])) for n in BWD_KERNELS}
+    for pairs in ev.values():
+        for a, b in pairs:
+            hip.destroy(a)
+            hip.destroy(b)
+    elapsed = t1 - t0
+    ms = elapsed / args.steps * 1e3
+    model, executed = backward_flops(cfg)
+    # the experts' data-gradient group (gate/up recompute, dh + SwiGLU
+    # backward, the rows' latent gradient): 10 T k L F executed FLOPs
+    dgrad_flops = 10.0 * cfg.T * cfg.k * cfg.L * cfg.F
+    wgrad_flops = 6.0 * cfg.T * cfg.k * cfg.L * cfg.F
+    line = {
+        "metric": "LatentMoE layer bwd tokens/sec on 1 MI355X; % bf16 MFMA peak",
+        "value": cfg.T * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.description, "T": cfg.T, "d": cfg.d, "latent": cfg.L,
+                   "experts": cfg.E, "top_k": cfg.k, "ffn": cfg.F, "seed": cfg.seed,
+                   "rounding": args.rounding},
+        "roofline": {"bound": "mfma", "kernel": "expert data-gradient group (gate/up "
+                     "recompute, dh + SwiGLU backward, dz rows)",
+                     "achieved": dgrad_flops / (kern_ms["bwd_dgrad"] * 1e-3) / 1e12,
+                     "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                     "frac": dgrad_flops / (kern_ms["bwd_dgrad"] * 1e-3) / MFMA_BF16_PEAK,
+                     "traffic": None},
+        "layer": {"model_flops": model, "executed_flops": executed,
+                  "mfma_frac_model": model / (ms * 1e-3) / MFMA_BF16_PEAK,
+                  "mfma_frac_executed": executed / (ms * 1e-3) / MFMA_BF16_PEAK,
+                  "expert_wgrad_tflops": wgrad_flops / (kern_ms["bwd_wgrad"] * 1e-3) / 1e12,
+                  "kernels_ms": {k: round(v, 4) for k, v in kern_ms.items()}},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -218,8 +318,12 @@ def main():
     import mixture_experts_layer_moe_amd as moe
     from moe_synth import CONFIGS, device
 
+    if args.config is None:
+        args.config = "base1_ep8" if args.backward else "base1_small_batch"
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")
+    if args.backward:
+        return bench_backward(args, cfg, dev)
     print(f"[bench] {cfg.description}; generating inputs on the GPU", file=sys.stderr, flush=True)
     dv = device.device_inputs(cfg, dev)
     w = moe.LatentMoEWeights(dv["w_router"], dv["b_router"], dv["w_dn"], dv["w_gate"], dv["w_up"],

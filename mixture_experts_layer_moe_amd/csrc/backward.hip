@@ -321,20 +321,26 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const floa
 //   C[m, n] (+)= sum_k A(m, k) B(k, n),  A(m, k) = A[m sam + k sak],
 //   B(k, n) = B[k ldb + n] (TB = float or bf16 bits).
 // 64 x 64 tiles, K steps of 16, 4 x 4 outputs per thread; each output is
-// written by one thread (no atomics, fixed order).
+// written by one thread (no atomics, fixed order).  Split K: workgroup z
+// covers K range [z k_chunk, (z + 1) k_chunk) and writes its partial result
+// to C + z c_split (a fixed-order sum of the partials follows).
 template <typename TB, bool A_MCONTIG>
 __global__ __launch_bounds__(256) void f32_gemm_kernel(const float* __restrict__ A, int64_t sam,
                                                        int64_t sak, const TB* __restrict__ B,
                                                        int64_t ldb, int64_t M, int64_t N,
                                                        int64_t K, float* __restrict__ C,
-                                                       int64_t ldc, int accumulate) {
+                                                       int64_t ldc, int accumulate,
+                                                       int64_t k_chunk, int64_t c_split) {
   __shared__ float As[16][64 + 4];
   __shared__ float Bs[16][64 + 4];
   const int tid = threadIdx.x;
   const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
   const int ty = tid >> 4, tx = tid & 15;
   float acc[4][4] = {};
-  for (int64_t k0 = 0; k0 < K; k0 += 16) {
+  const int64_t kb0 = (int64_t)blockIdx.z * k_chunk;
+  const int64_t kend = kb0 + k_chunk < K ? kb0 + k_chunk : K;
+  C += (int64_t)blockIdx.z * c_split;
+  for (int64_t k0 = kb0; k0 < kend; k0 += 16) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = tid + 256 * q;
@@ -342,11 +348,11 @@ __global__ __launch_bounds__(256) void f32_gemm_kernel(const float* __restrict__
       if (A_MCONTIG) { mm = e & 63; kk = e >> 6; }
       else { kk = e & 15; mm = e >> 4; }
       const int64_t gm = m0 + mm, gk = k0 + kk;
-      As[kk][mm] = (gm < M && gk < K) ? A[gm * sam + gk * sak] : 0.f;
+      As[kk][mm] = (gm < M && gk < kend) ? A[gm * sam + gk * sak] : 0.f;
       const int nn = e & 63, kb = e >> 6;
       const int64_t gn = n0 + nn, gkb = k0 + kb;
       float bv = 0.f;
-      if (gn < N && gkb < K) {
+      if (gn < N && gkb < kend) {
         if constexpr (sizeof(TB) == 2) bv = bf16_to_f32(B[gkb * ldb + gn]);
         else bv = B[gkb * ldb + gn];
       }
@@ -387,17 +393,36 @@ hipError_t launch_router_dx(const float* dl, const float* w_router, int64_t T, i
   hipLaunchKernelGGL((f32_gemm_kernel<float, false>),
                      dim3((unsigned)ceil_div(d, 64), (unsigned)ceil_div(T, 64)), dim3(256), 0, s,
                      dl, (int64_t)E, (int64_t)1, w_router, (int64_t)d, T, (int64_t)d, (int64_t)E,
-                     dx, (int64_t)d, 1);
+                     dx, (int64_t)d, 1, (int64_t)E, (int64_t)0);
   return hipGetLastError();
 }
 
-// dW_r = dl^T x  (M = E, N = d, K = T; x bf16 [T, d])
+// dW_r = dl^T x  (M = E, N = d, K = T; x bf16 [T, d]).  K (the tokens) is
+// split into chunks of ROUTER_DW_CHUNK tokens whose partial sums are added in chunk
+// order by a second kernel.
+constexpr int64_t ROUTER_DW_CHUNK = 1024;
+int64_t router_dw_partial_floats(int64_t T, int d, int E) {
+  return ceil_div(T, ROUTER_DW_CHUNK) * (int64_t)E * d;
+}
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restrict__ part,
+                                                           int64_t nsplit, int64_t n,
+                                                           float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float acc = 0.f;
+  for (int64_t z = 0; z < nsplit; ++z) acc += part[z * n + i];
+  out[i] = acc;
+}
 hipError_t launch_router_dw(const float* dl, const uint16_t* x, int64_t T, int d, int E,
-                            float* dw_router, hipStream_t s) {
+                            float* part, float* dw_router, hipStream_t s) {
+  const int64_t nsplit = ceil_div(T, ROUTER_DW_CHUNK);
+  const int64_t n = (int64_t)E * d;
   hipLaunchKernelGGL((f32_gemm_kernel<uint16_t, true>),
-                     dim3((unsigned)ceil_div(d, 64), (unsigned)ceil_div(E, 64)), dim3(256), 0, s,
-                     dl, (int64_t)1, (int64_t)E, x, (int64_t)d, (int64_t)E, (int64_t)d, T,
-                     dw_router, (int64_t)d, 0);
+                     dim3((unsigned)ceil_div(d, 64), (unsigned)ceil_div(E, 64), (unsigned)nsplit),
+                     dim3(256), 0, s, dl, (int64_t)1, (int64_t)E, x, (int64_t)d, (int64_t)E,
+                     (int64_t)d, T, part, (int64_t)d, 0, ROUTER_DW_CHUNK, n);
+  hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, part,
+                     nsplit, n, dw_router);
   return hipGetLastError();
 }
 

@@ -120,8 +120,9 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* idx, const floa
                              int E, int k, float* dl, hipStream_t s);
 hipError_t launch_router_dx(const float* dl, const float* w_router, int64_t T, int d, int E,
                             float* dx, hipStream_t s);
+int64_t router_dw_partial_floats(int64_t T, int d, int E);
 hipError_t launch_router_dw(const float* dl, const uint16_t* x, int64_t T, int d, int E,
-                            float* dw_router, hipStream_t s);
+                            float* part, float* dw_router, hipStream_t s);
 int64_t router_db_partial_floats(int64_t T, int E);
 hipError_t launch_router_db(const float* dl, int64_t T, int E, float* part, float* db,
                             hipStream_t s);

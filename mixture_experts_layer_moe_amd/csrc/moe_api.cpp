@@ -121,7 +121,7 @@ int64_t max_rounds(int64_t T, int E, int k, int G, int C) {
 // activations, the padded K layout of the weight-gradient GEMMs
 struct BwdWs {
   size_t go, goT, z, cb, cbT, dc, dyb, dtw, g, u, h, dgb, dub, dzp, dzb, dzbT, xT, kpre, dybT, hT,
-      dgbT, dubT, zpT, dl, dbp, pre_a, pre_b, exp_a, exp_b, queues, total;
+      dgbT, dubT, zpT, dl, dbp, dwp, pre_a, pre_b, exp_a, exp_b, queues, total;
   int64_t Tp, Rp;
 };
 BwdWs bwd_ws(int64_t T, int d, int L, int E, int k, int F) {
@@ -157,6 +157,7 @@ BwdWs bwd_ws(int64_t T, int d, int L, int E, int k, int F) {
   w.zpT = take((size_t)L * w.Rp * 2);
   w.dl = take((size_t)T * E * 4);
   w.dbp = take((size_t)router_db_partial_floats(T, E) * 4);
+  w.dwp = take((size_t)router_dw_partial_floats(T, d, E) * 4);
   w.pre_a = take((size_t)(E + 1) * 4);
   w.pre_b = take((size_t)(E + 1) * 4);
   w.exp_a = take(mt * 4);
@@ -701,7 +702,7 @@ int moe_backward(const uint16_t* x, const float* w_router, const float* router_l
   EventScope ev(K_BWD_ROUTER, s);
   st = hip_status(launch_router_bwd(router_logits, topk_idx, dtw, T, E, k, F32(w.dl), s));
   if (!st) st = hip_status(launch_router_dx(F32(w.dl), w_router, T, d, E, dx, s));
-  if (!st) st = hip_status(launch_router_dw(F32(w.dl), x, T, d, E, dw_router, s));
+  if (!st) st = hip_status(launch_router_dw(F32(w.dl), x, T, d, E, F32(w.dwp), dw_router, s));
   if (!st && db_router) {
     if (bias_mode == MOE_BIAS_LOGITS)
       st = hip_status(launch_router_db(F32(w.dl), T, E, F32(w.dbp), db_router, s));

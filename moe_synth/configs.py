@@ -59,6 +59,13 @@ CONFIGS = {
     "base1_imbalanced": MoEConfig(
         "base1_imbalanced", T=32768, d=6656, L=3072, E=512, k=8, F=10240, zipf_bias=True,
         description="MAI-Base-1-shaped layer, T=32768, Zipf-like router bias"),
+    # one expert-parallel rank's share of the Base-1 layer (EP 8: 64 of the 512
+    # experts, each receiving ~T*k/64 rows of the rank's T tokens); sized so
+    # that the backward pass (fp32 weight gradients, transposed weight copies,
+    # recomputed activations) fits one GPU
+    "base1_ep8": MoEConfig(
+        "base1_ep8", T=32768, d=6656, L=3072, E=64, k=8, F=10240,
+        description="MAI-Base-1 layer, one EP-8 rank's share: T=32768, 64 experts"),
     "base2": MoEConfig(
         "base2", T=16384, d=8704, L=4096, E=512, k=7, F=8192, Fs=12288,
         description="MAI-Base-2-shaped layer, T=16384, top-7 + one shared expert"),

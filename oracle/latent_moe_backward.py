@@ -101,14 +101,17 @@ def sr_bits(seed: int, stream: int, index) -> np.ndarray:
     return (h >> np.uint32(16)).astype(np.uint32)
 
 
-def round_bf16_sr(v, seed: int, stream: int) -> np.ndarray:
+def round_bf16_sr(v, seed: int, stream: int, index=None) -> np.ndarray:
     """Stochastic rounding of float values to bf16 (returned as float64): v is
     taken to float32, the stream's 16 random bits are added to its bit
     pattern and the low 16 bits dropped.  Element i is the flat row-major
-    index of ``v``."""
+    index of ``v`` in its tensor: 0 .. v.size - 1, or ``index`` (same shape
+    as v) for a part of a larger tensor."""
     v32 = np.ascontiguousarray(np.asarray(v, np.float64).astype(np.float32))
     u = v32.view(np.uint32).astype(np.uint64)
-    r = sr_bits(seed, stream, np.arange(v32.size, dtype=np.int64)).reshape(v32.shape)
+    idx = np.arange(v32.size, dtype=np.int64) if index is None else \
+        np.asarray(index, np.int64).ravel()
+    r = sr_bits(seed, stream, idx).reshape(v32.shape)
     out = ((u + r.astype(np.uint64)) & np.uint64(0xFFFF0000)).astype(np.uint32)
     return out.view(np.float32).astype(np.float64)
 
