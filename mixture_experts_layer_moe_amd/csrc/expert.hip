@@ -243,14 +243,37 @@ hipError_t launch_expert_down(const uint16_t* H, const int32_t* offsets,
   return grouped_gemm<256, false, EPI_F32>(a, rows, s);
 }
 
-// Backward: the gate/up GEMM again (recomputation), keeping g and u in FP32
-// and h in bf16 (bit-identical to the forward's h: same tiles, same order).
-hipError_t launch_gate_up_recompute(const uint16_t* z, const int32_t* offsets,
-                                    const int32_t* row_token, const int32_t* tile_prefix,
-                                    const int32_t* tile_expert, int32_t* queue,
-                                    const uint16_t* w_gate, const uint16_t* w_up, int64_t T,
-                                    int64_t rows, int E, int L, int F, int bm, float* g, float* u,
-                                    uint16_t* h, hipStream_t s) {
+// Backward, first: dh = dy W_d[e] per expert (B = W_d[e]^T [F, L]), fp32.
+hipError_t launch_expert_dh(const uint16_t* dy_b, const int32_t* offsets,
+                            const int32_t* tile_prefix, const int32_t* tile_expert,
+                            int32_t* queue, const uint16_t* w_down_t, int64_t rows, int E, int L,
+                            int F, int bm, float* dh, hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = dy_b; a.seg[0].lda = L; a.seg[0].B = w_down_t; a.seg[0].ldb = L; a.seg[0].K = L;
+  a.nseg = 1;
+  a.N = F;
+  a.offsets = offsets;
+  a.tile_prefix = tile_prefix;
+  a.tile_expert = tile_expert;
+  a.queue = queue;
+  a.E = E;
+  a.b_expert_stride = (int64_t)F * L;
+  a.C = dh;
+  a.ldc = F;
+  if (bm == 128) return grouped_gemm<128, false, EPI_F32>(a, rows, s);
+  return grouped_gemm<256, false, EPI_F32>(a, rows, s);
+}
+
+// Backward, then: the gate/up GEMM again (recomputation: same tiles and order
+// as the forward, so g, u and h are the forward's bit for bit), with the
+// SwiGLU backward in its epilogue: dg = dh u silu'(g), du = dh silu(g) cast
+// to bf16 (RNE or stochastic rounding with the stream keys), and h.
+hipError_t launch_gate_up_bwd(const uint16_t* z, const int32_t* offsets, const int32_t* row_token,
+                              const int32_t* tile_prefix, const int32_t* tile_expert,
+                              int32_t* queue, const uint16_t* w_gate, const uint16_t* w_up,
+                              const float* dh, int64_t T, int64_t rows, int E, int L, int F, int bm,
+                              int sr, uint32_t key_dg, uint32_t key_du, uint16_t* dg_b,
+                              uint16_t* du_b, uint16_t* h, hipStream_t s) {
   GemmArgs a = {};
   a.seg[0].A = z; a.seg[0].lda = L; a.seg[0].B = w_gate; a.seg[0].B2 = w_up; a.seg[0].ldb = L;
   a.seg[0].K = L;
@@ -264,43 +287,16 @@ hipError_t launch_gate_up_recompute(const uint16_t* z, const int32_t* offsets,
   a.row_token = row_token;
   a.queue = queue;
   a.M = (int)T;
-  a.C = g;
-  a.C2 = u;
-  a.C3 = h;
-  a.ldc = F;
-  if (bm == 128) return grouped_gemm<128, true, EPI_GU_F32>(a, rows, s);
-  return grouped_gemm<256, true, EPI_GU_F32>(a, rows, s);
-}
-
-// Backward: dh = dy W_d[e] per expert (B = W_d[e]^T [F, L]), and in the
-// epilogue dg = dh u silu'(g), du = dh silu(g), both cast to bf16 (RNE or
-// stochastic rounding with the stream keys).
-hipError_t launch_swiglu_bwd(const uint16_t* dy_b, const int32_t* offsets,
-                             const int32_t* tile_prefix, const int32_t* tile_expert,
-                             int32_t* queue, const uint16_t* w_down_t, const float* g,
-                             const float* u, int64_t rows, int E, int L, int F, int bm, int sr,
-                             uint32_t key_dg, uint32_t key_du, uint16_t* dg_b, uint16_t* du_b,
-                             hipStream_t s) {
-  GemmArgs a = {};
-  a.seg[0].A = dy_b; a.seg[0].lda = L; a.seg[0].B = w_down_t; a.seg[0].ldb = L; a.seg[0].K = L;
-  a.nseg = 1;
-  a.N = F;
-  a.offsets = offsets;
-  a.tile_prefix = tile_prefix;
-  a.tile_expert = tile_expert;
-  a.queue = queue;
-  a.E = E;
-  a.b_expert_stride = (int64_t)F * L;
   a.C = dg_b;
   a.C2 = du_b;
-  a.aux_g = g;
-  a.aux_u = u;
+  a.C3 = h;
+  a.aux_g = dh;
   a.sr = sr;
   a.sr_key_c = key_dg;
   a.sr_key_c2 = key_du;
   a.ldc = F;
-  if (bm == 128) return grouped_gemm<128, false, EPI_SWIGLU_BWD>(a, rows, s);
-  return grouped_gemm<256, false, EPI_SWIGLU_BWD>(a, rows, s);
+  if (bm == 128) return grouped_gemm<128, true, EPI_GU_BWD>(a, rows, s);
+  return grouped_gemm<256, true, EPI_GU_BWD>(a, rows, s);
 }
 
 // Backward: the rows' latent gradient dzp = dg W_g[e] + du W_u[e] (fp32), one

@@ -71,12 +71,12 @@ constexpr uint32_t RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data format
 constexpr int DENSE_GM = 4;                     // M panels per tile group (dense GEMMs)
 
 enum GemmEpi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_BIAS = 2, EPI_SWIGLU = 3, EPI_Q8 = 4,
-               EPI_SWIGLU_Q8 = 5, EPI_GU_F32 = 6, EPI_SWIGLU_BWD = 7 };
+               EPI_SWIGLU_Q8 = 5, EPI_GU_BWD = 6 };
 
 // B tiles that interleave the gate and up matrices (a lane holds g and u of
 // the same element)
 constexpr bool epi_swiglu(int epi) {
-  return epi == EPI_SWIGLU || epi == EPI_SWIGLU_Q8 || epi == EPI_GU_F32;
+  return epi == EPI_SWIGLU || epi == EPI_SWIGLU_Q8 || epi == EPI_GU_BWD;
 }
 constexpr float E4M3_MAX = 448.0f;
 
@@ -119,18 +119,18 @@ struct GemmArgs {
   const int32_t* seg_end;
   const int32_t* h_base;
   int h_side;
-  // backward.  EPI_GU_F32: g -> C, u -> C2 (fp32), h = bf16(silu(g) u) -> C3.
-  // EPI_SWIGLU_BWD: the accumulator is dh; with g = aux_g, u = aux_u at the
-  // same (row, column) (leading dimension ldc), dg -> C and du -> C2 as bf16,
+  // backward.  EPI_GU_BWD (the gate/up GEMM recomputed): with g, u the
+  // accumulators and dh = aux_g at the same (row, column) (leading dimension
+  // ldc, fp32): dg = dh u silu'(g) -> C and du = dh silu(g) -> C2 as bf16,
   // rounded to nearest even (sr == 0) or stochastically with the random
-  // stream keys sr_key_c, sr_key_c2 (element index row * ldc + column).
+  // stream keys sr_key_c, sr_key_c2 (element index row * ldc + column), and
+  // h = bf16(silu(g) u) -> C3 (the forward's h, bit for bit).
   // KG (K-grouped tiles, weight gradients): tile -> (expert, M tile, N tile)
   // with expert e's K range [kpre[e], kpre[e + 1]) of A and B (multiples of
   // the stage width), C of expert e at C + e * c_expert_stride.
   void* C2;
   void* C3;
   const float* aux_g;
-  const float* aux_u;
   uint32_t sr_key_c, sr_key_c2;
   int sr;
   const int32_t* kpre;
@@ -536,10 +536,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
             if (cl < nrows) {
               const float g = acc[i][j][r] * dq_b, u = acc[i][j + 1][r] * dq_b2;
               const uint16_t hb = f32_to_bf16_rne(g / (1.0f + __expf(-g)) * u);
-              if constexpr (EPI == EPI_GU_F32) {
+              if constexpr (EPI == EPI_GU_BWD) {
                 const int64_t o = row * a.ldc + n0 + cl;
-                ((float*)a.C)[o] = g;
-                ((float*)a.C2)[o] = u;
+                const float dh = a.aux_g[o];
+                const float sg = 1.0f / (1.0f + __expf(-g));
+                const float dg = dh * u * (sg * (1.0f + g * (1.0f - sg)));
+                const float du = dh * (g * sg);
+                if (a.sr) {
+                  ((uint16_t*)a.C)[o] = f32_to_bf16_sr(dg, a.sr_key_c, (uint64_t)o);
+                  ((uint16_t*)a.C2)[o] = f32_to_bf16_sr(du, a.sr_key_c2, (uint64_t)o);
+                } else {
+                  ((uint16_t*)a.C)[o] = f32_to_bf16_rne(dg);
+                  ((uint16_t*)a.C2)[o] = f32_to_bf16_rne(du);
+                }
                 ((uint16_t*)a.C3)[o] = hb;
               } else if constexpr (EPI == EPI_SWIGLU_Q8) {
                 const float hv = bf16_to_f32(hb);
@@ -559,20 +568,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
             const float val = acc[i][j][r] * dq_b;
             if constexpr (EPI == EPI_BF16) {
               ((uint16_t*)a.C)[row * a.ldc + col] = f32_to_bf16_rne(val);
-            } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-              // val = dh; h = silu(g) u with silu(g) = g s, s = sigmoid(g)
-              const int64_t o = row * a.ldc + col;
-              const float g = a.aux_g[o], u = a.aux_u[o];
-              const float sg = 1.0f / (1.0f + __expf(-g));
-              const float dg = val * u * (sg * (1.0f + g * (1.0f - sg)));
-              const float du = val * (g * sg);
-              if (a.sr) {
-                ((uint16_t*)a.C)[o] = f32_to_bf16_sr(dg, a.sr_key_c, (uint64_t)o);
-                ((uint16_t*)a.C2)[o] = f32_to_bf16_sr(du, a.sr_key_c2, (uint64_t)o);
-              } else {
-                ((uint16_t*)a.C)[o] = f32_to_bf16_rne(dg);
-                ((uint16_t*)a.C2)[o] = f32_to_bf16_rne(du);
-              }
             } else if constexpr (EPI == EPI_Q8) {
               const float zv = bf16_to_f32(f32_to_bf16_rne(val));
               amax_run = fmaxf(amax_run, fabsf(zv));

@@ -82,20 +82,18 @@ hipError_t launch_round_experts(const uint16_t* z, const int32_t* seg_start,
 
 int device_cu_count();
 
-// backward (expert.hip): gate/up recomputation, SwiGLU backward GEMM, latent
-// gradient of the routed rows
-hipError_t launch_gate_up_recompute(const uint16_t* z, const int32_t* offsets,
-                                    const int32_t* row_token, const int32_t* tile_prefix,
-                                    const int32_t* tile_expert, int32_t* queue,
-                                    const uint16_t* w_gate, const uint16_t* w_up, int64_t T,
-                                    int64_t rows, int E, int L, int F, int bm, float* g, float* u,
-                                    uint16_t* h, hipStream_t s);
-hipError_t launch_swiglu_bwd(const uint16_t* dy_b, const int32_t* offsets,
-                             const int32_t* tile_prefix, const int32_t* tile_expert,
-                             int32_t* queue, const uint16_t* w_down_t, const float* g,
-                             const float* u, int64_t rows, int E, int L, int F, int bm, int sr,
-                             uint32_t key_dg, uint32_t key_du, uint16_t* dg_b, uint16_t* du_b,
-                             hipStream_t s);
+// backward (expert.hip): dh, the gate/up recomputation with the SwiGLU backward in
+// its epilogue, the latent gradient of the routed rows
+hipError_t launch_expert_dh(const uint16_t* dy_b, const int32_t* offsets,
+                            const int32_t* tile_prefix, const int32_t* tile_expert,
+                            int32_t* queue, const uint16_t* w_down_t, int64_t rows, int E, int L,
+                            int F, int bm, float* dh, hipStream_t s);
+hipError_t launch_gate_up_bwd(const uint16_t* z, const int32_t* offsets, const int32_t* row_token,
+                              const int32_t* tile_prefix, const int32_t* tile_expert,
+                              int32_t* queue, const uint16_t* w_gate, const uint16_t* w_up,
+                              const float* dh, int64_t T, int64_t rows, int E, int L, int F, int bm,
+                              int sr, uint32_t key_dg, uint32_t key_du, uint16_t* dg_b,
+                              uint16_t* du_b, uint16_t* h, hipStream_t s);
 hipError_t launch_dzp(const uint16_t* dg_b, const uint16_t* du_b, const int32_t* offsets,
                       const int32_t* tile_prefix, const int32_t* tile_expert, int32_t* queue,
                       const uint16_t* w_gate_t, const uint16_t* w_up_t, int64_t rows, int E,

@@ -120,7 +120,7 @@ int64_t max_rounds(int64_t T, int E, int k, int G, int C) {
 // backward: gradient casts and their transposes, recomputed expert
 // activations, the padded K layout of the weight-gradient GEMMs
 struct BwdWs {
-  size_t go, goT, z, cb, cbT, dc, dyb, dtw, g, u, h, dgb, dub, dzp, dzb, dzbT, xT, kpre, dybT, hT,
+  size_t go, goT, z, cb, cbT, dc, dyb, dtw, dh, h, dgb, dub, dzp, dzb, dzbT, xT, kpre, dybT, hT,
       dgbT, dubT, zpT, dl, dbp, dwp, pre_a, pre_b, exp_a, exp_b, queues, total;
   int64_t Tp, Rp;
 };
@@ -140,8 +140,7 @@ BwdWs bwd_ws(int64_t T, int d, int L, int E, int k, int F) {
   w.dc = take((size_t)T * L * 4);
   w.dyb = take((size_t)R * L * 2);
   w.dtw = take((size_t)R * 4);
-  w.g = take((size_t)R * F * 4);
-  w.u = take((size_t)R * F * 4);
+  w.dh = take((size_t)R * F * 4);
   w.h = take((size_t)R * F * 2);
   w.dgb = take((size_t)R * F * 2);
   w.dub = take((size_t)R * F * 2);
@@ -642,21 +641,22 @@ int moe_backward(const uint16_t* x, const float* w_router, const float* router_l
   }
   if (st) return st;
   {
-    // experts: z and g, u, h recomputed; dh with the SwiGLU backward in its
-    // epilogue; the rows' latent gradient
+    // experts: dh = dy W_d; z and the gate/up GEMM recomputed with the SwiGLU
+    // backward in its epilogue (dg, du, and h for dW_d); the rows' latent
+    // gradient
     EventScope ev(K_BWD_DGRAD, s);
     st = hip_status(launch_latent_down(x, w_lat_down, T, d, L, B16(w.z), s));
     if (!st) st = hip_status(launch_tile_prefix(expert_offsets, E, plan.bm_gate_up, plan.bm_down,
                                                 I32(w.pre_a), I32(w.pre_b), I32(w.exp_a),
                                                 I32(w.exp_b), I32(w.queues), s));
     if (!st) st = hip_status(launch_zero_u32((uint32_t*)I32(w.queues) + 16, 8, s));
-    if (!st) st = hip_status(launch_gate_up_recompute(
-        B16(w.z), expert_offsets, row_token, I32(w.pre_a), I32(w.exp_a), I32(w.queues), w_gate,
-        w_up, T, R, E, L, F, plan.bm_gate_up, F32(w.g), F32(w.u), B16(w.h), s));
-    if (!st) st = hip_status(launch_swiglu_bwd(
-        B16(w.dyb), expert_offsets, I32(w.pre_a), I32(w.exp_a), I32(w.queues) + 8, w_down_t,
-        F32(w.g), F32(w.u), R, E, L, F, plan.bm_gate_up, sr, sr_stream_key(seed, 3),
-        sr_stream_key(seed, 4), B16(w.dgb), B16(w.dub), s));
+    if (!st) st = hip_status(launch_expert_dh(B16(w.dyb), expert_offsets, I32(w.pre_b),
+                                              I32(w.exp_b), I32(w.queues), w_down_t, R, E, L, F,
+                                              plan.bm_down, F32(w.dh), s));
+    if (!st) st = hip_status(launch_gate_up_bwd(
+        B16(w.z), expert_offsets, row_token, I32(w.pre_a), I32(w.exp_a), I32(w.queues) + 8,
+        w_gate, w_up, F32(w.dh), T, R, E, L, F, plan.bm_gate_up, sr, sr_stream_key(seed, 3),
+        sr_stream_key(seed, 4), B16(w.dgb), B16(w.dub), B16(w.h), s));
     if (!st) st = hip_status(launch_dzp(B16(w.dgb), B16(w.dub), expert_offsets, I32(w.pre_b),
                                         I32(w.exp_b), I32(w.queues) + 16, w_gate_t, w_up_t, R, E,
                                         L, F, plan.bm_down, F32(w.dzp), s));
