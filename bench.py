@@ -132,7 +132,7 @@ def layer_bytes(cfg, touched, esize=2):
     return w + T * d * 2.0 + T * d * 4.0
 
 
-def cpu_baseline(cfg, n_tok=2048, n_exp=24, seed=0, fp8=False):
+def cpu_baseline(cfg, n_tok=4096, n_exp=192, seed=0, fp8=False):
     """The oracle (float64 numpy, as it stands) on a bounded sample of the
     workload, extrapolated to tokens/s of the whole layer:
       router + permutation over all T tokens (timed in full),
