@@ -159,3 +159,31 @@ def test_grad_cast_bit_exact(cuda, stream_id, seed):
     torch.cuda.synchronize()
     got = dst.view(torch.int16).cpu().numpy().view(np.uint16)
     np.testing.assert_array_equal(got, OB.bf16_bits(oracle.round_bf16(v.astype(np.float64))))
+
+
+def test_backward_selection_bias_mode(cuda):
+    """Loss-free-balancer bias (selection only): the weights are the softmax of
+    the unbiased logits, the bias gets no gradient."""
+    cfg, host, dv, g_out = setup_case("zipf", cuda)
+    w = weights_of(dv)
+    buf = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, device=cuda,
+                               keep_logits=True)
+    moe.moe_route_ex(dv["x"], dv["w_router"], dv["b_router"], moe.MOE_BIAS_SELECTION, cfg.k,
+                     buf.topk_idx, buf.topk_w, logits_out=buf.logits, ws=buf.ws)
+    moe.forward(dv["x"], w, cfg.k, buf, route=False)
+    wt = moe.backward_prepare(w)
+    grads = moe.LatentMoEGrads(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, device=cuda)
+    moe.backward(dv["x"], w, wt, buf, torch.from_numpy(g_out).to(cuda), grads,
+                 rounding=moe.MOE_ROUND_STOCHASTIC, seed=3, bias_mode=moe.MOE_BIAS_SELECTION)
+    torch.cuda.synchronize()
+    gidx = U.to_np(buf.topk_idx)
+    ref = oracle.backward(host["x"], host["w_router"], host["b_router"], cfg.k, host["w_dn"],
+                          U.experts_of(host), host["w_lat_up"], g_out.astype(np.float64),
+                          mode="bf16_operands", rounding="sr", seed=3,
+                          routing=(gidx, U.to_np(buf.topk_w).astype(np.float64)),
+                          bias_mode="selection")
+    assert not np.any(U.to_np(grads.db_router))
+    for gname, oname in GRADS:
+        emax, erms = U.rel_err(U.to_np(getattr(grads, gname)), np.asarray(ref[oname]))
+        U.log(f"[zipf/selection] {gname}: max {emax:.2e} rms {erms:.2e}")
+        assert emax <= GRAD_TOL_MAX and erms <= GRAD_TOL_RMS, (gname, emax, erms)
