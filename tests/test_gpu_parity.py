@@ -31,6 +31,12 @@ CASES = {
     "deeptail": MoEConfig("deeptail", T=3000, d=320, L=192, E=4, k=1, F=320, seed=13),
     # Zipf-like router bias: hot experts and empty experts
     "zipf": MoEConfig("zipf", T=1024, d=256, L=128, E=64, k=4, F=256, zipf_bias=True, seed=11),
+    # degenerate cases of the method: one expert (a dense latent SwiGLU FFN,
+    # gate weight 1), every expert selected (k = E: a dense soft mixture), a
+    # single token
+    "single": MoEConfig("single", T=100, d=128, L=64, E=1, k=1, F=128, seed=15),
+    "dense": MoEConfig("dense", T=64, d=128, L=64, E=8, k=8, F=128, seed=17),
+    "one_token": MoEConfig("one_token", T=1, d=256, L=128, E=16, k=2, F=256, seed=19),
 }
 
 
@@ -281,3 +287,21 @@ def test_bitwise_determinism(cuda):
         for a, b in zip(outs[0], o):
             assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
                                b.view(torch.int32) if b.dtype == torch.float32 else b)
+
+
+def test_layer_empty_batch(cuda):
+    """T = 0: every entry point of a forward and a backward pass is a
+    successful no-op, and the permutation metadata is defined (all zero)."""
+    cfg = CASES["tiny"].replace(T=0)
+    dv = device.device_inputs(cfg, cuda)
+    w = weights_of(dv)
+    buf = moe.LatentMoEBuffers(0, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, device=cuda, keep_logits=True)
+    buf.expert_counts.fill_(7)
+    buf.expert_offsets.fill_(7)
+    moe.forward(dv["x"], w, cfg.k, buf)
+    wt = moe.backward_prepare(w)
+    grads = moe.LatentMoEGrads(0, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, device=cuda, bias=False)
+    moe.backward(dv["x"], w, wt, buf, torch.zeros((0, cfg.d), dtype=torch.float32, device=cuda),
+                 grads)
+    torch.cuda.synchronize()
+    assert not torch.any(buf.expert_counts) and not torch.any(buf.expert_offsets)
