@@ -1,0 +1,82 @@
+"""The entry points are capturable in a HIP graph: a forward pass and a
+backward pass captured once and replayed give, on every replay, bitwise the
+results of eager runs (the library launches kernels only -- no memset, no
+host synchronisation, no allocation -- and is deterministic).  Replays are
+interleaved with eager work and synchronisations, and every replay is
+checked."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_moe_amd as moe
+from moe_synth import MoEConfig, device
+
+pytestmark = pytest.mark.gpu
+
+CFG = MoEConfig("graph", T=512, d=256, L=128, E=32, k=4, F=256, zipf_bias=True, seed=51)
+
+
+@pytest.fixture(scope="module")
+def cuda():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.load()
+    return torch.device("cuda:0")
+
+
+def _weights(dv):
+    return moe.LatentMoEWeights(dv["w_router"], dv["b_router"], dv["w_dn"], dv["w_gate"],
+                                dv["w_up"], dv["w_down"], dv["w_lat_up"])
+
+
+def test_forward_and_backward_replay_bitwise(cuda):
+    cfg = CFG
+    dv = device.device_inputs(cfg, cuda)
+    w = _weights(dv)
+    wt = moe.backward_prepare(w)
+    g_out = torch.randn((cfg.T, cfg.d), generator=torch.Generator(device=cuda).manual_seed(5),
+                        device=cuda, dtype=torch.float32)
+
+    def bufs():
+        b = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, device=cuda,
+                                 keep_logits=True)
+        g = moe.LatentMoEGrads(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, device=cuda)
+        return b, g
+
+    def step(b, g):
+        moe.forward(dv["x"], w, cfg.k, b)
+        moe.backward(dv["x"], w, wt, b, g_out, g, rounding=moe.MOE_ROUND_STOCHASTIC, seed=9)
+
+    def snapshot(b, g):
+        return [t.clone() for t in (b.topk_idx, b.topk_w, b.row_token, b.y_rows, b.out, g.dx,
+                                    g.dw_gate, g.dw_down, g.dw_router, g.db_router)]
+
+    # eager reference
+    be, ge = bufs()
+    step(be, ge)
+    torch.cuda.synchronize()
+    ref = snapshot(be, ge)
+
+    # capture (after one eager warmup of the same buffers)
+    bg, gg = bufs()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(bg, gg)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(bg, gg)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (bg.out, gg.dx, gg.dw_gate, bg.expert_counts):
+            t.zero_()                      # stale results must not survive a replay
+        step(be, ge)                        # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = snapshot(bg, gg)
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager run"
+        assert torch.equal(bg.expert_counts.cpu(),
+                           torch.bincount(ref[0].cpu().view(-1).long(), minlength=cfg.E).int())
