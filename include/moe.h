@@ -354,8 +354,10 @@ int moe_latent_ffn_forward_rounds(const uint16_t* x, const uint16_t* w_lat_down,
  * mode), dw_lat_down [L, d], dw_gate [E, F, L], dw_up [E, F, L],
  * dw_down [E, L, F], dw_lat_up [d, L], dtopk_w [T, k] (nullable: the
  * gradient of the gate weights).  Workspace: MOE_OP_BACKWARD.  Limits and
- * errors as for the forward; Fs != 0 is MOE_ERR_UNSUPPORTED.  Deterministic:
- * every reduction has a fixed order.
+ * errors as for the forward, and T * k + 64 * E < 2^22 (the weight-gradient
+ * GEMMs address 256-row tiles of the transposed operands with 32-bit
+ * offsets); otherwise MOE_ERR_UNSUPPORTED.  There is no shared expert in the
+ * backward.  Deterministic: every reduction has a fixed order.
  */
 /* moe_grad_cast_bf16: dst[i] = src[i] cast to bf16 with the backward's
  * gradient rounding (MOE_ROUND_NEAREST, or MOE_ROUND_STOCHASTIC with the

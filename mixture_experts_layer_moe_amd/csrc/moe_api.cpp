@@ -609,6 +609,10 @@ int moe_backward(const uint16_t* x, const float* w_router, const float* router_l
   for (const void* p : al)
     if (!aligned16(p)) return MOE_ERR_UNSUPPORTED;
   const BwdWs w = bwd_ws(T, d, L, E, k, F);
+  // the weight-gradient GEMMs read 256-row tiles of the transposed operands
+  // (row length Tp or Rp) through 32-bit buffer offsets
+  if ((int64_t)256 * 2 * (w.Tp > w.Rp ? w.Tp : w.Rp) >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
   if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   char* base = (char*)ws;

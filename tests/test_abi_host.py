@@ -220,6 +220,7 @@ def test_backward_workspace_and_bad_args():
     assert _bwd(lib, x=P + 4) == -2
     assert _bwd(lib, wsb=1000) == -3
     assert _bwd(lib, T=0) == 0
+    assert _bwd(lib, T=1 << 19, k=8, L=64, d=64, F=64) == -2    # T*k rows beyond 2^22
     # prepare: sizes and pointers are checked before any launch
     assert lib.moe_backward_prepare(P, P, P, P, P, 512, 256, 0, 512, P, P, P, P, P, None) == -1
     assert lib.moe_backward_prepare(P, P, P, P, P, 500, 256, 16, 512, P, P, P, P, P, None) == -2
