@@ -59,6 +59,15 @@ hipError_t launch_router_gemm(const uint16_t* x, const float* w_router, const fl
     return launch_gemm<TileBig, false, false, EPI_F32_BIAS, 3>(a, (int64_t)a.m_tiles * a.n_tiles,
                                                             s);
   }
+  // mid batches (e.g. T = 16,384 at E = 512): 128 x 256 tiles, one per CU;
+  // the 64 x 128 router tile reads 3 fragment blocks per 2 MFMAs and is only
+  // worth it when nothing larger fills the chip
+  if (ceil_div(T, TileMid::bm) * ceil_div(E, TileMid::bn) >= device_cu_count()) {
+    a.m_tiles = (int)ceil_div(T, TileMid::bm);
+    a.n_tiles = (int)ceil_div(E, TileMid::bn);
+    return launch_gemm<TileMid, false, false, EPI_F32_BIAS, 3>(a, (int64_t)a.m_tiles * a.n_tiles,
+                                                            s);
+  }
   a.m_tiles = (int)ceil_div(T, TileRouter::bm);
   a.n_tiles = (int)ceil_div(E, TileRouter::bn);
   return launch_gemm<TileRouter, false, false, EPI_F32_BIAS, 3>(a, (int64_t)a.m_tiles * a.n_tiles,
