@@ -160,12 +160,17 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint4* lds, uint
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, 0, 0, NT ? 2 : 0);
 }
 
-// Position of 16-byte chunk c of LDS row r (KCH chunks per row).  128-byte
-// rows: c ^ (r & 7).  64-byte rows: c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1), which
-// maps rows r, r + 4, r + 8, r + 12 (same bank offset) to different chunks.
+// Position of 16-byte chunk c of LDS row r (KCH chunks per row).  gfx950's
+// LDS has 64 four-byte banks and serves a 16-byte-per-lane read 16 lanes
+// (256 bytes) at a time, so the 16 consecutive rows one such group of a
+// fragment read touches must cover all 16 bank quads.  128-byte rows: rows
+// r and r + 8 share a bank half, so c ^ (r & 7) ^ ((r >> 3) & 1) (measured:
+// 166 B/clk/CU of fragment reads against 103 for c ^ (r & 7)).  64-byte rows:
+// c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1), which maps rows r, r + 4, r + 8,
+// r + 12 (same bank quad) to different chunks.  Both depend on r & 15 only.
 template <int KCH>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (KCH == 8) return r & 7;
+  if constexpr (KCH == 8) return (r & 7) ^ ((r >> 3) & 1);
   else return ((r >> 1) & 3) ^ ((r >> 3) & 1);
 }
 
@@ -226,7 +231,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   const int wrow = wave / WN;
   const int wn0 = (wave % WN) * WTN;
   const int lrow = lane / KCH;                     // row inside a DMA row group
-  const int lchunk = (lane % KCH) ^ swz<KCH>(lrow);   // chunk this lane fetches
+  // chunk this lane fetches: the swizzle of its LDS row, which is
+  // (wave + i NW) RPI + lrow for DMA instruction i and equals
+  // wave RPI + lrow in its low four bits
+  static_assert((NW * RPI) % 16 == 0, "DMA row groups keep the swizzle per lane");
+  const int lchunk = (lane % KCH) ^ swz<KCH>(wave * RPI + lrow);
   const int fr = lane & 31;                        // fragment row inside a 32-row block
   const int fq = lane >> 5;                        // which half of a sub-step's K this lane holds
 
