@@ -31,8 +31,10 @@ Precision of the backward on the pages ("The Training and RL Infrastructure
 Behind MAI-Thinking-1", section 2 "Numerics", "Pre-training and mid-training
 precision"): weight-gradient GEMMs in BF16 with FP32 accumulation, the router
 and the MoE combine in FP32, and stochastic rounding wherever a gradient is
-cast from higher to lower precision.  (The data-gradient GEMMs are FP8 E5M2
-there; this build's backward runs them on BF16 operands.)
+cast from higher to lower precision.  The data-gradient GEMMs are FP8 E5M2
+there, with delayed scaling ("FP8 and MoE GEMMs"); ``grad_fp8`` selects that
+for the routed experts' two data-gradient GEMMs (below); without it they run
+on the bf16 operands.
 
 Modes
 -----
@@ -46,6 +48,28 @@ Modes
                    with the counter-based generator below).  dh, dz rows, the
                    combine gradient and everything on the router side stay
                    float64 (FP32 on the GPU).
+
+FP8 data gradients (``grad_fp8``, bf16_operands mode only).  The pages give
+the format (E5M2) and delayed scaling; the operand pairing is the plainest
+reading of an FP8 GEMM: both operands FP8, the gradient in E5M2 and the
+weight in E4M3 quantized as the forward quantizes it (one scale per expert
+matrix, 448 / its amax).  For each of dy, dg, du (per tensor, scale s from
+the caller's amax history, s = 448 / max history as for the forward; the
+E5M2 operand takes 128 s = 57344 / max, E5M2's largest finite value over the
+maximum) the operand is q = e5m2(float32(float32(v) * float32(128 s))), and
+    dh    = (q_dy Q(W_d[e])) / (128 s_dy  s_Wd[e])
+    dz_r  = (q_dg Q(W_g[e])) / (128 s_dg  s_Wg[e]) + (q_du Q(W_u[e])) / (128 s_du  s_Wu[e])
+with Q the forward's E4M3 quantization.  The bf16 copies of dy, dg, du still
+feed the weight-gradient GEMMs (BF16 on the pages).  The step's maxima
+max |dy|, max |dg|, max |du| (before scaling) are returned for the history.
+E5M2 (OCP): 5 exponent bits with bias 15, 2 fraction bits, subnormals below
+2^-14 spaced 2^-16, largest finite 57344; values saturate at +-57344.
+Rounding to E5M2: "rne" to nearest, ties to even; "sr" (the pages'
+stochastic rounding of a gradient cast): for a magnitude a >= 2^-14 with
+float32 bits u, the result is the float32 with bits (u + r) with the low 21
+bits cleared, r = top 21 bits of the stream hash below; below 2^-14 (scaled
+values 2^-30 of the tensor's maximum) to nearest even.  Streams 6 dy, 7 dg,
+8 du, element index as for the bf16 casts.
 
 Stochastic rounding (reading: the pages name the technique, not the
 generator).  A value v is first taken to float32 (the GPU holds it in fp32);
@@ -72,6 +96,10 @@ from . import latent_moe as F
 
 ROUNDINGS = ("rne", "sr")
 SR_STREAM = {"g_out": 1, "dy": 2, "dg": 3, "du": 4, "dz": 5}
+FP8_STREAM = {"dy": 6, "dg": 7, "du": 8}
+E5M2_MAX = 57344.0
+E5M2_MIN_NORMAL = 2.0 ** -14
+E5M2_OVER_E4M3 = 128.0      # 57344 / 448
 _M32 = np.uint64(0xFFFFFFFF)
 
 
@@ -91,14 +119,19 @@ def lowbias32(x) -> np.ndarray:
     return x.astype(np.uint32)
 
 
-def sr_bits(seed: int, stream: int, index) -> np.ndarray:
-    """Uniform 16-bit integers for elements ``index`` (int64 array) of a
-    stream, as defined in the module notes."""
+def sr_hash(seed: int, stream: int, index) -> np.ndarray:
+    """The stream's 32-bit hash of elements ``index`` (int64 array), as
+    defined in the module notes."""
     key = lowbias32(np.uint64((int(seed) + 0x9E3779B9 * int(stream)) & 0xFFFFFFFF))
     i = np.asarray(index, np.int64).astype(np.uint64)
     h = lowbias32((i & _M32) ^ np.uint64(key))
-    h = lowbias32(h.astype(np.uint64) ^ (i >> np.uint64(32)))
-    return (h >> np.uint32(16)).astype(np.uint32)
+    return lowbias32(h.astype(np.uint64) ^ (i >> np.uint64(32)))
+
+
+def sr_bits(seed: int, stream: int, index) -> np.ndarray:
+    """Uniform 16-bit integers for elements ``index`` (int64 array) of a
+    stream: the top 16 bits of its hash."""
+    return (sr_hash(seed, stream, index) >> np.uint32(16)).astype(np.uint32)
 
 
 def round_bf16_sr(v, seed: int, stream: int, index=None) -> np.ndarray:
@@ -114,6 +147,49 @@ def round_bf16_sr(v, seed: int, stream: int, index=None) -> np.ndarray:
     r = sr_bits(seed, stream, idx).reshape(v32.shape)
     out = ((u + r.astype(np.uint64)) & np.uint64(0xFFFF0000)).astype(np.uint32)
     return out.view(np.float32).astype(np.float64)
+
+
+def round_e5m2(v) -> np.ndarray:
+    """Round float64 values to E5M2 with ties to even, saturating at
+    +-57344.  Written from the format: the spacing of representable values is
+    2**(e - 2) in the binade [2**e, 2**(e+1)) for e >= -14, and 2**-16
+    below 2**-14."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), E5M2_MAX)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    quantum = np.exp2(np.maximum(e, -14.0) - 2.0)
+    r = np.minimum(np.rint(a / quantum) * quantum, E5M2_MAX)   # np.rint: half to even
+    return np.copysign(r, v)
+
+
+def round_e5m2_sr(x, seed: int, stream: int, index=None) -> np.ndarray:
+    """Stochastic rounding of float32 values x to E5M2 (returned as the
+    float64 values of the codes), as defined in the module notes: magnitudes
+    saturate at 57344; at or above 2**-14 the stream's top 21 hash bits are
+    added to the float32 bit pattern and the low 21 bits dropped; below, to
+    nearest even.  Element i is the flat index of x or ``index``."""
+    x32 = np.ascontiguousarray(np.asarray(x, np.float32))
+    a = np.minimum(np.abs(x32), np.float32(E5M2_MAX))
+    u = a.view(np.uint32).astype(np.uint64)
+    idx = np.arange(x32.size, dtype=np.int64) if index is None else \
+        np.asarray(index, np.int64).ravel()
+    r = (sr_hash(seed, stream, idx) >> np.uint32(11)).astype(np.uint64).reshape(x32.shape)
+    up = ((u + r) & np.uint64(0xFFE00000)).astype(np.uint32).view(np.float32).astype(np.float64)
+    sub = np.rint(a.astype(np.float64) * 2.0 ** 16) / 2.0 ** 16
+    out = np.where(a.astype(np.float64) >= E5M2_MIN_NORMAL, up, sub)
+    return np.copysign(out, x32.astype(np.float64))
+
+
+def quantize_grad_e5m2(v, scale, rounding: str, seed: int, name: str, index=None):
+    """E5M2 operand of a gradient tensor with (E4M3-convention) scale s:
+    the code values of e5m2(float32(float32(v) * float32(128 s))), float64."""
+    s5 = np.float32(E5M2_OVER_E4M3) * np.float32(scale)
+    x32 = np.asarray(v, np.float64).astype(np.float32) * s5
+    if rounding == "rne":
+        return round_e5m2(x32.astype(np.float64))
+    if rounding == "sr":
+        return round_e5m2_sr(x32, seed, FP8_STREAM[name], index)
+    raise ValueError(f"unknown rounding {rounding!r}")
 
 
 def bf16_bits(v) -> np.ndarray:
@@ -166,18 +242,19 @@ def combine_backward(dc, y_rows, topk_w, assign_row):
     return dy, dw
 
 
-def expert_backward(zr, w_gate, w_up, w_down, dy_b, mode):
+def expert_backward(zr, w_gate, w_up, w_down, dy_b, mode, dh=None):
     """First half of one expert's backward on its rows (the part before the
     gate/up gradients are rounded): recomputes g, u and h, and returns them
-    with dh = dy W_d, dg = dh u silu'(g), du = dh silu(g) and
-    dW_down = dy^T h."""
+    with dh = dy W_d (or the given dh), dg = dh u silu'(g), du = dh silu(g)
+    and dW_down = dy^T h."""
     wg = np.asarray(w_gate, np.float64)
     wu = np.asarray(w_up, np.float64)
     wd = np.asarray(w_down, np.float64)
     g = zr @ wg.T
     u = zr @ wu.T
     h = F._maybe_bf16(F.silu(g) * u, mode)
-    dh = dy_b @ wd
+    if dh is None:
+        dh = dy_b @ wd
     dg = dh * u * silu_grad(g)
     du = dh * F.silu(g)
     return {"g": g, "u": u, "h": h, "dh": dh, "dg": dg, "du": du,
@@ -189,16 +266,21 @@ def expert_backward(zr, w_gate, w_up, w_down, dy_b, mode):
 # ---------------------------------------------------------------------------
 
 def backward(x, w_router, b_router, k, w_dn, experts, w_lat_up, g_out, mode="exact",
-             rounding="rne", seed=0, routing=None, bias_mode="logits"):
+             rounding="rne", seed=0, routing=None, bias_mode="logits", grad_fp8=None):
     """Gradients of the LatentMoE forward (no shared expert) for dLoss/d out =
     g_out.  ``routing`` = (topk_idx, topk_w) replays a routing (the weights'
     gradient still flows through the softmax of this oracle's own logits at
-    the replayed indices).  Returns a dict with dx, dW_router, db_router,
-    dW_dn, dW_gate, dW_up, dW_down ([E, ...] arrays), dW_lat_up, the gate
-    weight gradient dtopk_w, the router logit gradient dlogits, and the
-    intermediates (go, dc, dy_b, dzp, dz, dz_b, ...)."""
+    the replayed indices).  ``grad_fp8`` = {"grad_scale": (s_dy, s_dg, s_du),
+    "w_scale": (s_Wg[E], s_Wu[E], s_Wd[E])} runs the experts' data-gradient
+    GEMMs in FP8 (module notes).  Returns a dict with dx, dW_router,
+    db_router, dW_dn, dW_gate, dW_up, dW_down ([E, ...] arrays), dW_lat_up,
+    the gate weight gradient dtopk_w, the router logit gradient dlogits, the
+    intermediates (go, dc, dy_b, dzp, dz, dz_b, ...) and, with grad_fp8, the
+    maxima "grad_amax" = (max|dy|, max|dg|, max|du|)."""
     if mode not in ("exact", "bf16_operands"):
         raise ValueError(f"backward mode {mode!r} not supported")
+    if grad_fp8 is not None and mode != "bf16_operands":
+        raise ValueError("FP8 data gradients need the bf16_operands mode")
     if rounding not in ROUNDINGS:
         raise ValueError(f"unknown rounding {rounding!r}")
     x = np.asarray(x, np.float64)
@@ -235,6 +317,11 @@ def backward(x, w_router, b_router, k, w_dn, experts, w_lat_up, g_out, mode="exa
     # combine
     dy, dtopk_w = combine_backward(dc, y, w, assign_row)
     dy_b = _grad_round(dy, "dy", mode, rounding, seed)
+    if grad_fp8 is not None:
+        s_dy, s_dg, s_du = (np.float32(s) for s in grad_fp8["grad_scale"])
+        s_wg, s_wu, s_wd = (np.asarray(s, np.float32) for s in grad_fp8["w_scale"])
+        q_dy = quantize_grad_e5m2(dy, s_dy, rounding, seed, "dy")
+        f5 = float(np.float32(E5M2_OVER_E4M3))
     # experts
     dh = np.zeros((R, Fw), np.float64)
     dg = np.zeros((R, Fw), np.float64)
@@ -246,11 +333,19 @@ def backward(x, w_router, b_router, k, w_dn, experts, w_lat_up, g_out, mode="exa
         a, b = int(off[e]), int(off[e + 1])
         if a == b:
             continue
-        res = expert_backward(zp[a:b], *experts[e], dy_b[a:b], mode)
+        dh_e = None
+        if grad_fp8 is not None:
+            # W_d[e] is [L, F]: dh = q_dy Q(W_d[e]) over L
+            dh_e = (q_dy[a:b] @ F.quantize_e4m3(experts[e][2], s_wd[e])) / \
+                (f5 * float(s_dy) * float(s_wd[e]))
+        res = expert_backward(zp[a:b], *experts[e], dy_b[a:b], mode, dh=dh_e)
         dh[a:b], dg[a:b], du[a:b] = res["dh"], res["dg"], res["du"]
         dW_down[e] = res["dW_down"]
     dg_b = _grad_round(dg, "dg", mode, rounding, seed)
     du_b = _grad_round(du, "du", mode, rounding, seed)
+    if grad_fp8 is not None:
+        q_dg = quantize_grad_e5m2(dg, s_dg, rounding, seed, "dg")
+        q_du = quantize_grad_e5m2(du, s_du, rounding, seed, "du")
     dzp = np.zeros((R, L), np.float64)
     for e in range(E):
         a, b = int(off[e]), int(off[e + 1])
@@ -258,7 +353,12 @@ def backward(x, w_router, b_router, k, w_dn, experts, w_lat_up, g_out, mode="exa
             continue
         wg = np.asarray(experts[e][0], np.float64)
         wu = np.asarray(experts[e][1], np.float64)
-        dzp[a:b] = dg_b[a:b] @ wg + du_b[a:b] @ wu
+        if grad_fp8 is not None:
+            dzp[a:b] = (q_dg[a:b] @ F.quantize_e4m3(wg, s_wg[e])) / \
+                (f5 * float(s_dg) * float(s_wg[e])) + \
+                (q_du[a:b] @ F.quantize_e4m3(wu, s_wu[e])) / (f5 * float(s_du) * float(s_wu[e]))
+        else:
+            dzp[a:b] = dg_b[a:b] @ wg + du_b[a:b] @ wu
         dW_gate[e] = dg_b[a:b].T @ zp[a:b]
         dW_up[e] = du_b[a:b].T @ zp[a:b]
     # gather the rows' latent gradients back to their tokens, fixed slot order
@@ -285,7 +385,10 @@ def backward(x, w_router, b_router, k, w_dn, experts, w_lat_up, g_out, mode="exa
         db = np.zeros(E, np.float64)
     else:
         db = dl.sum(axis=0)
-    return {"dx": dx + dx_router, "dx_latent": dx, "dx_router": dx_router,
+    extra = {}
+    if grad_fp8 is not None:
+        extra["grad_amax"] = tuple(float(np.abs(t).max()) if t.size else 0.0 for t in (dy, dg, du))
+    return {**extra, "dx": dx + dx_router, "dx_latent": dx, "dx_router": dx_router,
             "dW_router": dW_router, "db_router": db, "dW_dn": dW_dn, "dW_gate": dW_gate,
             "dW_up": dW_up, "dW_down": dW_down, "dW_lat_up": dW_lat_up, "dtopk_w": dtopk_w,
             "dlogits": dl, "probs": probs, "go": go, "dc": dc, "dy_b": dy_b, "dh": dh,

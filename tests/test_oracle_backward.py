@@ -233,3 +233,139 @@ def test_lowbias32_is_a_bijection_by_its_inverse():
     np.testing.assert_array_equal(v, x)
     # and the published mixer's first values are well spread
     assert len(np.unique(B.lowbias32(np.arange(1 << 16)))) == 1 << 16
+
+
+# ---------------------------------------------------------------------------
+# FP8 E5M2 data gradients
+# ---------------------------------------------------------------------------
+
+def _e5m2_values():
+    """Every finite non-negative E5M2 value, from the code layout (sign,
+    5 exponent bits with bias 15, 2 fraction bits; exponent field 31 is
+    inf/NaN): subnormals m 2^-16, normals (1 + m/4) 2^(e - 15)."""
+    vals = [m * 2.0 ** -16 for m in range(4)]
+    for e in range(1, 31):
+        vals += [(1 + m / 4) * 2.0 ** (e - 15) for m in range(4)]
+    return np.array(vals)
+
+
+def test_e5m2_grid_closed_form():
+    v = _e5m2_values()
+    assert v.max() == 57344.0 and v[1] == 2.0 ** -16 and v[4] == 2.0 ** -14
+    assert np.array_equal(B.round_e5m2(v), v)
+    assert np.array_equal(B.round_e5m2(-v), -v)
+
+
+def test_e5m2_rne_midpoints_and_saturation():
+    v = _e5m2_values()
+    mid = (v[:-1] + v[1:]) / 2
+    got = B.round_e5m2(mid)
+    # ties go to the neighbour with an even fraction field
+    lo_even = (np.arange(v.size - 1) % 2) == 0
+    assert np.array_equal(got, np.where(lo_even, v[:-1], v[1:]))
+    assert np.array_equal(B.round_e5m2(mid * (1 + 1e-9)), v[1:])
+    assert np.array_equal(B.round_e5m2(mid * (1 - 1e-9)), v[:-1])
+    assert np.array_equal(B.round_e5m2([1e9, -7e4, 61440.0]), [57344.0, -57344.0, 57344.0])
+
+
+def _e5m2_neighbours(x):
+    v = _e5m2_values()
+    a = np.minimum(np.abs(x), 57344.0)
+    i = np.searchsorted(v, a, side="right") - 1
+    lo = v[i]
+    hi = v[np.minimum(i + 1, v.size - 1)]
+    return np.copysign(lo, x), np.copysign(hi, x)
+
+
+def test_e5m2_sr_picks_a_neighbour_and_keeps_exact_values():
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal(20000) * np.exp2(rng.integers(-13, 15, 20000))).astype(np.float32)
+    got = B.round_e5m2_sr(x, seed=3, stream=6)
+    lo, hi = _e5m2_neighbours(x.astype(np.float64))
+    assert np.all((got == lo) | (got == hi))
+    v = np.concatenate([_e5m2_values(), -_e5m2_values()]).astype(np.float32)
+    assert np.array_equal(B.round_e5m2_sr(v, seed=9, stream=7), v.astype(np.float64))
+    # below 2^-14: nearest even; above 57344: saturated
+    tiny = np.array([3e-5, 1.3e-5, -4.2e-5], np.float32)
+    assert np.array_equal(B.round_e5m2_sr(tiny, 1, 8), B.round_e5m2(tiny.astype(np.float64)))
+    assert np.array_equal(B.round_e5m2_sr(np.array([9e4, -1e30], np.float32), 1, 6),
+                          [57344.0, -57344.0])
+
+
+def test_e5m2_sr_is_unbiased():
+    # 1.1 lies between 1 and 1.25: rounds up with probability 0.4
+    n = 200000
+    x = np.full(n, 1.1, np.float32)
+    up = (B.round_e5m2_sr(x, seed=5, stream=7) == 1.25).mean()
+    p = (float(np.float32(1.1)) - 1.0) / 0.25
+    assert abs(up - p) < 5 * np.sqrt(p * (1 - p) / n)
+
+
+def test_grad_quantizer_scales_in_float32():
+    v = np.array([0.001, -0.02, 3.5e-3])
+    s = np.float32(448.0 / 0.03)
+    q = B.quantize_grad_e5m2(v, s, "rne", 0, "dy")
+    x32 = v.astype(np.float32) * (np.float32(128.0) * s)
+    assert np.array_equal(q, B.round_e5m2(x32.astype(np.float64)))
+
+
+def _fp8_args(p, gscale=(1.0, 1.0, 1.0)):
+    E = p["w_gate"].shape[0]
+    ws = [np.float32(448.0) / np.abs(p[n].reshape(E, -1)).max(axis=1).astype(np.float32)
+          for n in ("w_gate", "w_up", "w_down")]
+    return {"grad_scale": gscale, "w_scale": ws}
+
+
+def _amax_scales(p, k):
+    """Scales 224 / max of the step's own dy, dg, du (one binade of headroom:
+    the FP8 run's dg, du differ from those of the run that measured them)."""
+    r = bwd(p, k, mode="bf16_operands", rounding="rne", grad_fp8=_fp8_args(p))
+    return tuple(np.float32(224.0) / np.float32(m) for m in r["grad_amax"])
+
+
+def test_fp8_grad_mode_with_identity_quantizers_equals_bf16_mode(monkeypatch):
+    """The FP8 data-gradient path divides its scales back out and pairs the
+    operands like the bf16 path: with both quantizers replaced by exact
+    scaling, it reproduces bf16_operands mode."""
+    p, k = small_layer(seed=3)
+    ref = bwd(p, k, mode="bf16_operands", rounding="sr", seed=2)
+    # the bf16 path's operand (same stochastic rounding), scaled exactly
+    monkeypatch.setattr(B, "quantize_grad_e5m2",
+                        lambda v, s, r, seed, name, index=None:
+                        B.round_bf16_sr(v, seed, B.SR_STREAM[name])
+                        * float(np.float32(128.0) * np.float32(s)))
+    monkeypatch.setattr(B.F, "quantize_e4m3",
+                        lambda v, s: np.asarray(v, np.float64) * float(np.float32(s)))
+    got = bwd(p, k, mode="bf16_operands", rounding="sr", seed=2,
+              grad_fp8=_fp8_args(p, (0.75, 3.0, 40.0)))
+    for n in ("dx", "dW_dn", "dW_gate", "dW_up", "dW_down", "dzp", "dh"):
+        np.testing.assert_allclose(got[n], ref[n], rtol=1e-12, atol=1e-14, err_msg=n)
+
+
+def test_fp8_grad_mode_invariant_to_power_of_two_scales():
+    """Scaling a gradient tensor's scale by 2^j shifts its E5M2 exponents and
+    nothing else (no value reaches saturation or the subnormal range here):
+    the dequantized GEMMs, hence every gradient, are unchanged."""
+    p, k = small_layer(seed=5)
+    s = _amax_scales(p, k)
+    a = bwd(p, k, mode="bf16_operands", rounding="sr", seed=4, grad_fp8=_fp8_args(p, s))
+    s2 = (s[0] * np.float32(0.25), s[1] * np.float32(0.5), s[2] * np.float32(0.125))
+    b = bwd(p, k, mode="bf16_operands", rounding="sr", seed=4, grad_fp8=_fp8_args(p, s2))
+    for n in ("dx", "dW_dn", "dW_gate", "dW_up", "dW_down", "dzp", "dh"):
+        np.testing.assert_allclose(a[n], b[n], rtol=1e-13, atol=1e-15, err_msg=n)
+
+
+def test_fp8_grad_mode_close_to_bf16_mode_and_reports_maxima():
+    p, k = small_layer(seed=6, T=40, d=16, L=24, E=4, k=2, Fw=32)
+    s = _amax_scales(p, k)
+    ref = bwd(p, k, mode="bf16_operands", rounding="rne")
+    got = bwd(p, k, mode="bf16_operands", rounding="rne", grad_fp8=_fp8_args(p, s))
+    dy = np.zeros_like(got["dy_b"])
+    for j in range(k):
+        dy[got["assign_row"][:, j]] = got["topk_w"][:, j:j + 1] * got["dc"]
+    assert got["grad_amax"][0] == np.abs(dy).max()
+    for n in ("dh", "dzp", "dx"):
+        rel = np.sqrt(np.mean((got[n] - ref[n]) ** 2) / np.mean(ref[n] ** 2))
+        assert 1e-4 < rel < 0.1, (n, rel)     # FP8 noise: present, and small
+    for n in ("dW_down", "dW_lat_up"):        # upstream of / outside the FP8 GEMMs
+        np.testing.assert_array_equal(got[n], ref[n])
