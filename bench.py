@@ -59,6 +59,9 @@ def parse():
     p.add_argument("--backward", action="store_true",
                    help="time the backward pass (moe_backward) after one forward pass instead "
                         "of the forward (default workload then: base1_ep8)")
+    p.add_argument("--grad-fp8", action="store_true",
+                   help="with --backward: the experts' data-gradient GEMMs in FP8 (E5M2 "
+                        "gradients, E4M3 weights, delayed scaling)")
     p.add_argument("--rounding", choices=["sr", "rne"], default="sr",
                    help="backward gradient casts: stochastic (the pages' choice) or nearest")
     p.add_argument("--copy-calibration", action="store_true",
@@ -246,13 +249,21 @@ def bench_backward(args, cfg, dev):
     moe.forward(dv["x"], w, cfg.k, buf)
     wt = moe.backward_prepare(w)
     grads = moe.LatentMoEGrads(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, device=dev,
-                               bias=dv["b_router"] is not None)
+                               bias=dv["b_router"] is not None, fp8=args.grad_fp8)
     g = torch.Generator(device=dev)
     g.manual_seed(1234)
     g_out = torch.randn((cfg.T, cfg.d), generator=g, dtype=torch.float32, device=dev)
     rounding = moe.MOE_ROUND_STOCHASTIC if args.rounding == "sr" else moe.MOE_ROUND_NEAREST
-    step = lambda i: moe.backward(dv["x"], w, wt, buf, g_out, grads, rounding=rounding,  # noqa: E731
-                                  seed=i)
+    if args.grad_fp8:
+        # E4M3 transposed expert weights (the forward's scales) and the
+        # gradients' delayed scaling; warmup steps fill the amax history
+        wt8 = moe.quantize_transposed(wt, moe.quantize_experts(w))
+        gsc = moe.Fp8GradScaling(device=dev)
+        step = lambda i: moe.backward_fp8(dv["x"], w, wt, wt8, buf, g_out, grads, gsc,  # noqa: E731
+                                          rounding=rounding, seed=i)
+    else:
+        step = lambda i: moe.backward(dv["x"], w, wt, buf, g_out, grads,  # noqa: E731
+                                      rounding=rounding, seed=i)
     torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup} backward steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -282,19 +293,27 @@ def bench_backward(args, cfg, dev):
     # backward, the rows' latent gradient): 10 T k L F executed FLOPs
     dgrad_flops = 10.0 * cfg.T * cfg.k * cfg.L * cfg.F
     wgrad_flops = 6.0 * cfg.T * cfg.k * cfg.L * cfg.F
+    # its time at peak: all bf16, or (FP8 data gradients) the gate/up
+    # recompute (4 T k L F) at the bf16 peak and dh + dz rows (6 T k L F) at
+    # the FP8 peak
+    tkLF = cfg.T * cfg.k * cfg.L * cfg.F
+    dgrad_peak_s = (4.0 * tkLF / MFMA_BF16_PEAK + 6.0 * tkLF / MFMA_FP8_PEAK) if args.grad_fp8 \
+        else dgrad_flops / MFMA_BF16_PEAK
+    dgrad_s = kern_ms["bwd_dgrad"] * 1e-3
     line = {
         "metric": "LatentMoE layer bwd tokens/sec on 1 MI355X; % bf16 MFMA peak",
         "value": cfg.T * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16, fp8 data gradients" if args.grad_fp8 else "bf16", "data": "synthetic",
         "config": {"workload": cfg.description, "T": cfg.T, "d": cfg.d, "latent": cfg.L,
                    "experts": cfg.E, "top_k": cfg.k, "ffn": cfg.F, "seed": cfg.seed,
-                   "rounding": args.rounding},
+                   "rounding": args.rounding, "grad_fp8": bool(args.grad_fp8)},
         "roofline": {"bound": "mfma", "kernel": "expert data-gradient group (gate/up "
                      "recompute, dh + SwiGLU backward, dz rows)",
-                     "achieved": dgrad_flops / (kern_ms["bwd_dgrad"] * 1e-3) / 1e12,
-                     "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
-                     "frac": dgrad_flops / (kern_ms["bwd_dgrad"] * 1e-3) / MFMA_BF16_PEAK,
+                     "achieved": dgrad_flops / dgrad_s / 1e12,
+                     "peak": dgrad_flops / dgrad_peak_s / 1e12, "unit": "TFLOP/s",
+                     "frac": dgrad_peak_s / dgrad_s,
                      "traffic": None},
         "layer": {"model_flops": model, "executed_flops": executed,
                   "mfma_frac_model": model / (ms * 1e-3) / MFMA_BF16_PEAK,

@@ -385,6 +385,70 @@ int moe_backward(const uint16_t* x, const float* w_router, const float* router_l
                  float* dw_gate, float* dw_up, float* dw_down, float* dw_lat_up, float* dtopk_w,
                  void* ws, size_t ws_bytes, void* stream);
 
+/* ---- backward with FP8 data gradients ----------------------------------------
+ * "The Training and RL Infrastructure Behind MAI-Thinking-1", section 2
+ * "Numerics", "Pre-training and mid-training precision" (GEMM table: the
+ * backward's data-gradient GEMMs in FP8 E5M2; delayed scaling over a
+ * 1,024-step amax history; stochastic rounding of every gradient downcast)
+ * and section 3 "Custom kernels" ("FP8 and MoE GEMMs").
+ *
+ * E5M2 (OCP): exponent bias 15, 2 fraction bits, subnormals spaced 2^-16
+ * below 2^-14, largest finite 57344; casts saturate at +-57344.  A gradient
+ * tensor's scale s follows the E4M3 convention of the forward (s = 448 /
+ * max of its amax history, moe_fp8_scale_update); its E5M2 operand is
+ * e5m2(float32(v) * (128 s)) (57344 / 448 = 128).  Rounding: to nearest even
+ * (MOE_ROUND_NEAREST), or stochastic (MOE_ROUND_STOCHASTIC): for a magnitude
+ * at or above 2^-14, the top 21 bits of the stream's hash h (as for the
+ * bf16 casts above) are added to the fp32 bit pattern of the magnitude and
+ * the low 21 bits dropped; below 2^-14 to nearest even.  Streams: 6 dy, 7
+ * dg, 8 du (element index as for streams 2, 3, 4).
+ */
+
+/* moe_grad_cast_e5m2: dst[i] = e5m2(src[i] * 128 scale[0]) (one byte each),
+ * rounded with `rounding` (stochastic: stream `stream_id` under `seed`); the
+ * cast the FP8 backward applies to dy, dg and du.  n a multiple of 4; src
+ * 16-byte and dst 4-byte aligned (MOE_ERR_UNSUPPORTED); scale is a device
+ * fp32. */
+int moe_grad_cast_e5m2(const float* src, int64_t n, const float* scale, int32_t rounding,
+                       uint32_t seed, int32_t stream_id, uint8_t* dst, void* stream);
+
+/* moe_backward_fp8: moe_backward with the routed experts' two data-gradient
+ * GEMMs in FP8, the gradient operand in E5M2 and the weight in E4M3 (the
+ * forward's quantization, one scale per expert matrix):
+ *   dh   = (q_dy Q(W_d[e])) / (128 s_dy s_Wd[e])
+ *   dz_r = (q_dg Q(W_g[e])) / (128 s_dg s_Wg[e]) + (q_du Q(W_u[e])) / (128 s_du s_Wu[e])
+ * with q_t the E5M2 operand of gradient t.  The combine backward writes dy
+ * in bf16 (the weight-gradient GEMMs, BF16 on the pages) and in E5M2; the
+ * gate/up recompute writes dg and du likewise.  Arguments as for
+ * moe_backward, except:
+ *   w_gate_t8, w_up_t8 : [E, L, F] E4M3 bytes, Q(W_g[e])^T, Q(W_u[e])^T
+ *   w_down_t8          : [E, F, L] E4M3 bytes, Q(W_d[e])^T
+ *                        (e.g. moe_fp8_quantize of moe_backward_prepare's
+ *                        bf16 transposes with the forward's w_scale:
+ *                        quantizing commutes with transposing)
+ *   w_scale            : [3E] fp32, the scales of W_g[e], W_u[e], W_d[e] (as
+ *                        for moe_latent_ffn_forward_fp8)
+ *   grad_scale         : [3] fp32, s_dy, s_dg, s_du for this step (from their
+ *                        amax histories)
+ *   grad_amax (out)    : [3] fp32, max |dy|, max |dg|, max |du| of this step
+ *                        (fp32 values before scaling), for the histories
+ * The recompute of g, u and h stays bf16 (the forward's values).  L and F
+ * must be multiples of 128 (MOE_ERR_UNSUPPORTED).  Workspace:
+ * MOE_OP_BACKWARD_FP8.  Deterministic (the maxima are order-independent). */
+#define MOE_OP_BACKWARD_FP8  6
+int moe_backward_fp8(const uint16_t* x, const float* w_router, const float* router_logits,
+                     int32_t bias_mode, const int32_t* topk_idx, const float* topk_w,
+                     const int32_t* expert_offsets, const int32_t* row_token,
+                     const int32_t* assign_row, const float* y_rows, const uint16_t* w_lat_down,
+                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_lat_down_t,
+                     const uint8_t* w_gate_t8, const uint8_t* w_up_t8, const uint8_t* w_down_t8,
+                     const float* w_scale, const uint16_t* w_lat_up_t, const float* g_out,
+                     const float* grad_scale, int64_t T, int32_t d, int32_t L, int32_t E,
+                     int32_t k, int32_t F, int32_t rounding, uint32_t seed, float* dx,
+                     float* dw_router, float* db_router, float* dw_lat_down, float* dw_gate,
+                     float* dw_up, float* dw_down, float* dw_lat_up, float* dtopk_w,
+                     float* grad_amax, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- profiling hook ------------------------------------------------------
  * Register two hipEvent_t (created by the caller) that the library records on
  * the call's stream immediately before and after every launch of `kernel`

@@ -6,12 +6,14 @@ does not load the library; the first call does, and raises if it is missing.
 """
 from ._lib import (MOE_BIAS_LOGITS, MOE_BIAS_SELECTION, MOE_ROUND_NEAREST,  # noqa: F401
                    MOE_ROUND_STOCHASTIC, MoEError, load, moe_backward, moe_backward_prepare,
-                   moe_grad_cast_bf16,
+                   moe_backward_fp8, moe_grad_cast_bf16, moe_grad_cast_e5m2,
                    moe_combine, moe_fp8_amax, moe_fp8_quantize, moe_fp8_scale_update,
                    moe_latent_ffn_forward, moe_latent_ffn_forward_fp8,
                    moe_latent_ffn_forward_rounds, moe_permute, moe_route, moe_route_ex,
                    moe_set_kernel_events, moe_status_string, moe_workspace_bytes,
                    moe_workspace_bytes_rounds)
-from .layer import (Fp8Scaling, LatentMoEBuffers, LatentMoEFp8Experts,  # noqa: F401
-                    LatentMoEGrads, LatentMoETransposed, LatentMoEWeights, backward,
-                    backward_prepare, forward, forward_fp8, forward_rounds, quantize_experts)
+from .layer import (Fp8GradScaling, Fp8Scaling, LatentMoEBuffers,  # noqa: F401
+                    LatentMoEFp8Experts, LatentMoEFp8Transposed, LatentMoEGrads,
+                    LatentMoETransposed, LatentMoEWeights, backward, backward_fp8,
+                    backward_prepare, forward, forward_fp8, forward_rounds, quantize_experts,
+                    quantize_transposed)

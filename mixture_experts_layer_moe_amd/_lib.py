@@ -21,6 +21,7 @@ MOE_BIAS_LOGITS, MOE_BIAS_SELECTION = 0, 1
 MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_LATENT_FFN, MOE_OP_COMBINE = 0, 1, 2, 3
 MOE_OP_LATENT_FFN_FP8 = 4
 MOE_OP_BACKWARD = 5
+MOE_OP_BACKWARD_FP8 = 6
 MOE_ROUND_NEAREST, MOE_ROUND_STOCHASTIC = 0, 1
 KERNELS = {"router_gemm": 0, "router_topk": 1, "permute": 2, "latent_down": 3, "gate_up": 4,
            "expert_down": 5, "combine": 6, "latent_up": 7, "bwd_up": 8, "bwd_combine": 9,
@@ -86,6 +87,12 @@ def load():
     lib.moe_backward.restype = ctypes.c_int
     lib.moe_backward.argtypes = ([_vp, _vp, _vp, _i32] + [_vp] * 15 + [_i64, _i32, _i32, _i32,
                                   _i32, _i32, _i32, ctypes.c_uint32] + [_vp] * 10 + [_sz, _vp])
+    lib.moe_grad_cast_e5m2.restype = ctypes.c_int
+    lib.moe_grad_cast_e5m2.argtypes = [_vp, _i64, _vp, _i32, ctypes.c_uint32, _i32, _vp, _vp]
+    lib.moe_backward_fp8.restype = ctypes.c_int
+    lib.moe_backward_fp8.argtypes = ([_vp, _vp, _vp, _i32] + [_vp] * 17 + [_i64, _i32, _i32, _i32,
+                                      _i32, _i32, _i32, ctypes.c_uint32] + [_vp] * 11 +
+                                     [_sz, _vp])
     lib.moe_set_kernel_events.restype = ctypes.c_int
     lib.moe_set_kernel_events.argtypes = [ctypes.c_int, _vp, _vp]
     _lib = lib
@@ -356,4 +363,51 @@ def moe_grad_cast_bf16(src, rounding, seed, stream_id, dst, stream=None):
         raise ValueError("dst must have one value per src value")
     _check("moe_grad_cast_bf16", load().moe_grad_cast_bf16(
         _ptr(src), src.numel(), int(rounding), int(seed) & 0xFFFFFFFF, int(stream_id), _ptr(dst),
+        _stream(stream)))
+
+
+def moe_grad_cast_e5m2(src, scale, rounding, seed, stream_id, dst, stream=None):
+    _need(src, "src", torch.float32)
+    _need(scale, "scale", torch.float32)
+    _need(dst, "dst", torch.uint8)
+    if dst.numel() != src.numel():
+        raise ValueError("dst must have one byte per src value")
+    _check("moe_grad_cast_e5m2", load().moe_grad_cast_e5m2(
+        _ptr(src), src.numel(), _ptr(scale), int(rounding), int(seed) & 0xFFFFFFFF,
+        int(stream_id), _ptr(dst), _stream(stream)))
+
+
+def moe_backward_fp8(x, w_router, router_logits, bias_mode, topk_idx, topk_w, expert_offsets,
+                     row_token, assign_row, y_rows, w_lat_down, w_gate, w_up, w_lat_down_t,
+                     w_gate_t8, w_up_t8, w_down_t8, w_scale, w_lat_up_t, g_out, grad_scale,
+                     rounding, seed, dx, dw_router, db_router, dw_lat_down, dw_gate, dw_up,
+                     dw_down, dw_lat_up, dtopk_w, grad_amax, ws, stream=None):
+    _need(x, "x", torch.bfloat16, 2)
+    for n, t in (("w_router", w_router), ("router_logits", router_logits), ("topk_w", topk_w),
+                 ("y_rows", y_rows), ("g_out", g_out), ("dx", dx), ("dw_router", dw_router),
+                 ("db_router", db_router), ("dw_lat_down", dw_lat_down), ("dw_gate", dw_gate),
+                 ("dw_up", dw_up), ("dw_down", dw_down), ("dw_lat_up", dw_lat_up),
+                 ("dtopk_w", dtopk_w), ("w_scale", w_scale), ("grad_scale", grad_scale),
+                 ("grad_amax", grad_amax)):
+        _need(t, n, torch.float32)
+    for n, t in (("topk_idx", topk_idx), ("expert_offsets", expert_offsets),
+                 ("row_token", row_token), ("assign_row", assign_row)):
+        _need(t, n, torch.int32)
+    for n, t in (("w_lat_down", w_lat_down), ("w_gate", w_gate), ("w_up", w_up),
+                 ("w_lat_down_t", w_lat_down_t), ("w_lat_up_t", w_lat_up_t)):
+        _need(t, n, torch.bfloat16)
+    for n, t in (("w_gate_t8", w_gate_t8), ("w_up_t8", w_up_t8), ("w_down_t8", w_down_t8)):
+        _need(t, n, torch.uint8, 3)
+    _need(ws, "ws", torch.uint8, 1)
+    T, d = x.shape
+    E, F, L = w_gate.shape
+    k = topk_idx.shape[1]
+    _check("moe_backward_fp8", load().moe_backward_fp8(
+        _ptr(x), _ptr(w_router), _ptr(router_logits), int(bias_mode), _ptr(topk_idx),
+        _ptr(topk_w), _ptr(expert_offsets), _ptr(row_token), _ptr(assign_row), _ptr(y_rows),
+        _ptr(w_lat_down), _ptr(w_gate), _ptr(w_up), _ptr(w_lat_down_t), _ptr(w_gate_t8),
+        _ptr(w_up_t8), _ptr(w_down_t8), _ptr(w_scale), _ptr(w_lat_up_t), _ptr(g_out),
+        _ptr(grad_scale), T, d, L, E, k, F, int(rounding), int(seed) & 0xFFFFFFFF, _ptr(dx),
+        _ptr(dw_router), _ptr(db_router), _ptr(dw_lat_down), _ptr(dw_gate), _ptr(dw_up),
+        _ptr(dw_down), _ptr(dw_lat_up), _ptr(dtopk_w), _ptr(grad_amax), _ptr(ws), _nbytes(ws),
         _stream(stream)))

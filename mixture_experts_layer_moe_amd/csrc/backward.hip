@@ -52,6 +52,33 @@ hipError_t launch_cvt_grad(const float* src, int64_t n, int sr, uint32_t key, ui
   return hipGetLastError();
 }
 
+// fp32 -> E5M2 gradient cast: dst[i] = e5m2(src[i] * 128 scale[0]) with the
+// gradient rounding (element index = flat index); n a multiple of 4.
+__global__ __launch_bounds__(256) void cvt_e5m2_kernel(const float* __restrict__ src, int64_t n,
+                                                       const float* __restrict__ scale, int sr,
+                                                       uint32_t key, uint8_t* __restrict__ dst) {
+  const float s5 = E5M2_OVER_E4M3 * scale[0];
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    const float4 v = *(const float4*)(src + i);
+    uchar4 o;
+    o.x = f32_to_e5m2(v.x * s5, sr, key, (uint64_t)i);
+    o.y = f32_to_e5m2(v.y * s5, sr, key, (uint64_t)i + 1);
+    o.z = f32_to_e5m2(v.z * s5, sr, key, (uint64_t)i + 2);
+    o.w = f32_to_e5m2(v.w * s5, sr, key, (uint64_t)i + 3);
+    *(uchar4*)(dst + i) = o;
+  }
+}
+
+hipError_t launch_cvt_e5m2(const float* src, int64_t n, const float* scale, int sr, uint32_t key,
+                           uint8_t* dst, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = ceil_div(n / 4, 256);
+  hipLaunchKernelGGL(cvt_e5m2_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256),
+                     0, s, src, n, scale, sr, key, dst);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // padded K layout of the per-expert weight-gradient GEMMs: expert e's rows
 // become columns [kpre[e], kpre[e] + rows_e) of a transposed matrix, each
@@ -170,13 +197,19 @@ hipError_t launch_transpose_grouped(const uint16_t* src, const int32_t* gather, 
 // combine backward: for each (t, j), r = assign_row[t, j]:
 //   dy[r] = w[t, j] dc[t]            (FP32, then cast to bf16 for the GEMMs)
 //   dw[t, j] = dc[t] . y[r]          (FP32, fixed-order reduction)
-// One workgroup per token.
+// One workgroup per token.  Q8 (FP8 data gradients) also writes dy as E5M2
+// codes (dy8, scale 128 grad_scale[0], stream key key8) and records max |dy|
+// in grad_amax[0] (one integer atomic max per wave: order-independent).
 // ---------------------------------------------------------------------------
+template <bool Q8>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const float* __restrict__ dc, const float* __restrict__ y, const float* __restrict__ w,
     const int32_t* __restrict__ assign_row, int64_t T, int L, int k, int sr, uint32_t key,
-    uint16_t* __restrict__ dy_b, float* __restrict__ dw) {
+    uint16_t* __restrict__ dy_b, float* __restrict__ dw, uint8_t* __restrict__ dy8,
+    const float* __restrict__ grad_scale, uint32_t key8, uint32_t* __restrict__ grad_amax) {
   const int64_t t = blockIdx.x;
+  const float s5 = Q8 ? E5M2_OVER_E4M3 * grad_scale[0] : 1.f;
+  float amax = 0.f;
   __shared__ int rows[16];
   __shared__ float ws[16];
   __shared__ float red[16][4];
@@ -206,10 +239,25 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
       q.z = round_grad(wj * g.z, sr, key, o + 2);
       q.w = round_grad(wj * g.w, sr, key, o + 3);
       *(ushort4*)(dy_b + r * L + l) = q;
+      if constexpr (Q8) {
+        const float4 dv = make_float4(wj * g.x, wj * g.y, wj * g.z, wj * g.w);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(dv.x), fabsf(dv.y)), fmaxf(fabsf(dv.z), fabsf(dv.w))));
+        uchar4 q8;
+        q8.x = f32_to_e5m2(dv.x * s5, sr, key8, o);
+        q8.y = f32_to_e5m2(dv.y * s5, sr, key8, o + 1);
+        q8.z = f32_to_e5m2(dv.z * s5, sr, key8, o + 2);
+        q8.w = f32_to_e5m2(dv.w * s5, sr, key8, o + 3);
+        *(uchar4*)(dy8 + r * L + l) = q8;
+      }
     }
   }
   // fixed-order reduction: wave tree, then the 4 wave sums in order
   const int lane = tid & 63, wave = tid >> 6;
+  if constexpr (Q8) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    if (lane == 0 && amax > 0.f) atomicMax(grad_amax, __float_as_uint(amax));
+  }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     if (j >= k) break;
@@ -225,8 +273,20 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
 hipError_t launch_combine_bwd(const float* dc, const float* y_rows, const float* topk_w,
                               const int32_t* assign_row, int64_t T, int L, int k, int sr,
                               uint32_t key, uint16_t* dy_b, float* dw, hipStream_t s) {
-  hipLaunchKernelGGL(combine_bwd_kernel, dim3((unsigned)T), dim3(256), 0, s, dc, y_rows, topk_w,
-                     assign_row, T, L, k, sr, key, dy_b, dw);
+  hipLaunchKernelGGL(combine_bwd_kernel<false>, dim3((unsigned)T), dim3(256), 0, s, dc, y_rows,
+                     topk_w, assign_row, T, L, k, sr, key, dy_b, dw, (uint8_t*)nullptr,
+                     (const float*)nullptr, 0u, (uint32_t*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd_q8(const float* dc, const float* y_rows, const float* topk_w,
+                                 const int32_t* assign_row, int64_t T, int L, int k, int sr,
+                                 uint32_t key, uint16_t* dy_b, float* dw, uint8_t* dy8,
+                                 const float* grad_scale, uint32_t key8, uint32_t* grad_amax,
+                                 hipStream_t s) {
+  hipLaunchKernelGGL(combine_bwd_kernel<true>, dim3((unsigned)T), dim3(256), 0, s, dc, y_rows,
+                     topk_w, assign_row, T, L, k, sr, key, dy_b, dw, dy8, grad_scale, key8,
+                     grad_amax);
   return hipGetLastError();
 }
 
@@ -491,7 +551,7 @@ hipError_t launch_kgrouped_f32(const uint16_t* A, int64_t lda, const uint16_t* B
   a.c_expert_stride = c_expert_stride;
   a.m_tiles = (int)ceil_div(M, Cfg::bm);
   a.n_tiles = (int)ceil_div(N, Cfg::bn);
-  return launch_gemm<Cfg, false, false, EPI_F32, 1, false, true>(
+  return launch_gemm<Cfg, false, false, EPI_F32, 1, F8_NONE, true>(
       a, (int64_t)E * a.m_tiles * a.n_tiles, s);
 }
 

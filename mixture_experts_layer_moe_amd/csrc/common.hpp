@@ -65,6 +65,32 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
+// FP8 E5M2 (OCP: exponent bias 15, 2 fraction bits, subnormals spaced 2^-16
+// below 2^-14, largest finite 57344) of a gradient value v that is already
+// scaled.  The magnitude saturates at 57344 (the hardware conversion does
+// not).  Nearest (sr == 0): the hardware conversion, ties to even.
+// Stochastic: at or above 2^-14 the top 21 bits of the stream's hash of
+// element idx are added to the fp32 bit pattern of the magnitude and the low
+// 21 bits dropped (round up with probability equal to the discarded
+// fraction; the result is exactly an E5M2 value, so the conversion that
+// follows is exact); below 2^-14 to nearest.  The hash is the one of
+// f32_to_bf16_sr.
+__device__ __forceinline__ uint8_t f32_to_e5m2(float v, int sr, uint32_t key, uint64_t idx) {
+  constexpr float E5M2_MAX = 57344.0f;
+  float a = fminf(fabsf(v), E5M2_MAX);
+  if (sr && a >= 0x1p-14f) {
+    uint32_t h = lowbias32((uint32_t)idx ^ key);
+    h = lowbias32(h ^ (uint32_t)(idx >> 32));
+    a = __uint_as_float((__float_as_uint(a) + (h >> 11)) & 0xFFE00000u);
+  }
+  return (uint8_t)(__builtin_amdgcn_cvt_pk_bf8_f32(copysignf(a, v), 0.0f, 0, false) & 0xff);
+}
+
+// Largest finite E5M2 value over the largest E4M3 value: a gradient whose
+// scale s follows the E4M3 convention (s = 448 / amax) enters E5M2 scaled by
+// 128 s (exact: a power of two times s).
+constexpr float E5M2_OVER_E4M3 = 128.0f;
+
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Upper bound of sum_e ceil(M_e / BM) over any routing of `rows` rows to E

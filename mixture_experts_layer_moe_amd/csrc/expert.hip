@@ -191,7 +191,7 @@ hipError_t launch_round_tables(const int32_t* offsets, int E, int G, int C, int 
   return hipGetLastError();
 }
 
-template <int BM, bool GATHER, int EPI, bool F8 = false, int NSEG = 1>
+template <int BM, bool GATHER, int EPI, int F8 = F8_NONE, int NSEG = 1>
 static hipError_t grouped_gemm(GemmArgs a, int64_t rows, hipStream_t s) {
   using C = std::conditional_t<BM == 128, TileStream, TileBig>;
   static_assert(C::bm == BM, "tile height");
@@ -318,8 +318,109 @@ hipError_t launch_dzp(const uint16_t* dg_b, const uint16_t* du_b, const int32_t*
   a.b_expert_stride = (int64_t)L * F;
   a.C = dzp;
   a.ldc = L;
-  if (bm == 128) return grouped_gemm<128, false, EPI_F32, false, 2>(a, rows, s);
-  return grouped_gemm<256, false, EPI_F32, false, 2>(a, rows, s);
+  if (bm == 128) return grouped_gemm<128, false, EPI_F32, F8_NONE, 2>(a, rows, s);
+  return grouped_gemm<256, false, EPI_F32, F8_NONE, 2>(a, rows, s);
+}
+
+// Backward with FP8 data gradients: the gate/up recompute as above that also
+// writes dg and du as E5M2 codes (dg8, du8; scales 128 grad_scale[1], 128
+// grad_scale[2]; rounding as for the bf16 casts, stream keys key_dg8 and
+// key_du8) and records max |dg|, max |du| in grad_amax[1], grad_amax[2].
+hipError_t launch_gate_up_bwd_q8(const uint16_t* z, const int32_t* offsets,
+                                 const int32_t* row_token, const int32_t* tile_prefix,
+                                 const int32_t* tile_expert, int32_t* queue,
+                                 const uint16_t* w_gate, const uint16_t* w_up, const float* dh,
+                                 int64_t T, int64_t rows, int E, int L, int F, int bm, int sr,
+                                 uint32_t key_dg, uint32_t key_du, uint32_t key_dg8,
+                                 uint32_t key_du8, const float* grad_scale, uint32_t* grad_amax,
+                                 uint16_t* dg_b, uint16_t* du_b, uint16_t* h, uint8_t* dg8,
+                                 uint8_t* du8, hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = z; a.seg[0].lda = L; a.seg[0].B = w_gate; a.seg[0].B2 = w_up; a.seg[0].ldb = L;
+  a.seg[0].K = L;
+  a.nseg = 1;
+  a.N = F;
+  a.offsets = offsets;
+  a.tile_prefix = tile_prefix;
+  a.tile_expert = tile_expert;
+  a.E = E;
+  a.b_expert_stride = (int64_t)F * L;
+  a.row_token = row_token;
+  a.queue = queue;
+  a.M = (int)T;
+  a.C = dg_b;
+  a.C2 = du_b;
+  a.C3 = h;
+  a.C4 = dg8;
+  a.C5 = du8;
+  a.aux_g = dh;
+  a.sr = sr;
+  a.sr_key_c = key_dg;
+  a.sr_key_c2 = key_du;
+  a.sr_key_c4 = key_dg8;
+  a.sr_key_c5 = key_du8;
+  a.out_scale = grad_scale;
+  a.amax = grad_amax;
+  a.ldc = F;
+  if (bm == 128) return grouped_gemm<128, true, EPI_GU_BWD_Q8>(a, rows, s);
+  return grouped_gemm<256, true, EPI_GU_BWD_Q8>(a, rows, s);
+}
+
+// FP8 data gradient dh = (q_dy Q(W_d[e])) / (128 s_dy s_Wd[e]): dy8 [rows, L]
+// E5M2 codes, w_down_t8 = Q(W_d[e])^T [E, F, L] E4M3 (the transpose of the
+// forward's quantized weight), dy_scale the E4M3-convention scale s_dy.
+hipError_t launch_expert_dh_fp8(const uint8_t* dy8, const int32_t* offsets,
+                                const int32_t* tile_prefix, const int32_t* tile_expert,
+                                int32_t* queue, const uint8_t* w_down_t8, const float* dy_scale,
+                                const float* wd_scale, int64_t rows, int E, int L, int F, int bm,
+                                float* dh, hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = dy8; a.seg[0].lda = L; a.seg[0].B = w_down_t8; a.seg[0].ldb = L; a.seg[0].K = L;
+  a.nseg = 1;
+  a.N = F;
+  a.offsets = offsets;
+  a.tile_prefix = tile_prefix;
+  a.tile_expert = tile_expert;
+  a.queue = queue;
+  a.E = E;
+  a.b_expert_stride = (int64_t)F * L;
+  a.C = dh;
+  a.ldc = F;
+  a.a_scale = dy_scale;
+  a.b_scale = wd_scale;
+  if (bm == 128) return grouped_gemm<128, false, EPI_F32, F8_E5M2_A>(a, rows, s);
+  return grouped_gemm<256, false, EPI_F32, F8_E5M2_A>(a, rows, s);
+}
+
+// FP8 rows' latent gradient dzp = (q_dg Q(W_g[e])) / (128 s_dg s_Wg[e]) +
+// (q_du Q(W_u[e])) / (128 s_du s_Wu[e]), one accumulation over two K
+// segments with separate dequantization (w_gate_t8, w_up_t8 = Q(W_g[e])^T,
+// Q(W_u[e])^T [E, L, F] E4M3).
+hipError_t launch_dzp_fp8(const uint8_t* dg8, const uint8_t* du8, const int32_t* offsets,
+                          const int32_t* tile_prefix, const int32_t* tile_expert, int32_t* queue,
+                          const uint8_t* w_gate_t8, const uint8_t* w_up_t8,
+                          const float* dg_scale, const float* du_scale, const float* wg_scale,
+                          const float* wu_scale, int64_t rows, int E, int L, int F, int bm,
+                          float* dzp, hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = dg8; a.seg[0].lda = F; a.seg[0].B = w_gate_t8; a.seg[0].ldb = F; a.seg[0].K = F;
+  a.seg[1].A = du8; a.seg[1].lda = F; a.seg[1].B = w_up_t8; a.seg[1].ldb = F; a.seg[1].K = F;
+  a.nseg = 2;
+  a.N = L;
+  a.offsets = offsets;
+  a.tile_prefix = tile_prefix;
+  a.tile_expert = tile_expert;
+  a.queue = queue;
+  a.E = E;
+  a.b_expert_stride = (int64_t)L * F;
+  a.C = dzp;
+  a.ldc = L;
+  a.a_scale = dg_scale;
+  a.b_scale = wg_scale;
+  a.a2_scale = du_scale;
+  a.b2_scale = wu_scale;
+  if (bm == 128) return grouped_gemm<128, false, EPI_F32, F8_E5M2_A, 2>(a, rows, s);
+  return grouped_gemm<256, false, EPI_F32, F8_E5M2_A, 2>(a, rows, s);
 }
 
 // FP8 experts: z8 and the weights are E4M3 with scales (z: one, weights: one
@@ -351,8 +452,8 @@ hipError_t launch_gate_up_fp8(const uint8_t* z8, const int32_t* offsets, const i
   a.b2_scale = wu_scale;
   a.out_scale = h_scale;
   a.amax = amax;
-  if (bm == 128) return grouped_gemm<128, true, EPI_SWIGLU_Q8, true>(a, rows, s);
-  return grouped_gemm<256, true, EPI_SWIGLU_Q8, true>(a, rows, s);
+  if (bm == 128) return grouped_gemm<128, true, EPI_SWIGLU_Q8, F8_E4M3>(a, rows, s);
+  return grouped_gemm<256, true, EPI_SWIGLU_Q8, F8_E4M3>(a, rows, s);
 }
 
 hipError_t launch_expert_down_fp8(const uint8_t* H8, const int32_t* offsets,
@@ -374,8 +475,8 @@ hipError_t launch_expert_down_fp8(const uint8_t* H8, const int32_t* offsets,
   a.ldc = L;
   a.a_scale = h_scale;
   a.b_scale = wd_scale;
-  if (bm == 128) return grouped_gemm<128, false, EPI_F32, true>(a, rows, s);
-  return grouped_gemm<256, false, EPI_F32, true>(a, rows, s);
+  if (bm == 128) return grouped_gemm<128, false, EPI_F32, F8_E4M3>(a, rows, s);
+  return grouped_gemm<256, false, EPI_F32, F8_E4M3>(a, rows, s);
 }
 
 // A round of the multi-round schedule: gate/up over the round's rows of every

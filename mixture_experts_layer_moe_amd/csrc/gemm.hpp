@@ -62,6 +62,15 @@
 //     running maximum per wave, one integer atomic max per wave at the end
 //     (the bit patterns of non-negative floats order like unsigned integers,
 //     so the result does not depend on the order).
+//   * F8 = F8_E5M2_A (the backward's data-gradient GEMMs): A is an E5M2
+//     gradient (scale 128 s_A), B an E4M3 weight; the MFMA takes A's format
+//     as its source-0 format code.  With two K segments each segment has its
+//     own scales: at the second segment's first stage the accumulators are
+//     multiplied by dq_1 / dq_2 and the epilogue by dq_2 (so each segment's
+//     products end up divided by their own scales).
+//   * EPI_GU_BWD / EPI_GU_BWD_Q8: the gate/up GEMM of the backward
+//     (recomputation) with the SwiGLU backward in the epilogue; the _Q8
+//     variant also writes dg and du as E5M2 codes and records their maxima.
 #pragma once
 
 #include <type_traits>
@@ -74,13 +83,18 @@ constexpr uint32_t RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data format
 constexpr int DENSE_GM = 4;                     // M panels per tile group (dense GEMMs)
 
 enum GemmEpi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_BIAS = 2, EPI_SWIGLU = 3, EPI_Q8 = 4,
-               EPI_SWIGLU_Q8 = 5, EPI_GU_BWD = 6 };
+               EPI_SWIGLU_Q8 = 5, EPI_GU_BWD = 6, EPI_GU_BWD_Q8 = 7 };
+
+// FP8 operand formats of a GEMM (template parameter F8): none (bf16), both
+// operands E4M3, or the activation operand (A) E5M2 and the weights E4M3
+enum GemmF8 { F8_NONE = 0, F8_E4M3 = 1, F8_E5M2_A = 2 };
 
 // B tiles that interleave the gate and up matrices (a lane holds g and u of
 // the same element)
 constexpr bool epi_swiglu(int epi) {
-  return epi == EPI_SWIGLU || epi == EPI_SWIGLU_Q8 || epi == EPI_GU_BWD;
+  return epi == EPI_SWIGLU || epi == EPI_SWIGLU_Q8 || epi == EPI_GU_BWD || epi == EPI_GU_BWD_Q8;
 }
+constexpr bool epi_gu_bwd(int epi) { return epi == EPI_GU_BWD || epi == EPI_GU_BWD_Q8; }
 constexpr float E4M3_MAX = 448.0f;
 
 struct GemmSeg {
@@ -115,6 +129,10 @@ struct GemmArgs {
   const float* b2_scale;
   const float* out_scale;
   uint32_t* amax;
+  // FP8 with two K segments: the A scale of the second segment (its B scale
+  // is b2_scale).  The products of each segment are divided by their own
+  // scales.
+  const float* a2_scale;
   // grouped, multi-round schedule: expert e's rows this round are
   // [offsets[e], seg_end[e]) (seg_end null: offsets[e + 1]); with h_base,
   // row r of expert e sits at row h_base[e] + (r - offsets[e]) of the round's
@@ -131,10 +149,16 @@ struct GemmArgs {
   // KG (K-grouped tiles, weight gradients): tile -> (expert, M tile, N tile)
   // with expert e's K range [kpre[e], kpre[e + 1]) of A and B (multiples of
   // the stage width), C of expert e at C + e * c_expert_stride.
+  // EPI_GU_BWD_Q8 also writes dg and du as E5M2 codes -> C4, C5, scaled by
+  // 128 out_scale[1] and 128 out_scale[2], rounded to nearest (sr == 0) or
+  // stochastically with the keys sr_key_c4, sr_key_c5 (same element index),
+  // and records max |dg|, max |du| (fp32, before scaling) in amax[1], amax[2].
   void* C2;
   void* C3;
+  void* C4;
+  void* C5;
   const float* aux_g;
-  uint32_t sr_key_c, sr_key_c2;
+  uint32_t sr_key_c, sr_key_c2, sr_key_c4, sr_key_c5;
   int sr;
   const int32_t* kpre;
   int64_t c_expert_stride;
@@ -198,12 +222,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool GROUPED, bool GATHER, int EPI,
-          bool BNT, int NSEG, bool F8, bool KG>
+          bool BNT, int NSEG, int F8, bool KG>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   constexpr int ES = F8 ? 1 : 2;                   // operand bytes per element
   constexpr int KE = BK * 2 / ES;                  // K values per stage (BK * 2 bytes per row)
   constexpr bool SWG = epi_swiglu(EPI);
   constexpr bool Q8 = EPI == EPI_Q8 || EPI == EPI_SWIGLU_Q8;
+  constexpr bool GBQ8 = EPI == EPI_GU_BWD_Q8;
+  // FP8 with two K segments: separate dequantization of each segment
+  constexpr bool SEG_DQ = F8 != F8_NONE && NSEG == 2 && !epi_swiglu(EPI);
+  // the A operand's scale multiplier: E5M2 gradients take 128 s
+  constexpr float A_SMUL = F8 == F8_E5M2_A ? E5M2_OVER_E4M3 : 1.0f;
+  static_assert(!GBQ8 || F8 == F8_NONE, "the gate/up recompute runs on bf16 operands");
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -263,6 +293,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   });
   int nk = ktotal / KE;      // K-grouped tiles: set per tile
   float amax_run = 0.f;     // Q8: largest |bf16 output| this lane wrote
+  float amax_dg = 0.f, amax_du = 0.f;   // GBQ8: largest |dg|, |du| of this lane
 
   // The queue's tile index is broadcast through the last 16-byte slot of the
   // LDS array (one LDS object only, so the compiler's LDS-DMA alias tracking
@@ -311,9 +342,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       a_r0 = a.h_side == 2 ? hr0 : r0;
       c_r0 = a.h_side == 1 ? hr0 : r0;
       b_off = (int64_t)e * a.b_expert_stride * ES;
-      if constexpr (F8) {
-        dq_b = 1.0f / (a.a_scale[0] * a.b_scale[e]);
-        if constexpr (SWG) dq_b2 = 1.0f / (a.a_scale[0] * a.b2_scale[e]);
+      if constexpr (F8 != F8_NONE) {
+        dq_b = 1.0f / (A_SMUL * a.a_scale[0] * a.b_scale[e]);
+        if constexpr (SWG) dq_b2 = 1.0f / (A_SMUL * a.a_scale[0] * a.b2_scale[e]);
+        if constexpr (SEG_DQ) dq_b2 = 1.0f / (A_SMUL * a.a2_scale[0] * a.b2_scale[e]);
       }
     } else if constexpr (KG) {
       // expert, then N tile, then M tile (M fastest)
@@ -338,9 +370,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       r0 = (g * DENSE_GM + (r - n_tile * gm)) * BM;
       mrows = min(BM, a.M - r0);
       a_r0 = c_r0 = r0;
-      if constexpr (F8) {
-        dq_b = 1.0f / (a.a_scale[0] * a.b_scale[0]);
-        if constexpr (SWG) dq_b2 = 1.0f / (a.a_scale[0] * a.b2_scale[0]);
+      if constexpr (F8 != F8_NONE) {
+        dq_b = 1.0f / (A_SMUL * a.a_scale[0] * a.b_scale[0]);
+        if constexpr (SWG) dq_b2 = 1.0f / (A_SMUL * a.a_scale[0] * a.b2_scale[0]);
+        if constexpr (SEG_DQ) dq_b2 = 1.0f / (A_SMUL * a.a2_scale[0] * a.b2_scale[0]);
       }
     }
     const int n0 = SWG ? n_tile * (BN / 2) : n_tile * BN;   // first output col
@@ -476,6 +509,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
           wait_vmcnt<0>();
         }
         lds_barrier();     // every wave's DMA for stage kt landed; stage kt-1 fully consumed
+        if constexpr (SEG_DQ) {
+          // the first segment's products are complete: bring them to the
+          // second segment's scale, so that the final dq_b2 divides each
+          // segment by its own scales
+          if (kt * KE == kseg[0]) {
+            const float ratio = dq_b / dq_b2;
+#pragma unroll
+            for (int i = 0; i < NACT; ++i)
+#pragma unroll
+              for (int j = 0; j < TN; ++j) acc[i][j] *= ratio;
+          }
+        }
         const bool prefetch = kt + NSTAGE - 1 < nk;
         const uint4* sa = smem + (kt % NSTAGE) * STAGE;
         const uint4* sb = sa + BM * KCH;
@@ -483,7 +528,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
           constexpr int kk = decltype(kk_c)::value;
           if constexpr (kk < DPART)
             if (prefetch) issue(kt + NSTAGE - 1, kk_c);
-          if constexpr (NACT > 0 && !F8) {
+          if constexpr (NACT > 0 && F8 == F8_NONE) {
             // rows 32 (i WM + wrow) + fr all have the same swizzle as row fr
             const int ch = (kk * 2 + fq) ^ swz<KCH>(fr);
             bf16x8 bfr[TN], afr[NACT];
@@ -523,8 +568,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
             for (int i = 0; i < NACT; ++i)
 #pragma unroll
               for (int j = 0; j < TN; ++j)
+                // A format 0 (E4M3) or 1 (E5M2), B format 0 (E4M3); block scales 2^0
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    afr[i], bfr[j], acc[i][j], 0, 0, 0, 127, 0, 127);   // E4M3 x E4M3, scale 2^0
+                    afr[i], bfr[j], acc[i][j], F8 == F8_E5M2_A ? 1 : 0, 0, 0, 127, 0, 127);
           }
         });
       }
@@ -546,6 +592,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
     // ---- epilogue: in a 32x32 block, lane l holds column l & 31 and, in
     // register r, row 8 * (r / 4) + 4 * (l / 32) + r % 4 ----
     const float oscale = Q8 ? a.out_scale[0] : 1.f;
+    // GBQ8: the E5M2 scales of dg and du (128 s, exact)
+    const float q5_dg = GBQ8 ? E5M2_OVER_E4M3 * a.out_scale[1] : 1.f;
+    const float q5_du = GBQ8 ? E5M2_OVER_E4M3 * a.out_scale[2] : 1.f;
+    // FP8 with two K segments: the accumulators hold the second segment's scale
+    const float dq_out = SEG_DQ ? dq_b2 : dq_b;
     const int64_t c_off = KG ? (int64_t)kg_e * a.c_expert_stride : 0;   // KG: the expert's block
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -561,7 +612,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
             if (cl < nrows) {
               const float g = acc[i][j][r] * dq_b, u = acc[i][j + 1][r] * dq_b2;
               const uint16_t hb = f32_to_bf16_rne(g / (1.0f + __expf(-g)) * u);
-              if constexpr (EPI == EPI_GU_BWD) {
+              if constexpr (epi_gu_bwd(EPI)) {
                 const int64_t o = row * a.ldc + n0 + cl;
                 const float dh = a.aux_g[o];
                 const float sg = 1.0f / (1.0f + __expf(-g));
@@ -575,6 +626,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
                   ((uint16_t*)a.C2)[o] = f32_to_bf16_rne(du);
                 }
                 ((uint16_t*)a.C3)[o] = hb;
+                if constexpr (GBQ8) {
+                  amax_dg = fmaxf(amax_dg, fabsf(dg));
+                  amax_du = fmaxf(amax_du, fabsf(du));
+                  ((uint8_t*)a.C4)[o] = f32_to_e5m2(dg * q5_dg, a.sr, a.sr_key_c4, (uint64_t)o);
+                  ((uint8_t*)a.C5)[o] = f32_to_e5m2(du * q5_du, a.sr, a.sr_key_c5, (uint64_t)o);
+                }
               } else if constexpr (EPI == EPI_SWIGLU_Q8) {
                 const float hv = bf16_to_f32(hb);
                 amax_run = fmaxf(amax_run, fabsf(hv));
@@ -590,7 +647,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
             const int cl = wn0 + j * 32 + fr;
             if (cl >= nrows) continue;
             const int col = n0 + cl;
-            const float val = acc[i][j][r] * dq_b;
+            const float val = acc[i][j][r] * dq_out;
             if constexpr (EPI == EPI_BF16) {
               ((uint16_t*)a.C)[row * a.ldc + col] = f32_to_bf16_rne(val);
             } else if constexpr (EPI == EPI_Q8) {
@@ -613,6 +670,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) amax_run = fmaxf(amax_run, __shfl_xor(amax_run, o));
     if (lane == 0 && amax_run > 0.f) atomicMax(a.amax, __float_as_uint(amax_run));
+  }
+  if constexpr (GBQ8) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      amax_dg = fmaxf(amax_dg, __shfl_xor(amax_dg, o));
+      amax_du = fmaxf(amax_du, __shfl_xor(amax_du, o));
+    }
+    if (lane == 0 && amax_dg > 0.f) atomicMax(a.amax + 1, __float_as_uint(amax_dg));
+    if (lane == 0 && amax_du > 0.f) atomicMax(a.amax + 2, __float_as_uint(amax_du));
   }
 }
 
@@ -646,7 +712,7 @@ using TileBig = TileCfg<256, 256, 64, 2, 4, 2, false>;
 using TileMid = TileCfg<128, 256, 64, 2, 4, 3, false>;
 using TileRouter = TileCfg<64, 128, 64, 2, 2, 4, false>;
 
-template <class C, bool GROUPED, bool GATHER, int EPI, int NSEG = 1, bool F8 = false,
+template <class C, bool GROUPED, bool GATHER, int EPI, int NSEG = 1, int F8 = F8_NONE,
           bool KG = false>
 hipError_t launch_gemm(const GemmArgs& a, int64_t tiles_upper_bound, hipStream_t s) {
   if (tiles_upper_bound <= 0) return hipSuccess;

@@ -99,7 +99,36 @@ hipError_t launch_dzp(const uint16_t* dg_b, const uint16_t* du_b, const int32_t*
                       const uint16_t* w_gate_t, const uint16_t* w_up_t, int64_t rows, int E,
                       int L, int F, int bm, float* dzp, hipStream_t s);
 
+// backward with FP8 data gradients (expert.hip)
+hipError_t launch_gate_up_bwd_q8(const uint16_t* z, const int32_t* offsets,
+                                 const int32_t* row_token, const int32_t* tile_prefix,
+                                 const int32_t* tile_expert, int32_t* queue,
+                                 const uint16_t* w_gate, const uint16_t* w_up, const float* dh,
+                                 int64_t T, int64_t rows, int E, int L, int F, int bm, int sr,
+                                 uint32_t key_dg, uint32_t key_du, uint32_t key_dg8,
+                                 uint32_t key_du8, const float* grad_scale, uint32_t* grad_amax,
+                                 uint16_t* dg_b, uint16_t* du_b, uint16_t* h, uint8_t* dg8,
+                                 uint8_t* du8, hipStream_t s);
+hipError_t launch_expert_dh_fp8(const uint8_t* dy8, const int32_t* offsets,
+                                const int32_t* tile_prefix, const int32_t* tile_expert,
+                                int32_t* queue, const uint8_t* w_down_t8, const float* dy_scale,
+                                const float* wd_scale, int64_t rows, int E, int L, int F, int bm,
+                                float* dh, hipStream_t s);
+hipError_t launch_dzp_fp8(const uint8_t* dg8, const uint8_t* du8, const int32_t* offsets,
+                          const int32_t* tile_prefix, const int32_t* tile_expert, int32_t* queue,
+                          const uint8_t* w_gate_t8, const uint8_t* w_up_t8,
+                          const float* dg_scale, const float* du_scale, const float* wg_scale,
+                          const float* wu_scale, int64_t rows, int E, int L, int F, int bm,
+                          float* dzp, hipStream_t s);
+
 // backward.hip
+hipError_t launch_cvt_e5m2(const float* src, int64_t n, const float* scale, int sr, uint32_t key,
+                           uint8_t* dst, hipStream_t s);
+hipError_t launch_combine_bwd_q8(const float* dc, const float* y_rows, const float* topk_w,
+                                 const int32_t* assign_row, int64_t T, int L, int k, int sr,
+                                 uint32_t key, uint16_t* dy_b, float* dw, uint8_t* dy8,
+                                 const float* grad_scale, uint32_t key8, uint32_t* grad_amax,
+                                 hipStream_t s);
 hipError_t launch_cvt_grad(const float* src, int64_t n, int sr, uint32_t key, uint16_t* dst,
                            hipStream_t s);
 hipError_t launch_kpad_prefix(const int32_t* offsets, int E, int32_t* kpre, hipStream_t s);

@@ -121,10 +121,11 @@ int64_t max_rounds(int64_t T, int E, int k, int G, int C) {
 // activations, the padded K layout of the weight-gradient GEMMs
 struct BwdWs {
   size_t go, goT, z, cb, cbT, dc, dyb, dtw, dh, h, dgb, dub, dzp, dzb, dzbT, xT, kpre, dybT, hT,
-      dgbT, dubT, zpT, dl, dbp, dwp, pre_a, pre_b, exp_a, exp_b, queues, total;
+      dgbT, dubT, zpT, dl, dbp, dwp, pre_a, pre_b, exp_a, exp_b, queues, dy8, dg8, du8, total;
   int64_t Tp, Rp;
 };
-BwdWs bwd_ws(int64_t T, int d, int L, int E, int k, int F) {
+// fp8: the E5M2 codes of dy, dg and du as well (FP8 data gradients)
+BwdWs bwd_ws(int64_t T, int d, int L, int E, int k, int F, bool fp8 = false) {
   BwdWs w;
   const int64_t R = T * k;
   w.Tp = ceil_div(T, 64) * 64;
@@ -162,6 +163,9 @@ BwdWs bwd_ws(int64_t T, int d, int L, int E, int k, int F) {
   w.exp_a = take(mt * 4);
   w.exp_b = take(mt * 4);
   w.queues = take(24 * 4);
+  w.dy8 = fp8 ? take((size_t)R * L) : 0;
+  w.dg8 = fp8 ? take((size_t)R * F) : 0;
+  w.du8 = fp8 ? take((size_t)R * F) : 0;
   w.total = o;
   return w;
 }
@@ -199,6 +203,8 @@ size_t moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t L, int32_t E, i
     case MOE_OP_LATENT_FFN_FP8: return (L > 0 && F > 0) ? ffn8_ws(T, L, E, k, F).total : 0;
     case MOE_OP_BACKWARD:
       return (d > 0 && L > 0 && F > 0) ? bwd_ws(T, d, L, E, k, F).total : 0;
+    case MOE_OP_BACKWARD_FP8:
+      return (d > 0 && L > 0 && F > 0) ? bwd_ws(T, d, L, E, k, F, true).total : 0;
     default: return 0;
   }
 }
@@ -578,17 +584,30 @@ int moe_backward_prepare(const uint16_t* w_lat_down, const uint16_t* w_gate,
   return st;
 }
 
-int moe_backward(const uint16_t* x, const float* w_router, const float* router_logits,
-                 int32_t bias_mode, const int32_t* topk_idx, const float* topk_w,
-                 const int32_t* expert_offsets, const int32_t* row_token,
-                 const int32_t* assign_row, const float* y_rows, const uint16_t* w_lat_down,
-                 const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_lat_down_t,
-                 const uint16_t* w_gate_t, const uint16_t* w_up_t, const uint16_t* w_down_t,
-                 const uint16_t* w_lat_up_t, const float* g_out, int64_t T, int32_t d,
-                 int32_t L, int32_t E, int32_t k, int32_t F, int32_t rounding, uint32_t seed,
-                 float* dx, float* dw_router, float* db_router, float* dw_lat_down,
-                 float* dw_gate, float* dw_up, float* dw_down, float* dw_lat_up, float* dtopk_w,
-                 void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// FP8 data gradients of the backward: E4M3 transposed expert weights with
+// their scales, the gradients' scales, and the maxima out
+struct BwdFp8 {
+  const uint8_t *w_gate_t8, *w_up_t8, *w_down_t8;
+  const float* w_scale;      // [3E]: W_g, W_u, W_d
+  const float* grad_scale;   // [3]: dy, dg, du
+  float* grad_amax;          // [3]
+};
+
+int backward_impl(const uint16_t* x, const float* w_router, const float* router_logits,
+                  int32_t bias_mode, const int32_t* topk_idx, const float* topk_w,
+                  const int32_t* expert_offsets, const int32_t* row_token,
+                  const int32_t* assign_row, const float* y_rows, const uint16_t* w_lat_down,
+                  const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_lat_down_t,
+                  const uint16_t* w_gate_t, const uint16_t* w_up_t, const uint16_t* w_down_t,
+                  const uint16_t* w_lat_up_t, const float* g_out, int64_t T, int32_t d,
+                  int32_t L, int32_t E, int32_t k, int32_t F, int32_t rounding, uint32_t seed,
+                  float* dx, float* dw_router, float* db_router, float* dw_lat_down,
+                  float* dw_gate, float* dw_up, float* dw_down, float* dw_lat_up, float* dtopk_w,
+                  void* ws, size_t ws_bytes, void* stream, const BwdFp8* f8) {
   if (T < 0 || E <= 0 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
   if (bias_mode != MOE_BIAS_LOGITS && bias_mode != MOE_BIAS_SELECTION) return MOE_ERR_INVALID_ARG;
   if (rounding != MOE_ROUND_NEAREST && rounding != MOE_ROUND_STOCHASTIC)
@@ -597,18 +616,25 @@ int moe_backward(const uint16_t* x, const float* w_router, const float* router_l
       T * (int64_t)k >= (int64_t(1) << 31) || (int64_t)T * L * 2 >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
+  if (f8 && (L % 128 != 0 || F % 128 != 0)) return MOE_ERR_UNSUPPORTED;
+  // the expert data-gradient GEMMs read the bf16 transposes, or (f8) the
+  // E4M3 ones
+  const void* wg_t = f8 ? (const void*)f8->w_gate_t8 : (const void*)w_gate_t;
+  const void* wu_t = f8 ? (const void*)f8->w_up_t8 : (const void*)w_up_t;
+  const void* wd_t = f8 ? (const void*)f8->w_down_t8 : (const void*)w_down_t;
   const void* req[] = {x, w_router, router_logits, topk_idx, topk_w, expert_offsets, row_token,
-                       assign_row, y_rows, w_lat_down, w_gate, w_up, w_lat_down_t, w_gate_t,
-                       w_up_t, w_down_t, w_lat_up_t, g_out, dx, dw_router, dw_lat_down,
+                       assign_row, y_rows, w_lat_down, w_gate, w_up, w_lat_down_t, wg_t,
+                       wu_t, wd_t, w_lat_up_t, g_out, dx, dw_router, dw_lat_down,
                        dw_gate, dw_up, dw_down, dw_lat_up, ws};
   for (const void* p : req)
     if (!p) return MOE_ERR_INVALID_ARG;
+  if (f8 && (!f8->w_scale || !f8->grad_scale || !f8->grad_amax)) return MOE_ERR_INVALID_ARG;
   const void* al[] = {x, w_router, router_logits, y_rows, w_lat_down, w_gate, w_up,
-                      w_lat_down_t, w_gate_t, w_up_t, w_down_t, w_lat_up_t, g_out, dx,
+                      w_lat_down_t, wg_t, wu_t, wd_t, w_lat_up_t, g_out, dx,
                       dw_router, dw_lat_down, dw_gate, dw_up, dw_down, dw_lat_up, ws};
   for (const void* p : al)
     if (!aligned16(p)) return MOE_ERR_UNSUPPORTED;
-  const BwdWs w = bwd_ws(T, d, L, E, k, F);
+  const BwdWs w = bwd_ws(T, d, L, E, k, F, f8 != nullptr);
   // the weight-gradient GEMMs read 256-row tiles of the transposed operands
   // (row length Tp or Rp) through 32-bit buffer offsets
   if ((int64_t)256 * 2 * (w.Tp > w.Rp ? w.Tp : w.Rp) >= (int64_t(1) << 31))
@@ -638,10 +664,19 @@ int moe_backward(const uint16_t* x, const float* w_router, const float* router_l
                                               s));
   }
   if (st) return st;
+  uint32_t* gamax = f8 ? (uint32_t*)f8->grad_amax : nullptr;   // float bits, >= 0
   {
     EventScope ev(K_BWD_COMBINE, s);
-    st = hip_status(launch_combine_bwd(F32(w.dc), y_rows, topk_w, assign_row, T, L, k, sr,
-                                       sr_stream_key(seed, 2), B16(w.dyb), dtw, s));
+    if (f8) {
+      st = hip_status(launch_zero_u32(gamax, 3, s));
+      if (!st) st = hip_status(launch_combine_bwd_q8(
+          F32(w.dc), y_rows, topk_w, assign_row, T, L, k, sr, sr_stream_key(seed, 2), B16(w.dyb),
+          dtw, (uint8_t*)(base + w.dy8), f8->grad_scale,
+          sr_stream_key(seed, 6), gamax, s));
+    } else {
+      st = hip_status(launch_combine_bwd(F32(w.dc), y_rows, topk_w, assign_row, T, L, k, sr,
+                                         sr_stream_key(seed, 2), B16(w.dyb), dtw, s));
+    }
   }
   if (st) return st;
   {
@@ -654,16 +689,37 @@ int moe_backward(const uint16_t* x, const float* w_router, const float* router_l
                                                 I32(w.pre_a), I32(w.pre_b), I32(w.exp_a),
                                                 I32(w.exp_b), I32(w.queues), s));
     if (!st) st = hip_status(launch_zero_u32((uint32_t*)I32(w.queues) + 16, 8, s));
-    if (!st) st = hip_status(launch_expert_dh(B16(w.dyb), expert_offsets, I32(w.pre_b),
-                                              I32(w.exp_b), I32(w.queues), w_down_t, R, E, L, F,
-                                              plan.bm_down, F32(w.dh), s));
-    if (!st) st = hip_status(launch_gate_up_bwd(
-        B16(w.z), expert_offsets, row_token, I32(w.pre_a), I32(w.exp_a), I32(w.queues) + 8,
-        w_gate, w_up, F32(w.dh), T, R, E, L, F, plan.bm_gate_up, sr, sr_stream_key(seed, 3),
-        sr_stream_key(seed, 4), B16(w.dgb), B16(w.dub), B16(w.h), s));
-    if (!st) st = hip_status(launch_dzp(B16(w.dgb), B16(w.dub), expert_offsets, I32(w.pre_b),
-                                        I32(w.exp_b), I32(w.queues) + 16, w_gate_t, w_up_t, R, E,
-                                        L, F, plan.bm_down, F32(w.dzp), s));
+    if (f8) {
+      uint8_t* dy8 = (uint8_t*)(base + w.dy8);
+      uint8_t* dg8 = (uint8_t*)(base + w.dg8);
+      uint8_t* du8 = (uint8_t*)(base + w.du8);
+      const float* gs = f8->grad_scale;
+      const float* wsc = f8->w_scale;
+      if (!st) st = hip_status(launch_expert_dh_fp8(dy8, expert_offsets, I32(w.pre_b),
+                                                    I32(w.exp_b), I32(w.queues), f8->w_down_t8,
+                                                    gs, wsc + 2 * E, R, E, L, F, plan.bm_down,
+                                                    F32(w.dh), s));
+      if (!st) st = hip_status(launch_gate_up_bwd_q8(
+          B16(w.z), expert_offsets, row_token, I32(w.pre_a), I32(w.exp_a), I32(w.queues) + 8,
+          w_gate, w_up, F32(w.dh), T, R, E, L, F, plan.bm_gate_up, sr, sr_stream_key(seed, 3),
+          sr_stream_key(seed, 4), sr_stream_key(seed, 7), sr_stream_key(seed, 8), gs, gamax,
+          B16(w.dgb), B16(w.dub), B16(w.h), dg8, du8, s));
+      if (!st) st = hip_status(launch_dzp_fp8(dg8, du8, expert_offsets, I32(w.pre_b),
+                                              I32(w.exp_b), I32(w.queues) + 16, f8->w_gate_t8,
+                                              f8->w_up_t8, gs + 1, gs + 2, wsc, wsc + E, R, E, L,
+                                              F, plan.bm_down, F32(w.dzp), s));
+    } else {
+      if (!st) st = hip_status(launch_expert_dh(B16(w.dyb), expert_offsets, I32(w.pre_b),
+                                                I32(w.exp_b), I32(w.queues), w_down_t, R, E, L, F,
+                                                plan.bm_down, F32(w.dh), s));
+      if (!st) st = hip_status(launch_gate_up_bwd(
+          B16(w.z), expert_offsets, row_token, I32(w.pre_a), I32(w.exp_a), I32(w.queues) + 8,
+          w_gate, w_up, F32(w.dh), T, R, E, L, F, plan.bm_gate_up, sr, sr_stream_key(seed, 3),
+          sr_stream_key(seed, 4), B16(w.dgb), B16(w.dub), B16(w.h), s));
+      if (!st) st = hip_status(launch_dzp(B16(w.dgb), B16(w.dub), expert_offsets, I32(w.pre_b),
+                                          I32(w.exp_b), I32(w.queues) + 16, w_gate_t, w_up_t, R,
+                                          E, L, F, plan.bm_down, F32(w.dzp), s));
+    }
   }
   if (st) return st;
   {
@@ -714,6 +770,61 @@ int moe_backward(const uint16_t* x, const float* w_router, const float* router_l
       st = hip_status(launch_zero_u32((uint32_t*)db_router, E, s));
   }
   return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_backward(const uint16_t* x, const float* w_router, const float* router_logits,
+                 int32_t bias_mode, const int32_t* topk_idx, const float* topk_w,
+                 const int32_t* expert_offsets, const int32_t* row_token,
+                 const int32_t* assign_row, const float* y_rows, const uint16_t* w_lat_down,
+                 const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_lat_down_t,
+                 const uint16_t* w_gate_t, const uint16_t* w_up_t, const uint16_t* w_down_t,
+                 const uint16_t* w_lat_up_t, const float* g_out, int64_t T, int32_t d,
+                 int32_t L, int32_t E, int32_t k, int32_t F, int32_t rounding, uint32_t seed,
+                 float* dx, float* dw_router, float* db_router, float* dw_lat_down,
+                 float* dw_gate, float* dw_up, float* dw_down, float* dw_lat_up, float* dtopk_w,
+                 void* ws, size_t ws_bytes, void* stream) {
+  return backward_impl(x, w_router, router_logits, bias_mode, topk_idx, topk_w, expert_offsets,
+                       row_token, assign_row, y_rows, w_lat_down, w_gate, w_up, w_lat_down_t,
+                       w_gate_t, w_up_t, w_down_t, w_lat_up_t, g_out, T, d, L, E, k, F, rounding,
+                       seed, dx, dw_router, db_router, dw_lat_down, dw_gate, dw_up, dw_down,
+                       dw_lat_up, dtopk_w, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_backward_fp8(const uint16_t* x, const float* w_router, const float* router_logits,
+                     int32_t bias_mode, const int32_t* topk_idx, const float* topk_w,
+                     const int32_t* expert_offsets, const int32_t* row_token,
+                     const int32_t* assign_row, const float* y_rows, const uint16_t* w_lat_down,
+                     const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_lat_down_t,
+                     const uint8_t* w_gate_t8, const uint8_t* w_up_t8, const uint8_t* w_down_t8,
+                     const float* w_scale, const uint16_t* w_lat_up_t, const float* g_out,
+                     const float* grad_scale, int64_t T, int32_t d, int32_t L, int32_t E,
+                     int32_t k, int32_t F, int32_t rounding, uint32_t seed, float* dx,
+                     float* dw_router, float* db_router, float* dw_lat_down, float* dw_gate,
+                     float* dw_up, float* dw_down, float* dw_lat_up, float* dtopk_w,
+                     float* grad_amax, void* ws, size_t ws_bytes, void* stream) {
+  const BwdFp8 f8 = {w_gate_t8, w_up_t8, w_down_t8, w_scale, grad_scale, grad_amax};
+  return backward_impl(x, w_router, router_logits, bias_mode, topk_idx, topk_w, expert_offsets,
+                       row_token, assign_row, y_rows, w_lat_down, w_gate, w_up, w_lat_down_t,
+                       nullptr, nullptr, nullptr, w_lat_up_t, g_out, T, d, L, E, k, F, rounding,
+                       seed, dx, dw_router, db_router, dw_lat_down, dw_gate, dw_up, dw_down,
+                       dw_lat_up, dtopk_w, ws, ws_bytes, stream, &f8);
+}
+
+int moe_grad_cast_e5m2(const float* src, int64_t n, const float* scale, int32_t rounding,
+                       uint32_t seed, int32_t stream_id, uint8_t* dst, void* stream) {
+  if (n < 0 || (rounding != MOE_ROUND_NEAREST && rounding != MOE_ROUND_STOCHASTIC))
+    return MOE_ERR_INVALID_ARG;
+  if (n % 4 != 0) return MOE_ERR_UNSUPPORTED;
+  if (n == 0) return MOE_OK;
+  if (!src || !dst || !scale) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(src) || ((uintptr_t)dst & 3u)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_cvt_e5m2(src, n, scale, rounding == MOE_ROUND_STOCHASTIC,
+                                    sr_stream_key(seed, (uint32_t)stream_id), dst,
+                                    (hipStream_t)stream));
 }
 
 }  // extern "C"

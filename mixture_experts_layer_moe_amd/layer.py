@@ -211,7 +211,7 @@ class LatentMoEGrads:
     """fp32 gradients of every parameter and of x, the gate weights' gradient,
     and the backward's workspace."""
 
-    def __init__(self, T, d, L, E, k, F, device="cuda", bias=True):
+    def __init__(self, T, d, L, E, k, F, device="cuda", bias=True, fp8=False):
         dev = torch.device(device)
         f32 = torch.float32
         self.dx = torch.empty((T, d), dtype=f32, device=dev)
@@ -223,7 +223,8 @@ class LatentMoEGrads:
         self.dw_down = torch.empty((E, L, F), dtype=f32, device=dev)
         self.dw_lat_up = torch.empty((d, L), dtype=f32, device=dev)
         self.dtopk_w = torch.empty((T, k), dtype=f32, device=dev)
-        nb = _lib.moe_workspace_bytes(_lib.MOE_OP_BACKWARD, T, d, L, E, k, F, 0)
+        op = _lib.MOE_OP_BACKWARD_FP8 if fp8 else _lib.MOE_OP_BACKWARD
+        nb = _lib.moe_workspace_bytes(op, T, d, L, E, k, F, 0)
         self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
 
 
@@ -240,4 +241,73 @@ def backward(x, w: LatentMoEWeights, wt: LatentMoETransposed, buf: LatentMoEBuff
                       wt.w_lat_up_t, g_out, rounding, seed, grads.dx, grads.dw_router,
                       grads.db_router, grads.dw_lat_down, grads.dw_gate, grads.dw_up,
                       grads.dw_down, grads.dw_lat_up, grads.dtopk_w, grads.ws, stream=stream)
+    return grads
+
+
+# ---------------------------------------------------------------------------
+# backward pass with FP8 data gradients (E5M2 gradients x E4M3 weights)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class LatentMoEFp8Transposed:
+    """E4M3 transposes of the routed experts' weights for the FP8 data-gradient
+    GEMMs, quantized with the forward's per-expert scales w_scale."""
+    w_gate_t8: torch.Tensor   # [E, L, F] uint8
+    w_up_t8: torch.Tensor     # [E, L, F] uint8
+    w_down_t8: torch.Tensor   # [E, F, L] uint8
+    w_scale: torch.Tensor     # [3E] fp32: W_g, W_u, W_d
+
+
+def quantize_transposed(wt: LatentMoETransposed, w8: LatentMoEFp8Experts,
+                        stream=None) -> LatentMoEFp8Transposed:
+    """Quantize the bf16 transposes with the forward's scales (quantizing
+    commutes with transposing, so these are the forward's E4M3 weights,
+    transposed)."""
+    E = wt.w_gate_t.shape[0]
+    q = []
+    for i, t in enumerate((wt.w_gate_t, wt.w_up_t, wt.w_down_t)):
+        dst = torch.empty(t.shape, dtype=torch.uint8, device=t.device)
+        _lib.moe_fp8_quantize(t, E, w8.w_scale[i * E:(i + 1) * E], dst, stream=stream)
+        q.append(dst)
+    return LatentMoEFp8Transposed(q[0], q[1], q[2], w8.w_scale)
+
+
+class Fp8GradScaling:
+    """Delayed scaling state of the three FP8 gradient tensors (dy, dg, du):
+    an amax history of hist_len steps each, the scales for the next step
+    (E4M3 convention, 448 / max history; the E5M2 operand takes 128 times
+    that), and this step's maxima.  Scales start at 1."""
+
+    def __init__(self, hist_len=1024, device="cuda"):
+        dev = torch.device(device)
+        self.history = torch.zeros((3, hist_len), dtype=torch.float32, device=dev)
+        self.scale = torch.ones(3, dtype=torch.float32, device=dev)
+        self.amax = torch.zeros(3, dtype=torch.float32, device=dev)
+        self.step = 0
+
+    def update(self, stream=None):
+        _lib.moe_fp8_scale_update(self.history, self.amax, self.step % self.history.shape[1],
+                                  self.scale, stream=stream)
+        self.step += 1
+
+
+def backward_fp8(x, w: LatentMoEWeights, wt: LatentMoETransposed, wt8: LatentMoEFp8Transposed,
+                 buf: LatentMoEBuffers, g_out, grads: LatentMoEGrads, scaling: Fp8GradScaling,
+                 rounding=_lib.MOE_ROUND_STOCHASTIC, seed=0, bias_mode=_lib.MOE_BIAS_LOGITS,
+                 stream=None, update_scaling=True):
+    """The backward pass with the experts' data-gradient GEMMs in FP8 (grads
+    built with fp8=True): the step uses scaling.scale, records this step's
+    maxima and, with update_scaling, folds them into the history."""
+    if buf.logits is None:
+        raise ValueError("the forward buffers must keep the router logits (keep_logits=True)")
+    _lib.moe_backward_fp8(x, w.w_router, buf.logits, bias_mode, buf.topk_idx, buf.topk_w,
+                          buf.expert_offsets, buf.row_token, buf.assign_row, buf.y_rows,
+                          w.w_lat_down, w.w_gate, w.w_up, wt.w_lat_down_t, wt8.w_gate_t8,
+                          wt8.w_up_t8, wt8.w_down_t8, wt8.w_scale, wt.w_lat_up_t, g_out,
+                          scaling.scale, rounding, seed, grads.dx, grads.dw_router,
+                          grads.db_router, grads.dw_lat_down, grads.dw_gate, grads.dw_up,
+                          grads.dw_down, grads.dw_lat_up, grads.dtopk_w, scaling.amax, grads.ws,
+                          stream=stream)
+    if update_scaling:
+        scaling.update(stream=stream)
     return grads

@@ -231,3 +231,42 @@ def test_backward_workspace_and_bad_args():
     assert lib.moe_grad_cast_bf16(P + 4, 64, 1, 0, 1, P, None) == -2
     assert lib.moe_grad_cast_bf16(None, 64, 1, 0, 1, P, None) == -1
     assert lib.moe_grad_cast_bf16(P, 0, 1, 0, 1, P, None) == 0
+
+
+def _bwd8(lib, T=8, d=512, L=256, E=16, k=2, F=512, rounding=1, gscale=P, gamax=P, wg8=P,
+          wsb=1 << 40):
+    # x, w_router, logits, bias_mode, topk_idx, topk_w, offsets, row_token, assign_row, y_rows,
+    # w_lat_down, w_gate, w_up, w_lat_down_t, w_gate_t8, w_up_t8, w_down_t8, w_scale,
+    # w_lat_up_t, g_out, grad_scale
+    ins = [P] * 10 + [wg8, P, P, P, P, P, gscale]
+    outs = [P, P, None, P, P, P, P, P, None, gamax]
+    return lib.moe_backward_fp8(P, P, P, 0, *ins, T, d, L, E, k, F, rounding, 7, *outs, P, wsb,
+                                None)
+
+
+def test_backward_fp8_workspace_and_bad_args():
+    lib = _lib.load()
+    T, d, L, E, k, F = 4096, 6656, 3072, 64, 8, 10240
+    b16 = _lib.moe_workspace_bytes(5, T, d, L, E, k, F)
+    b8 = _lib.moe_workspace_bytes(6, T, d, L, E, k, F)
+    # the E5M2 codes of dy [T k, L] and dg, du [T k, F] on top of the bf16 backward's
+    assert b8 >= b16 + T * k * (L + 2 * F)
+    assert _bwd8(lib, rounding=2) == -1
+    assert _bwd8(lib, L=192) == -2          # FP8 widths: multiples of 128
+    assert _bwd8(lib, F=320) == -2
+    assert _bwd8(lib, gscale=None) == -1
+    assert _bwd8(lib, gamax=None) == -1
+    assert _bwd8(lib, wg8=None) == -1
+    assert _bwd8(lib, wg8=P + 4) == -2
+    # a workspace sized for the bf16 backward is too small (the call's own shape)
+    small16 = _lib.moe_workspace_bytes(5, 8, 512, 256, 16, 2, 512)
+    assert small16 < _lib.moe_workspace_bytes(6, 8, 512, 256, 16, 2, 512)
+    assert _bwd8(lib, wsb=small16) == -3
+    assert _bwd8(lib, T=0) == 0
+    # the E5M2 cast
+    assert lib.moe_grad_cast_e5m2(P, 64, P, 2, 0, 6, P, None) == -1
+    assert lib.moe_grad_cast_e5m2(P, 62, P, 1, 0, 6, P, None) == -2
+    assert lib.moe_grad_cast_e5m2(P + 4, 64, P, 1, 0, 6, P, None) == -2
+    assert lib.moe_grad_cast_e5m2(P, 64, P, 1, 0, 6, P + 2, None) == -2
+    assert lib.moe_grad_cast_e5m2(P, 64, None, 1, 0, 6, P, None) == -1
+    assert lib.moe_grad_cast_e5m2(P, 0, P, 1, 0, 6, P, None) == 0
