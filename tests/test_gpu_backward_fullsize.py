@@ -1,19 +1,26 @@
 """GPU parity of the backward pass at a full-size shape: one expert-parallel
 rank's share of the MAI-Base-1 layer (T = 32,768 tokens, d = 6,656, latent
 3,072, 64 experts of SwiGLU width 10,240, top-8; ~4,096 rows per expert), in
-the launch configuration ``bench.py --backward`` times, with stochastic
-rounding.
+the launch configuration ``bench.py --backward`` times (and ``--grad-fp8``),
+with stochastic rounding.
 
 The float64 oracle cannot run this backward whole, so it computes, from the
 pages' definitions in the same rounding model as tests/test_gpu_backward.py
-(bf16 operands, the same stochastic-rounding streams and element indices):
+and tests/test_gpu_backward_fp8.py (bf16 operands, the same stochastic-
+rounding streams and element indices; with FP8 data gradients the same E5M2
+operands, E4M3 weights and scales):
 * the input gradient dx and the gate-weight gradient of sampled tokens, one
   token at a time through each of its k experts and the router;
 * blocks (sampled rows x columns) of the weight gradients dW_down, dW_gate
   and dW_up of the two experts with the most and the fewest rows, summed over
   every row the expert received.
-Same rule as the small shapes: RMS(err)/RMS <= 1e-3, max|err|/RMS <= 5e-2.
-Every gradient the GPU wrote is finite.
+Rules as for the small shapes: bf16 data gradients RMS(err)/RMS <= 1e-3,
+max|err|/RMS <= 5e-2; with FP8 data gradients the gradients downstream of
+an FP8 GEMM (dx, dW_gate, dW_up) are held to the FP8 rule (8e-3, 0.15) and
+the others (the gate weights, dW_down) to the bf16 rule.  The FP8 gradient
+scales are 448 / the oracle's own maxima of dy, dg and du over the sampled
+tokens' rows (larger values saturate, identically on both sides).  Every
+gradient the GPU wrote is finite.
 """
 import numpy as np
 import pytest
@@ -25,23 +32,25 @@ from moe_synth import CONFIGS, device, gen
 from oracle import latent_moe_backward as OB
 from tests import gpu_util as U
 from tests.test_gpu_backward import GRAD_TOL_MAX, GRAD_TOL_RMS
+from tests.test_gpu_backward_fp8 import TOL_FP8_MAX, TOL_FP8_RMS
 
 pytestmark = [pytest.mark.gpu, pytest.mark.fullsize]
 
 SEED = 99
 N_TOKENS = 3
 N_COLS = 16
+F5 = float(np.float32(OB.E5M2_OVER_E4M3))
 
 
 def sr(v, stream, index):
     return OB.round_bf16_sr(v, SEED, stream, index=index)
 
 
-def check(name, got, want):
+def check(name, got, want, tol=(GRAD_TOL_MAX, GRAD_TOL_RMS)):
     emax, erms = U.rel_err(got, want)
     U.log(f"[bwd full] {name}: max|err|/RMS {emax:.2e}, RMS err {erms:.2e}")
-    assert emax <= GRAD_TOL_MAX, (name, emax)
-    assert erms <= GRAD_TOL_RMS, (name, erms)
+    assert emax <= tol[0], (name, emax)
+    assert erms <= tol[1], (name, erms)
 
 
 @pytest.fixture(scope="module")
@@ -51,29 +60,136 @@ def cuda():
     return torch.device("cuda:0")
 
 
-@pytest.mark.timeout(1200)
-def test_backward_full_size_sampled(cuda):
+class Host:
+    """Host-side inputs of the workload and one cached expert's weights (with
+    their E4M3 scales 448 / amax, float32)."""
+
+    def __init__(self, cfg):
+        self.cfg = cfg
+        U.log("[bwd full] host inputs")
+        self.x = gen.host_tensor_f64(cfg, "x")
+        self.w_dn = gen.host_tensor_f64(cfg, "w_dn")
+        self.w_lat_up = gen.host_tensor_f64(cfg, "w_lat_up")
+        self.w_r = gen.router_weights(cfg).astype(np.float64)
+        b = gen.router_bias(cfg)
+        self.b = None if b is None else b.astype(np.float64)
+        self._e, self._w, self._q = None, None, None
+
+    def expert(self, e):
+        if self._e != e:
+            ws = gen.expert_weights_f64(self.cfg, e)
+            sc = [np.float32(448.0) / np.float32(np.abs(m).max()) for m in ws]
+            self._e, self._w, self._q = e, (ws, sc), None
+        return self._w
+
+    def expert_e4m3(self, e):
+        """The expert's E4M3 weight values (the forward's quantization)."""
+        ws, sc = self.expert(e)
+        if self._q is None:
+            self._q = tuple(oracle.quantize_e4m3(m, s) for m, s in zip(ws, sc))
+        return self._q
+
+    def go_rows(self, g_out, ts):
+        idx = np.asarray(ts, np.int64)[:, None] * self.cfg.d + np.arange(self.cfg.d)[None, :]
+        return sr(g_out[ts].astype(np.float64), 1, idx)
+
+    def z_rows(self, ts):
+        return oracle.latent_down(self.x[ts], self.w_dn, "bf16_operands")
+
+
+def _dh(hst, e, dy, dy_b, idx, gscale, cols=slice(None)):
+    """dh = dy W_d[e] (columns cols): bf16 dy_b, or FP8 (E5M2 dy, E4M3 W_d)."""
+    (wg, wu, wd), (sg, su, sd) = hst.expert(e)
+    if gscale is None:
+        return dy_b @ wd[:, cols]
+    q = OB.quantize_grad_e5m2(dy, gscale[0], "sr", SEED, "dy", index=idx)
+    return (q @ hst.expert_e4m3(e)[2][:, cols]) / (F5 * float(gscale[0]) * float(sd))
+
+
+def _dz(hst, e, dg, du, dg_b, du_b, idx, gscale):
+    """The row's latent gradient dg W_g[e] + du W_u[e], bf16 or FP8."""
+    (wg, wu, wd), (sg, su, sd) = hst.expert(e)
+    if gscale is None:
+        return dg_b @ wg + du_b @ wu
+    qg = OB.quantize_grad_e5m2(dg, gscale[1], "sr", SEED, "dg", index=idx)
+    qu = OB.quantize_grad_e5m2(du, gscale[2], "sr", SEED, "du", index=idx)
+    qwg, qwu, _ = hst.expert_e4m3(e)
+    return (qg @ qwg) / (F5 * float(gscale[1]) * float(sg)) + \
+        (qu @ qwu) / (F5 * float(gscale[2]) * float(su))
+
+
+def _token_pass(hst, gi, g_out, toks, gscale):
+    """Per sampled token and slot: dtopk_w, and dz summed over the slots; with
+    gscale None also the maxima of |dy|, |dg|, |du| over the sampled rows."""
+    cfg = hst.cfg
+    L, F, k = cfg.L, cfg.F, cfg.k
+    dc = hst.go_rows(g_out, toks) @ hst.w_lat_up
+    z = hst.z_rows(toks)
+    dz = np.zeros((len(toks), L))
+    dtw = np.zeros((len(toks), k))
+    amax = np.zeros(3)
+    order = sorted(((int(gi["topk_idx"][t, j]), i, j) for i, t in enumerate(toks)
+                    for j in range(k)))
+    for e, i, j in order:
+        t = toks[i]
+        (wg, wu, wd), _ = hst.expert(e)
+        r = int(gi["assign_row"][t, j])
+        g = z[i] @ wg.T
+        u = z[i] @ wu.T
+        h = oracle.round_bf16(oracle.silu(g) * u)
+        dtw[i, j] = dc[i] @ (h @ wd.T)
+        lidx = r * L + np.arange(L)
+        fidx = r * F + np.arange(F)
+        dy = float(gi["topk_w"][t, j]) * dc[i]
+        dy_b = sr(dy, 2, lidx)
+        dh = _dh(hst, e, dy[None, :], dy_b[None, :], lidx[None, :], gscale)[0]
+        dg = dh * u * OB.silu_grad(g)
+        du = dh * oracle.silu(g)
+        amax = np.maximum(amax, [np.abs(dy).max(), np.abs(dg).max(), np.abs(du).max()])
+        dz[i] += _dz(hst, e, dg[None, :], du[None, :], sr(dg, 3, fidx)[None, :],
+                     sr(du, 4, fidx)[None, :], fidx[None, :], gscale)[0]
+    return dtw, dz, amax
+
+
+def _run(cuda, fp8):
     cfg = CONFIGS["base1_ep8"]
     T, d, L, E, k, F = cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F
-    U.log(f"[bwd full] {cfg.description}: inputs on the GPU, forward + backward")
+    U.log(f"[bwd full{' fp8' if fp8 else ''}] {cfg.description}: inputs on the GPU, forward")
     dv = device.device_inputs(cfg, cuda)
     w = moe.LatentMoEWeights(dv["w_router"], dv["b_router"], dv["w_dn"], dv["w_gate"], dv["w_up"],
                              dv["w_down"], dv["w_lat_up"])
     buf = moe.LatentMoEBuffers(T, d, L, E, k, F, device=cuda, keep_logits=True)
     moe.forward(dv["x"], w, k, buf)
-    wt = moe.backward_prepare(w)
-    grads = moe.LatentMoEGrads(T, d, L, E, k, F, device=cuda, bias=dv["b_router"] is not None)
+    torch.cuda.synchronize()
+    gi = {n: getattr(buf, n).cpu().numpy() for n in
+          ("topk_idx", "topk_w", "expert_counts", "expert_offsets", "row_token", "assign_row")}
     g_out = np.random.default_rng(SEED).standard_normal((T, d)).astype(np.float32)
-    moe.backward(dv["x"], w, wt, buf, torch.from_numpy(g_out).to(cuda), grads,
-                 rounding=moe.MOE_ROUND_STOCHASTIC, seed=SEED)
+    rng = np.random.default_rng(5)
+    toks = np.sort(rng.choice(T, N_TOKENS, replace=False))
+    hst = Host(cfg)
+    gscale = None
+    if fp8:
+        # scales from the oracle's own maxima over the sampled tokens' rows
+        _, _, am = _token_pass(hst, gi, g_out, toks, None)
+        gscale = tuple(np.float32(448.0) / np.float32(m) for m in am)
+        U.log(f"[bwd full fp8] gradient scales {gscale}")
+    U.log(f"[bwd full{' fp8' if fp8 else ''}] backward on the GPU")
+    wt = moe.backward_prepare(w)
+    grads = moe.LatentMoEGrads(T, d, L, E, k, F, device=cuda, bias=dv["b_router"] is not None,
+                               fp8=fp8)
+    go = torch.from_numpy(g_out).to(cuda)
+    if fp8:
+        wt8 = moe.quantize_transposed(wt, moe.quantize_experts(w))
+        sc = moe.Fp8GradScaling(hist_len=4, device=cuda)
+        sc.scale.copy_(torch.tensor(gscale, dtype=torch.float32))
+        moe.backward_fp8(dv["x"], w, wt, wt8, buf, go, grads, sc,
+                         rounding=moe.MOE_ROUND_STOCHASTIC, seed=SEED, update_scaling=False)
+    else:
+        moe.backward(dv["x"], w, wt, buf, go, grads, rounding=moe.MOE_ROUND_STOCHASTIC, seed=SEED)
     torch.cuda.synchronize()
     for n in ("dx", "dw_router", "dw_lat_down", "dw_gate", "dw_up", "dw_down", "dw_lat_up",
               "dtopk_w"):
         assert bool(torch.isfinite(getattr(grads, n)).all()), n
-    gi = {n: getattr(buf, n).cpu().numpy() for n in
-          ("topk_idx", "topk_w", "expert_counts", "expert_offsets", "row_token", "assign_row")}
-    rng = np.random.default_rng(5)
-    toks = np.sort(rng.choice(T, N_TOKENS, replace=False))
     dx_gpu = grads.dx[torch.from_numpy(toks).to(cuda)].cpu().numpy()
     dtw_gpu = grads.dtopk_w.cpu().numpy()[toks]
     counts = gi["expert_counts"]
@@ -85,60 +201,19 @@ def test_backward_full_size_sampled(cuda):
                       grads.dw_up[e].cpu().numpy()[np.ix_(fcols, lcols)]) for e in experts}
     del grads, wt, buf, w, dv
     torch.cuda.empty_cache()
-
-    U.log("[bwd full] host inputs")
-    x = gen.host_tensor_f64(cfg, "x")
-    w_dn = gen.host_tensor_f64(cfg, "w_dn")
-    w_lat_up = gen.host_tensor_f64(cfg, "w_lat_up")
-    w_r = gen.router_weights(cfg).astype(np.float64)
-    b = gen.router_bias(cfg)
-    logits = oracle.router_logits(x[toks], w_r, None if b is None else b.astype(np.float64))
-    probs = oracle.softmax(logits)
-
-    def go_rows(ts):
-        idx = np.asarray(ts, np.int64)[:, None] * d + np.arange(d)[None, :]
-        return sr(g_out[ts].astype(np.float64), 1, idx)
-
-    def z_rows(ts):
-        return oracle.latent_down(x[ts], w_dn, "bf16_operands")
+    tol8 = (TOL_FP8_MAX, TOL_FP8_RMS) if fp8 else (GRAD_TOL_MAX, GRAD_TOL_RMS)
 
     # ---- sampled tokens: dx and the gate-weight gradient ----
-    wcache = {}
-
-    def expert_w(e):
-        if e not in wcache:
-            wcache.clear()
-            wcache[e] = gen.expert_weights_f64(cfg, e)
-        return wcache[e]
-
-    dc = go_rows(toks) @ w_lat_up                       # [n, L]
-    z = z_rows(toks)
-    dz = np.zeros((len(toks), L))
-    dtw = np.zeros((len(toks), k))
-    order = sorted(((int(gi["topk_idx"][t, j]), i, j) for i, t in enumerate(toks) for j in range(k)))
-    for e, i, j in order:
-        t = toks[i]
-        wg, wu, wd = expert_w(e)
-        r = int(gi["assign_row"][t, j])
-        g = z[i] @ wg.T
-        u = z[i] @ wu.T
-        h = oracle.round_bf16(oracle.silu(g) * u)
-        y = h @ wd.T
-        dtw[i, j] = dc[i] @ y
-        dy_b = sr(float(gi["topk_w"][t, j]) * dc[i], 2, r * L + np.arange(L))
-        dh = dy_b @ wd
-        dg_b = sr(dh * u * OB.silu_grad(g), 3, r * F + np.arange(F))
-        du_b = sr(dh * oracle.silu(g), 4, r * F + np.arange(F))
-        dz[i] += dg_b @ wg + du_b @ wu
+    dtw, dz, _ = _token_pass(hst, gi, g_out, toks, gscale)
     dz_b = sr(dz, 5, toks[:, None].astype(np.int64) * L + np.arange(L)[None, :])
+    probs = oracle.softmax(oracle.router_logits(hst.x[toks], hst.w_r, hst.b))
     dp = np.zeros_like(probs)
     for i in range(len(toks)):
         for j in range(k):
             dp[i, gi["topk_idx"][toks[i], j]] += dtw[i, j]
-    dl = OB.softmax_backward(probs, dp)
-    dx = dz_b @ w_dn + dl @ w_r
+    dx = dz_b @ hst.w_dn + OB.softmax_backward(probs, dp) @ hst.w_r
     check("dtopk_w (sampled tokens)", dtw_gpu, dtw)
-    check("dx (sampled tokens)", dx_gpu, dx)
+    check("dx (sampled tokens)", dx_gpu, dx, tol8)
 
     # ---- weight-gradient blocks of two experts, over all their rows ----
     for e in experts:
@@ -148,14 +223,16 @@ def test_backward_full_size_sampled(cuda):
         slot = np.argmax(gi["assign_row"][ts] == rows[:, None], axis=1)
         wts = gi["topk_w"][ts, slot].astype(np.float64)
         U.log(f"[bwd full] expert {e}: {bnd - a} rows")
-        wg, wu, wd = expert_w(e)
-        zr = z_rows(ts)                                   # [R_e, L]
-        dcr = go_rows(ts) @ w_lat_up                      # [R_e, L]
-        dy_b = sr(wts[:, None] * dcr, 2, rows[:, None] * L + np.arange(L)[None, :])
+        (wg, wu, wd), _ = hst.expert(e)
+        zr = hst.z_rows(ts)                                   # [R_e, L]
+        dcr = hst.go_rows(g_out, ts) @ hst.w_lat_up           # [R_e, L]
+        lidx = rows[:, None] * L + np.arange(L)[None, :]
+        dy = wts[:, None] * dcr
+        dy_b = sr(dy, 2, lidx)
         g = zr @ wg[fcols].T
         u = zr @ wu[fcols].T
-        h = oracle.round_bf16(oracle.silu(g) * u)          # [R_e, n] at fcols
-        dh = dy_b @ wd[:, fcols]
+        h = oracle.round_bf16(oracle.silu(g) * u)             # [R_e, n] at fcols
+        dh = _dh(hst, e, dy, dy_b, lidx, gscale, cols=fcols)
         fidx = rows[:, None] * F + fcols[None, :]
         dg_b = sr(dh * u * OB.silu_grad(g), 3, fidx)
         du_b = sr(dh * oracle.silu(g), 4, fidx)
@@ -164,5 +241,15 @@ def test_backward_full_size_sampled(cuda):
         want_up = du_b.T @ zr[:, lcols]
         got_down, got_gate, got_up = blocks_gpu[e]
         check(f"dW_down[{e}] block", got_down, want_down)
-        check(f"dW_gate[{e}] block", got_gate, want_gate)
-        check(f"dW_up[{e}] block", got_up, want_up)
+        check(f"dW_gate[{e}] block", got_gate, want_gate, tol8)
+        check(f"dW_up[{e}] block", got_up, want_up, tol8)
+
+
+@pytest.mark.timeout(1200)
+def test_backward_full_size_sampled(cuda):
+    _run(cuda, fp8=False)
+
+
+@pytest.mark.timeout(1200)
+def test_backward_fp8_full_size_sampled(cuda):
+    _run(cuda, fp8=True)
