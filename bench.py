@@ -135,12 +135,14 @@ def layer_bytes(cfg, touched, esize=2):
     return w + T * d * 2.0 + T * d * 4.0
 
 
-def cpu_baseline(cfg, n_tok=4096, n_exp=192, seed=0, fp8=False):
+def cpu_baseline(cfg, n_tok=4096, n_exp=192, seed=0, fp8=False, reps=3):
     """The oracle (float64 numpy, as it stands) on a bounded sample of the
     workload, extrapolated to tokens/s of the whole layer:
       router + permutation over all T tokens (timed in full),
       latent down, combine and up-projection on n_tok tokens (x T/n_tok),
-      n_exp experts' SwiGLU FFNs on their routed rows (x E/n_exp).
+      n_exp experts' SwiGLU FFNs on their routed rows (x E/n_exp), each
+      timed reps times (the mean is used: ~10 s of timed work at Base-1
+      T = 4,096 without generating more weights).
     Input generation is not timed.  fp8: the experts in the oracle's
     fp8_operands mode (scales from the sample's own ranges)."""
     import numpy as np
@@ -195,8 +197,10 @@ def cpu_baseline(cfg, n_tok=4096, n_exp=192, seed=0, fp8=False):
             h = oracle.swiglu_activation(zr, wts[0], wts[1], "fp8_operands", sc)
             sc = (s_z, s_w[0], s_w[1], np.float32(448.0) / np.float32(np.abs(h).max()), s_w[2])
         t0 = time.perf_counter()
-        oracle.swiglu_expert(zr, *wts, mode="fp8_operands" if fp8 else "bf16_operands", fp8=sc)
-        t_exp += time.perf_counter() - t0
+        for _ in range(reps):
+            oracle.swiglu_expert(zr, *wts, mode="fp8_operands" if fp8 else "bf16_operands",
+                                 fp8=sc)
+        t_exp += (time.perf_counter() - t0) / reps
         rows_done += bnd - a
         del wts
     # experts scale by rows (their cost is linear in the rows they receive)
@@ -209,9 +213,10 @@ def cpu_baseline(cfg, n_tok=4096, n_exp=192, seed=0, fp8=False):
                    f"({t_route:.2f} s), latent down/combine/up on {len(toks)} tokens "
                    f"({t_tok:.2f} s, scaled x{cfg.T / len(toks):.0f}), SwiGLU experts on "
                    f"{len(sample)} sampled experts = {rows_done} routed rows ({t_exp:.2f} s, "
-                   f"scaled by rows to all {cfg.T * cfg.k}); {t_route + t_tok + t_exp:.1f} s of "
-                   f"timed oracle work, extrapolated {total:.1f} s per forward pass (weight "
-                   f"generation, {t_gen:.0f} s, not timed)"),
+                   f"mean of {reps} timings, scaled by rows to all {cfg.T * cfg.k}); "
+                   f"{t_route + t_tok + reps * t_exp:.1f} s of timed oracle work, extrapolated "
+                   f"{total:.1f} s per forward pass (weight generation, {t_gen:.0f} s, not "
+                   f"timed)"),
     }
 
 

@@ -80,3 +80,56 @@ def test_forward_and_backward_replay_bitwise(cuda):
             assert torch.equal(a, b), f"replay {rep} differs from the eager run"
         assert torch.equal(bg.expert_counts.cpu(),
                            torch.bincount(ref[0].cpu().view(-1).long(), minlength=cfg.E).int())
+
+
+def test_fp8_backward_replay_bitwise(cuda):
+    """The FP8-data-gradient backward (its gradient maxima zeroed by a fill
+    kernel) replays bitwise like eager runs with the same scales."""
+    cfg = CFG
+    dv = device.device_inputs(cfg, cuda)
+    w = _weights(dv)
+    wt = moe.backward_prepare(w)
+    wt8 = moe.quantize_transposed(wt, moe.quantize_experts(w))
+    g_out = torch.randn((cfg.T, cfg.d), generator=torch.Generator(device=cuda).manual_seed(6),
+                        device=cuda, dtype=torch.float32)
+    buf = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, device=cuda,
+                               keep_logits=True)
+    moe.forward(dv["x"], w, cfg.k, buf)
+    scales = torch.tensor([300.0, 120.0, 150.0], dtype=torch.float32, device=cuda)
+
+    def state():
+        g = moe.LatentMoEGrads(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, device=cuda, fp8=True)
+        sc = moe.Fp8GradScaling(hist_len=4, device=cuda)
+        sc.scale.copy_(scales)
+        return g, sc
+
+    def step(g, sc):
+        moe.backward_fp8(dv["x"], w, wt, wt8, buf, g_out, g, sc, seed=11, update_scaling=False)
+
+    def snapshot(g, sc):
+        return [t.clone() for t in (g.dx, g.dw_gate, g.dw_up, g.dw_lat_down, g.dtopk_w, sc.amax)]
+
+    ge, se = state()
+    step(ge, se)
+    torch.cuda.synchronize()
+    ref = snapshot(ge, se)
+    gg, sg = state()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(gg, sg)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(gg, sg)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (gg.dx, gg.dw_gate, sg.amax):
+            t.fill_(7.0)                   # stale results (and maxima) must not survive
+        step(ge, se)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, snapshot(gg, sg)):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager run"
