@@ -25,6 +25,7 @@ FULL = {  # workload -> number of sampled tokens for the output check
     "base1_compute": 3,
     "base1_imbalanced": 6,
     "base2": 2,
+    "base1_f5120": 3,
 }
 
 
