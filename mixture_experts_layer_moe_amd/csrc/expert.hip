@@ -24,10 +24,16 @@ ExpertGemmPlan plan_expert_gemms(int64_t rows, int E) {
   return p;
 }
 
-// Dense GEMM tile choice: 256 x 256 when that alone gives every CU two tiles,
-// else 128 x 256.
+// Dense GEMM tile choice: 256 x 256 when that alone gives every CU two tiles;
+// 256 x 192 when those tiles fill the chip exactly once (at most one per CU,
+// at least 90% of the CUs busy); else 128 x 256.
 static bool big_dense(int64_t M, int64_t Ncols) {
   return ceil_div(M, 256) * ceil_div(Ncols, 256) >= 2 * (int64_t)device_cu_count();
+}
+static bool wide_dense(int64_t M, int64_t Ncols) {
+  const int64_t tiles = ceil_div(M, 256) * ceil_div(Ncols, 192);
+  const int64_t cus = device_cu_count();
+  return tiles <= cus && tiles * 10 >= cus * 9;
 }
 
 template <class C, int EPI, int NSEG>
@@ -42,6 +48,8 @@ template <int EPI, int NSEG>
 hipError_t dense_gemm_auto(GemmArgs a, int64_t M, hipStream_t s) {
   const int64_t ncols = epi_swiglu(EPI) ? 2 * (int64_t)a.N : a.N;
   if (big_dense(M, ncols)) return dense_gemm<TileBig, EPI, NSEG>(a, M, s);
+  if constexpr (!epi_swiglu(EPI))
+    if (wide_dense(M, ncols)) return dense_gemm<TileWide, EPI, NSEG>(a, M, s);
   return dense_gemm<TileMid, EPI, NSEG>(a, M, s);
 }
 template hipError_t dense_gemm_auto<EPI_F32, 1>(GemmArgs, int64_t, hipStream_t);

@@ -702,6 +702,7 @@ inline int persistent_grid(int64_t tiles_upper_bound) {
 //   Mid    : 128 x 256, BK 64, 2 x 4 waves, 3 stages -- dense GEMMs too small
 //            to give every CU two 256 x 256 tiles
 //   Router :  64 x 128, BK 64, 2 x 2 waves, 4 stages (96 KB) -- small batches
+//   Wide   : below
 template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool BNT>
 struct TileCfg {
   static constexpr int bm = BM, bn = BN, bk = BK, wm = WM, wn = WN, nstage = NSTAGE;
@@ -711,6 +712,10 @@ using TileStream = TileCfg<128, 256, 64, 2, 4, 3, true>;
 using TileBig = TileCfg<256, 256, 64, 2, 4, 2, false>;
 using TileMid = TileCfg<128, 256, 64, 2, 4, 3, false>;
 using TileRouter = TileCfg<64, 128, 64, 2, 2, 4, false>;
+// Wide : 256 x 192, BK 64, 4 x 2 waves (64 x 96 each), 2 stages (112 KB) --
+//        dense GEMMs whose 256 x 192 tiles fill the chip exactly once (e.g.
+//        M 4,096 x N 3,072: 256 tiles), where 128 x 256 tiles take 1.5 waves
+using TileWide = TileCfg<256, 192, 64, 4, 2, 2, false>;
 
 template <class C, bool GROUPED, bool GATHER, int EPI, int NSEG = 1, int F8 = F8_NONE,
           bool KG = false>
