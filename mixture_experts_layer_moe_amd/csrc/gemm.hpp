@@ -162,6 +162,12 @@ struct GemmArgs {
   int sr;
   const int32_t* kpre;
   int64_t c_expert_stride;
+  // dense, split K (ksplit > 1): the concatenated K stages are cut into
+  // ksplit chunks of equal length (the last may be shorter or empty); tile
+  // -> (chunk, M tile, N tile), chunk s writing its partial result to
+  // C + s * c_split (the caller sums the chunks)
+  int ksplit;
+  int64_t c_split;
 };
 
 // fp32 -> FP8 E4M3 byte, round to nearest even, saturating at +-448
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   static_assert(!(KG && (GROUPED || GATHER || NSEG != 1)), "K-grouped tiles: one plain segment");
   if constexpr (GROUPED) total = a.tile_prefix[a.E] * a.n_tiles;
   else if constexpr (KG) total = a.E * a.m_tiles * a.n_tiles;
-  else total = a.m_tiles * a.n_tiles;
+  else total = a.m_tiles * a.n_tiles * (a.ksplit > 1 ? a.ksplit : 1);
   const int xcd = blockIdx.x & 7;
   const int nj = gridDim.x >> 3;
   const int t_begin = (int)((int64_t)total * xcd / 8);
@@ -291,7 +297,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
     ldb2[S] = (uint32_t)(a.seg[S].ldb * ES);
     ktotal += kseg[S];
   });
-  int nk = ktotal / KE;      // K-grouped tiles: set per tile
+  const int nk_all = ktotal / KE;
+  int nk = nk_all;           // K-grouped and split-K tiles: set per tile
   float amax_run = 0.f;     // Q8: largest |bf16 output| this lane wrote
   float amax_dg = 0.f, amax_du = 0.f;   // GBQ8: largest |dg|, |du| of this lane
 
@@ -323,6 +330,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
     int64_t b_off = 0;
     float dq_b = 1.f, dq_b2 = 1.f;     // F8: 1 / (s_A s_B), 1 / (s_A s_B2)
     int kg_e = 0, kg_k0 = 0, kg_k = 0; // KG: expert, first K column and K extent
+    int kt0 = 0, ks = 0;               // split K: the chunk's first stage, the chunk
     if constexpr (GROUPED) {
       // table reads at a uniform address: every lane gets the same value
       const int e = __builtin_amdgcn_readfirstlane(a.tile_expert[t / a.n_tiles]);
@@ -363,9 +371,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       // Groups of DENSE_GM M panels: inside a group the tiles go N tile by N
       // tile with the M panel fastest, so a window of concurrent tiles spans a
       // few M panels and a few N tiles and both operands are re-read rarely.
-      const int g = t / (DENSE_GM * a.n_tiles);
+      int td = t;
+      if (a.ksplit > 1) {
+        const int per = a.m_tiles * a.n_tiles;
+        const int ch = (nk_all + a.ksplit - 1) / a.ksplit;
+        ks = td / per;
+        td -= ks * per;
+        kt0 = ks * ch;
+        nk = max(0, min(ch, nk_all - kt0));
+      }
+      const int g = td / (DENSE_GM * a.n_tiles);
       const int gm = min(DENSE_GM, a.m_tiles - g * DENSE_GM);
-      const int r = t - g * DENSE_GM * a.n_tiles;
+      const int r = td - g * DENSE_GM * a.n_tiles;
       n_tile = r / gm;
       r0 = (g * DENSE_GM + (r - n_tile * gm)) * BM;
       mrows = min(BM, a.M - r0);
@@ -460,8 +477,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
         }
       }
     };
-    auto issue = [&](int kt, auto part_c) {
-      int k0 = kt * KE;
+    auto issue = [&](int kt, auto part_c) {   // kt: the tile's stage (its ring slot)
+      int k0 = (kt0 + kt) * KE;
       if constexpr (NSEG == 1) {
         issue_seg(std::integral_constant<int, 0>{}, kt, k0, part_c);
       } else {
@@ -513,7 +530,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
           // the first segment's products are complete: bring them to the
           // second segment's scale, so that the final dq_b2 divides each
           // segment by its own scales
-          if (kt * KE == kseg[0]) {
+          if ((kt0 + kt) * KE == kseg[0]) {
             const float ratio = dq_b / dq_b2;
 #pragma unroll
             for (int i = 0; i < NACT; ++i)
@@ -597,7 +614,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
     const float q5_du = GBQ8 ? E5M2_OVER_E4M3 * a.out_scale[2] : 1.f;
     // FP8 with two K segments: the accumulators hold the second segment's scale
     const float dq_out = SEG_DQ ? dq_b2 : dq_b;
-    const int64_t c_off = KG ? (int64_t)kg_e * a.c_expert_stride : 0;   // KG: the expert's block
+    // KG: the expert's block; split K: the chunk's partial result
+    const int64_t c_off = KG ? (int64_t)kg_e * a.c_expert_stride : (int64_t)ks * a.c_split;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -655,7 +673,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
               amax_run = fmaxf(amax_run, fabsf(zv));
               ((uint8_t*)a.C)[row * a.ldc + col] = f32_to_e4m3_sat(zv * oscale);
             } else if constexpr (EPI == EPI_F32_BIAS) {
-              ((float*)a.C)[row * a.ldc + col] = val + (a.bias ? a.bias[col] : 0.f);
+              ((float*)a.C)[c_off + row * a.ldc + col] = val + (a.bias ? a.bias[col] : 0.f);
             } else {
               ((float*)a.C)[c_off + row * a.ldc + col] = val;
             }
@@ -701,7 +719,6 @@ inline int persistent_grid(int64_t tiles_upper_bound) {
 //   Big    : 256 x 256, BK 64, 2 x 4 waves, 2 stages (128 KB) -- MFMA-bound
 //   Mid    : 128 x 256, BK 64, 2 x 4 waves, 3 stages -- dense GEMMs too small
 //            to give every CU two 256 x 256 tiles
-//   Router :  64 x 128, BK 64, 2 x 2 waves, 4 stages (96 KB) -- small batches
 //   Wide   : below
 template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool BNT>
 struct TileCfg {
@@ -711,7 +728,6 @@ struct TileCfg {
 using TileStream = TileCfg<128, 256, 64, 2, 4, 3, true>;
 using TileBig = TileCfg<256, 256, 64, 2, 4, 2, false>;
 using TileMid = TileCfg<128, 256, 64, 2, 4, 3, false>;
-using TileRouter = TileCfg<64, 128, 64, 2, 2, 4, false>;
 // Wide : 256 x 192, BK 64, 4 x 2 waves (64 x 96 each), 2 stages (112 KB) --
 //        dense GEMMs whose 256 x 192 tiles fill the chip exactly once (e.g.
 //        M 4,096 x N 3,072: 256 tiles), where 128 x 256 tiles take 1.5 waves

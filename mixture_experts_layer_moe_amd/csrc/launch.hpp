@@ -8,16 +8,26 @@
 namespace moe {
 
 // route.hip
+// K chunks of the routing GEMM (a function of the shapes only): 1, or 2-4
+// when its 128 x 256 tiles alone would leave MI355X's CUs idle; the GEMM then
+// writes router_ksplit partial logit arrays [T, E] (no bias) that the top-k
+// kernel sums.
+int router_ksplit(int64_t T, int E);
+// logits: router_ksplit(T, E) arrays of T * E floats, back to back.  With one
+// chunk the logits (with bias) are final; with several, partials.
 hipError_t launch_router_gemm(const uint16_t* x, const float* w_router, const float* bias,
                               int64_t T, int d, int E, uint16_t* w3, float* logits,
                               hipStream_t s);
-// Softmax over all E logits and top-k.  sel_bias (nullable): per-expert bias
-// added to the selection values only.  prob_sum (nullable): per-expert sum of
+// Softmax over all E logits and top-k.  logits: nsplit partial arrays of T * E
+// floats (summed in order, then lbias added when given; logits_out, when
+// given, receives the sums).  sel_bias (nullable): per-expert bias added to
+// the selection values only.  prob_sum (nullable): per-expert sum of
 // probabilities over all tokens (prob_part: topk_partial_floats(T, E) floats
 // of scratch for the deterministic fixed-order reduction).
 int64_t topk_chunks(int64_t T);
 int64_t topk_partial_floats(int64_t T, int E);
-hipError_t launch_softmax_topk(const float* logits, const float* sel_bias, int64_t T, int E, int k,
+hipError_t launch_softmax_topk(const float* logits, int nsplit, const float* lbias,
+                               float* logits_out, const float* sel_bias, int64_t T, int E, int k,
                                int32_t* topk_idx, float* topk_w, float* prob_part,
                                float* prob_sum, hipStream_t s);
 

@@ -35,7 +35,7 @@ RouteWs route_ws(int64_t T, int d, int E) {
   RouteWs w;
   w.w3 = 0;
   w.logits = align_up((size_t)3 * E * d * 2);
-  w.part = w.logits + align_up((size_t)T * E * 4);
+  w.part = w.logits + align_up((size_t)router_ksplit(T, E) * T * E * 4);
   w.total = w.part + align_up((size_t)topk_partial_floats(T, E) * 4);
   return w;
 }
@@ -247,9 +247,14 @@ int moe_route_ex(const uint16_t* x, const float* w_router, const float* b_router
   if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   char* base = (char*)ws;
-  float* logits = logits_out ? logits_out : (float*)(base + w.logits);
-  // bias in the logits: added by the GEMM epilogue; selection only: added by
-  // the top-k kernel to the selection values
+  // one K chunk: the GEMM writes the final logits (into logits_out when
+  // given); several: partial logits in the workspace, summed by the top-k
+  // kernel, which then writes logits_out
+  const int ks = router_ksplit(T, E);
+  float* logits = (ks == 1 && logits_out) ? logits_out : (float*)(base + w.logits);
+  // bias in the logits: added by the GEMM epilogue (one chunk) or the top-k
+  // kernel (several); selection only: added by the top-k kernel to the
+  // selection values
   const float* gemm_bias = bias_mode == MOE_BIAS_LOGITS ? b_router : nullptr;
   const float* sel_bias = bias_mode == MOE_BIAS_SELECTION ? b_router : nullptr;
   {
@@ -259,7 +264,9 @@ int moe_route_ex(const uint16_t* x, const float* w_router, const float* b_router
   }
   if (st) return st;
   EventScope ev(K_ROUTER_TOPK, s);
-  return hip_status(launch_softmax_topk(logits, sel_bias, T, E, k, topk_idx, topk_w,
+  return hip_status(launch_softmax_topk(logits, ks, ks > 1 ? gemm_bias : nullptr,
+                                        ks > 1 ? logits_out : nullptr, sel_bias, T, E, k,
+                                        topk_idx, topk_w,
                                         prob_sum ? (float*)(base + w.part) : nullptr, prob_sum,
                                         s));
 }

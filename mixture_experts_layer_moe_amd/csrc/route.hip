@@ -52,26 +52,42 @@ hipError_t launch_router_gemm(const uint16_t* x, const float* w_router, const fl
   a.C = logits;
   a.ldc = E;
   a.bias = bias;
+  // the K split is decided from the shapes first (the top-k kernel sums as
+  // many partial arrays)
+  const int ks = router_ksplit(T, E);
   // large batches: 256 x 256 tiles already give every CU a tile
-  if (ceil_div(T, TileBig::bm) * ceil_div(E, TileBig::bn) >= device_cu_count()) {
+  if (ks == 1 && ceil_div(T, TileBig::bm) * ceil_div(E, TileBig::bn) >= device_cu_count()) {
     a.m_tiles = (int)ceil_div(T, TileBig::bm);
     a.n_tiles = (int)ceil_div(E, TileBig::bn);
     return launch_gemm<TileBig, false, false, EPI_F32_BIAS, 3>(a, (int64_t)a.m_tiles * a.n_tiles,
                                                             s);
   }
-  // mid batches (e.g. T = 16,384 at E = 512): 128 x 256 tiles, one per CU;
-  // the 64 x 128 router tile reads 3 fragment blocks per 2 MFMAs and is only
-  // worth it when nothing larger fills the chip
-  if (ceil_div(T, TileMid::bm) * ceil_div(E, TileMid::bn) >= device_cu_count()) {
-    a.m_tiles = (int)ceil_div(T, TileMid::bm);
-    a.n_tiles = (int)ceil_div(E, TileMid::bn);
+  // mid batches (e.g. T = 16,384 at E = 512): 128 x 256 tiles, one per CU
+  a.m_tiles = (int)ceil_div(T, TileMid::bm);
+  a.n_tiles = (int)ceil_div(E, TileMid::bn);
+  if (ks == 1)
     return launch_gemm<TileMid, false, false, EPI_F32_BIAS, 3>(a, (int64_t)a.m_tiles * a.n_tiles,
                                                             s);
-  }
-  a.m_tiles = (int)ceil_div(T, TileRouter::bm);
-  a.n_tiles = (int)ceil_div(E, TileRouter::bn);
-  return launch_gemm<TileRouter, false, false, EPI_F32_BIAS, 3>(a, (int64_t)a.m_tiles * a.n_tiles,
-                                                             s);
+  // small batches (e.g. T = 4,096): the same tiles, K split into ks chunks
+  // (each a run of 3 d / ks of the hi/mid/lo K), so that ks times as many
+  // workgroups share the long K loop; each chunk writes partial logits
+  // without bias and the top-k kernel sums them in chunk order
+  a.ksplit = ks;
+  a.c_split = T * (int64_t)E;
+  a.bias = nullptr;
+  return launch_gemm<TileMid, false, false, EPI_F32_BIAS, 3>(
+      a, (int64_t)a.m_tiles * a.n_tiles * ks, s);
+}
+
+// Chunks so that the 128 x 256 tiles times the chunks come near the 256 CUs
+// of an MI355X (at most 4), unless the 128 x 256 tiles fill them already.
+// A function of the shapes only, so that workspace sizes are too.
+int router_ksplit(int64_t T, int E) {
+  constexpr int64_t CUS = 256;
+  const int64_t tiles = ceil_div(T, 128) * ceil_div(E, 256);
+  if (tiles >= CUS) return 1;
+  const int64_t ks = CUS / (tiles > 0 ? tiles : 1);
+  return (int)(ks < 1 ? 1 : (ks > 4 ? 4 : ks));
 }
 
 // ---------------------------------------------------------------------------
@@ -92,11 +108,15 @@ constexpr int TOPK_CHUNK = 4 * TOPK_TOK_PER_WAVE;   // tokens per workgroup
 
 template <int PER_LANE>
 __global__ __launch_bounds__(256) void softmax_topk_kernel(const float* __restrict__ logits,
+                                                           int nsplit,
+                                                           const float* __restrict__ lbias,
+                                                           float* __restrict__ logits_out,
                                                            const float* __restrict__ sel_bias,
                                                            int64_t T, int E, int k,
                                                            int32_t* __restrict__ topk_idx,
                                                            float* __restrict__ topk_w,
                                                            float* __restrict__ prob_part) {
+  const int64_t split_stride = T * (int64_t)E;
   __shared__ float part[4][PER_LANE * 64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -119,7 +139,16 @@ __global__ __launch_bounds__(256) void softmax_topk_kernel(const float* __restri
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) {
       const int e = lane + 64 * i;
-      v[i] = e < E ? row[e] : -INFINITY;
+      if (e < E) {
+        // K chunks of the routing GEMM in order, then the logit bias
+        float l = row[e];
+        for (int c = 1; c < nsplit; ++c) l += row[c * split_stride + e];
+        if (lbias != nullptr) l += lbias[e];
+        if (logits_out != nullptr) logits_out[t * E + e] = l;
+        v[i] = l;
+      } else {
+        v[i] = -INFINITY;
+      }
       m = fmaxf(m, v[i]);
     }
 #pragma unroll
@@ -217,14 +246,15 @@ int64_t topk_partial_floats(int64_t T, int E) {
   return (n + ceil_div(n, PROB_GROUP)) * E;
 }
 
-hipError_t launch_softmax_topk(const float* logits, const float* sel_bias, int64_t T, int E, int k,
+hipError_t launch_softmax_topk(const float* logits, int nsplit, const float* lbias,
+                               float* logits_out, const float* sel_bias, int64_t T, int E, int k,
                                int32_t* topk_idx, float* topk_w, float* prob_part,
                                float* prob_sum, hipStream_t s) {
   const dim3 grid((unsigned)topk_chunks(T)), block(256);
   const int per = (int)ceil_div(E, 64);
 #define MOE_TOPK_LAUNCH(P)                                                                      \
-  hipLaunchKernelGGL(softmax_topk_kernel<P>, grid, block, 0, s, logits, sel_bias, T, E, k,      \
-                     topk_idx, topk_w, prob_part)
+  hipLaunchKernelGGL(softmax_topk_kernel<P>, grid, block, 0, s, logits, nsplit, lbias,          \
+                     logits_out, sel_bias, T, E, k, topk_idx, topk_w, prob_part)
   if (per <= 1) MOE_TOPK_LAUNCH(1);
   else if (per <= 2) MOE_TOPK_LAUNCH(2);
   else if (per <= 4) MOE_TOPK_LAUNCH(4);
