@@ -92,7 +92,9 @@ int router_ksplit(int64_t T, int E) {
 
 // ---------------------------------------------------------------------------
 // softmax over all E logits + top-k.  A workgroup is 4 waves; each wave
-// handles TOPK_TOK_PER_WAVE consecutive tokens, one at a time.
+// handles TOPK_TOK_PER_WAVE consecutive tokens, one at a time (one token per
+// wave: at T = 4,096 that is 1,024 workgroups, enough waves in flight to hide
+// the loads of the logits; four per wave took 2.5x as long there).
 // Lane l holds logits l, l+64, ...; the max, the sum of exponentials and each
 // of the k argmax rounds are wave reductions with a fixed butterfly order, so
 // the result is deterministic.  Ranking key: (selection value descending,
@@ -103,7 +105,7 @@ int router_ksplit(int64_t T, int E) {
 // the 4 waves in order) to prob_part[chunk][E]; reduce_prob_kernel sums the
 // chunks in order.
 // ---------------------------------------------------------------------------
-constexpr int TOPK_TOK_PER_WAVE = 4;
+constexpr int TOPK_TOK_PER_WAVE = 1;
 constexpr int TOPK_CHUNK = 4 * TOPK_TOK_PER_WAVE;   // tokens per workgroup
 
 template <int PER_LANE>

@@ -40,14 +40,14 @@ def test_status_strings():
 def test_workspace_sizes():
     a = lambda v: (v + 255) // 256 * 256  # noqa: E731
     T, d, L, E, k, F = 4096, 6656, 3072, 512, 8, 10240
-    n = (T + 15) // 16   # 16-token chunks of the probability partials
+    n = (T + 3) // 4     # 4-token chunks of the probability partials
     # router: the split weights, then the logits -- at T = 4,096 the routing
     # GEMM's 128 x 256 tiles (32 x 2) are split into 4 K chunks of partial
     # logits -- then the probability partials
     assert _lib.moe_workspace_bytes(0, T, d, L, E, k, F) == \
         a(3 * E * d * 2) + a(4 * T * E * 4) + a((n + (n + 63) // 64) * E * 4)
     T2 = 32768     # 512 tiles of 128 x 256: no split
-    n2 = (T2 + 15) // 16
+    n2 = (T2 + 3) // 4
     assert _lib.moe_workspace_bytes(0, T2, d, L, E, k, F) == \
         a(3 * E * d * 2) + a(T2 * E * 4) + a((n2 + (n2 + 63) // 64) * E * 4)
     assert _lib.moe_workspace_bytes(1, T, d, L, E, k, F) == 2 * a(16 * E * 4)
