@@ -24,16 +24,22 @@ ExpertGemmPlan plan_expert_gemms(int64_t rows, int E) {
   return p;
 }
 
-// Dense GEMM tile choice: 256 x 256 when that alone gives every CU two tiles;
-// 256 x 192 when those tiles fill the chip exactly once (at most one per CU,
-// at least 90% of the CUs busy); else 128 x 256.
-static bool big_dense(int64_t M, int64_t Ncols) {
-  return ceil_div(M, 256) * ceil_div(Ncols, 256) >= 2 * (int64_t)device_cu_count();
-}
-static bool wide_dense(int64_t M, int64_t Ncols) {
-  const int64_t tiles = ceil_div(M, 256) * ceil_div(Ncols, 192);
+// Dense GEMM tile choice by the cost rounds x tile area / efficiency (rounds
+// = tiles over CUs, rounded up; areas 4 : 3 : 2 for 256 x 256 : 256 x 192 :
+// 128 x 256, efficiencies 1 : 0.94 : 0.83 -- a smaller tile reads more operand
+// bytes per MFMA), ties to the larger tile.  E.g. M 4,096 x N 3,072: 256 x 192
+// (one round of 256 tiles); M 4,096 x N 6,656: 256 x 256 (416 tiles, two
+// rounds) rather than 128 x 256 (832 tiles, four); M 16,384 x N 8,704: 256 x
+// 256 (9 rounds) rather than 128 x 256 (17).
+enum DenseTile { DT_BIG, DT_WIDE, DT_MID };
+static DenseTile dense_tile(int64_t M, int64_t Ncols, bool wide_ok) {
   const int64_t cus = device_cu_count();
-  return tiles <= cus && tiles * 10 >= cus * 9;
+  auto rounds = [&](int bm, int bn) { return ceil_div(ceil_div(M, bm) * ceil_div(Ncols, bn), cus); };
+  const int64_t big = 40 * rounds(256, 256), wide = 32 * rounds(256, 192),
+                mid = 24 * rounds(128, 256);
+  if (big <= mid && (!wide_ok || big <= wide)) return DT_BIG;
+  if (wide_ok && wide <= mid) return DT_WIDE;
+  return DT_MID;
 }
 
 template <class C, int EPI, int NSEG>
@@ -47,10 +53,15 @@ static hipError_t dense_gemm(GemmArgs a, int64_t M, hipStream_t s) {
 template <int EPI, int NSEG>
 hipError_t dense_gemm_auto(GemmArgs a, int64_t M, hipStream_t s) {
   const int64_t ncols = epi_swiglu(EPI) ? 2 * (int64_t)a.N : a.N;
-  if (big_dense(M, ncols)) return dense_gemm<TileBig, EPI, NSEG>(a, M, s);
-  if constexpr (!epi_swiglu(EPI))
-    if (wide_dense(M, ncols)) return dense_gemm<TileWide, EPI, NSEG>(a, M, s);
-  return dense_gemm<TileMid, EPI, NSEG>(a, M, s);
+  // the 256 x 192 tile splits 192 columns into 2 waves of 96: not for the
+  // interleaved gate/up pairs of the SwiGLU epilogue
+  switch (dense_tile(M, ncols, !epi_swiglu(EPI))) {
+    case DT_BIG: return dense_gemm<TileBig, EPI, NSEG>(a, M, s);
+    case DT_WIDE:
+      if constexpr (!epi_swiglu(EPI)) return dense_gemm<TileWide, EPI, NSEG>(a, M, s);
+      return hipErrorInvalidValue;
+    default: return dense_gemm<TileMid, EPI, NSEG>(a, M, s);
+  }
 }
 template hipError_t dense_gemm_auto<EPI_F32, 1>(GemmArgs, int64_t, hipStream_t);
 template hipError_t dense_gemm_auto<EPI_F32, 2>(GemmArgs, int64_t, hipStream_t);

@@ -50,6 +50,9 @@ CASES = {
     "single": MoEConfig("single", T=100, d=128, L=64, E=1, k=1, F=128, seed=15),
     "dense": MoEConfig("dense", T=64, d=128, L=64, E=8, k=8, F=128, seed=17),
     "one_token": MoEConfig("one_token", T=1, d=256, L=128, E=16, k=2, F=256, seed=19),
+    # Base-1 hidden and latent widths: the dense weight gradients dW_up [d, L]
+    # and dW_dn [L, d] then take the 256 x 192 tiles
+    "wide": MoEConfig("wide", T=64, d=6656, L=3072, E=8, k=2, F=256, seed=21),
 }
 
 
