@@ -717,9 +717,11 @@ inline int persistent_grid(int64_t tiles_upper_bound) {
 //   Stream : 128 x 256, BK 64, 2 x 4 waves, 3 stages (144 KB), non-temporal
 //            weight loads -- few rows per expert, HBM-bound weight streaming
 //   Big    : 256 x 256, BK 64, 2 x 4 waves, 2 stages (128 KB) -- MFMA-bound
-//   Mid    : 128 x 256, BK 64, 2 x 4 waves, 3 stages -- dense GEMMs too small
-//            to give every CU two 256 x 256 tiles
-//   Wide   : below
+//   Mid    : 128 x 256, BK 64, 2 x 4 waves, 3 stages -- smaller dense GEMMs
+//            and the routing GEMM at mid and small batches
+//   Wide   : 256 x 192 (below)
+// (the dense GEMMs choose among Big, Wide and Mid by rounds x tile area /
+// efficiency)
 template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool BNT>
 struct TileCfg {
   static constexpr int bm = BM, bn = BN, bk = BK, wm = WM, wn = WN, nstage = NSTAGE;
@@ -729,8 +731,8 @@ using TileStream = TileCfg<128, 256, 64, 2, 4, 3, true>;
 using TileBig = TileCfg<256, 256, 64, 2, 4, 2, false>;
 using TileMid = TileCfg<128, 256, 64, 2, 4, 3, false>;
 // Wide : 256 x 192, BK 64, 4 x 2 waves (64 x 96 each), 2 stages (112 KB) --
-//        dense GEMMs whose 256 x 192 tiles fill the chip exactly once (e.g.
-//        M 4,096 x N 3,072: 256 tiles), where 128 x 256 tiles take 1.5 waves
+//        e.g. M 4,096 x N 3,072: 256 tiles fill the chip exactly once, where
+//        128 x 256 tiles take 1.5 waves
 using TileWide = TileCfg<256, 192, 64, 4, 2, 2, false>;
 
 template <class C, bool GROUPED, bool GATHER, int EPI, int NSEG = 1, int F8 = F8_NONE,
