@@ -10,9 +10,13 @@ grouped gate/up GEMM) measured with HIP events recorded by the library around
 that kernel on the stream it runs on, per-kernel average times, and the CPU
 oracle timed on a bounded sample of the same workload.
 
-Default workload: the MAI-Base-1-shaped layer at T=4,096 tokens (d=6,656,
+Default workload: the MAI-Base-1-shaped layer at T=32,768 tokens (d=6,656,
 latent 3,072, 512 experts, top-8, SwiGLU width 10,240; bf16 operands, fp32
-accumulation), all 512 experts resident (~97 GB of expert weights).
+accumulation; ~512 routed rows per expert, compute-bound), all 512 experts
+resident (~97 GB of expert weights).  The same layer at T=4,096 tokens
+(small batch, bound by streaming the weights from HBM) is timed in the same
+run on the same weights (its x is the first 4,096 tokens) and reported under
+"secondary", with its own roofline.
 """
 from __future__ import annotations
 
@@ -46,7 +50,10 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default=None,
-                   help="workload (default: base1_small_batch; base1_ep8 with --backward)")
+                   help="workload (default: base1_compute; base1_ep8 with --backward)")
+    p.add_argument("--secondary", default="base1_small_batch",
+                   help="a second workload with the same weights and a smaller batch, timed in "
+                        "the same run and reported under 'secondary' ('none' to skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--fp8", action="store_true",
                    help="routed experts' GEMMs in FP8 E4M3 with delayed scaling (not the headline "
@@ -135,14 +142,15 @@ def layer_bytes(cfg, touched, esize=2):
     return w + T * d * 2.0 + T * d * 4.0
 
 
-def cpu_baseline(cfg, n_tok=4096, n_exp=192, seed=0, fp8=False, reps=3):
+def cpu_baseline(cfg, n_tok=4096, n_exp=192, rows_budget=12288, seed=0, fp8=False, reps=3):
     """The oracle (float64 numpy, as it stands) on a bounded sample of the
     workload, extrapolated to tokens/s of the whole layer:
       router + permutation over all T tokens (timed in full),
       latent down, combine and up-projection on n_tok tokens (x T/n_tok),
-      n_exp experts' SwiGLU FFNs on their routed rows (x E/n_exp), each
-      timed reps times (the mean is used: ~10 s of timed work at Base-1
-      T = 4,096 without generating more weights).
+      randomly drawn experts' SwiGLU FFNs on their routed rows, up to n_exp
+      experts or rows_budget rows (x all T*k rows / the rows done), each
+      timed reps times (the mean is used: ~10-20 s of timed work on the
+      Base-1 shapes: 192 experts at T = 4,096, ~24 at T = 32,768).
     Input generation is not timed.  fp8: the experts in the oracle's
     fp8_operands mode (scales from the sample's own ranges)."""
     import numpy as np
@@ -179,7 +187,10 @@ def cpu_baseline(cfg, n_tok=4096, n_exp=192, seed=0, fp8=False, reps=3):
     t_tok = time.perf_counter() - t0
     counts = p["expert_counts"]
     nonempty = np.nonzero(counts)[0]
-    sample = rng.choice(nonempty, size=min(n_exp, nonempty.size), replace=False)
+    order = rng.permutation(nonempty)
+    csum = np.cumsum(counts[order])
+    n_take = min(n_exp, int(np.searchsorted(csum, rows_budget)) + 1, order.size)
+    sample = order[:n_take]
     t_exp = 0.0
     t_gen = 0.0
     rows_done = 0
@@ -330,37 +341,28 @@ def bench_backward(args, cfg, dev):
     print(json.dumps(line), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1).", file=sys.stderr)
-        sys.exit(2)
+def same_weights(a, b):
+    """Two workloads whose weights are the same tensors (same shapes, seed and
+    router bias): the generator keys every tensor by (seed, tensor), so their
+    weights are bit-identical and x of the smaller batch is the first rows of
+    the larger one's."""
+    return (a.d, a.L, a.E, a.k, a.F, a.Fs, a.zipf_bias, a.seed) == \
+        (b.d, b.L, b.E, b.k, b.F, b.Fs, b.zipf_bias, b.seed)
+
+
+def time_forward(args, cfg, w, x, dev, w8=None):
+    """Warm up, then time args.steps forward passes of workload cfg on one
+    stream with inputs resident in HBM; per-kernel HIP events are recorded by
+    the library around each kernel on that stream.  Returns the result
+    fields of one workload (without the CPU baseline)."""
     import numpy as np
     import torch
 
     import mixture_experts_layer_moe_amd as moe
-    from moe_synth import CONFIGS, device
-
-    if args.config is None:
-        args.config = "base1_ep8" if args.backward else "base1_small_batch"
-    cfg = CONFIGS[args.config]
-    dev = torch.device("cuda:0")
-    if args.backward:
-        return bench_backward(args, cfg, dev)
-    print(f"[bench] {cfg.description}; generating inputs on the GPU", file=sys.stderr, flush=True)
-    dv = device.device_inputs(cfg, dev)
-    w = moe.LatentMoEWeights(dv["w_router"], dv["b_router"], dv["w_dn"], dv["w_gate"], dv["w_up"],
-                             dv["w_down"], dv["w_lat_up"], dv.get("ws_gate"), dv.get("ws_up"),
-                             dv.get("ws_down"))
     buf = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, cfg.Fs, device=dev)
-    x = dv["x"]
     step = lambda: moe.forward(x, w, cfg.k, buf)  # noqa: E731
     rounds_info = None
     if args.capacity > 0:
-        if args.fp8:
-            print("--capacity runs the bf16 experts only", file=sys.stderr)
-            sys.exit(2)
         cap = max(1, int(round(args.capacity * cfg.T * cfg.k / cfg.E)))
         gs = min(args.group_size, cfg.E)
         nb = moe.moe_workspace_bytes_rounds(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, cfg.Fs, cap,
@@ -370,36 +372,18 @@ def main():
         rounds_info = {"capacity": cap, "group_size": gs, "workspace_bytes": nb}
         step = lambda: moe.forward_rounds(x, w, cfg.k, buf, cap, gs, ws_rounds=ws_r,  # noqa: E731
                                           rounds_out=rounds_t)
-    if args.fp8:
-        # weights quantized once (448 / amax per expert matrix); the bf16
-        # expert weights are then dropped; activation scales are delayed:
-        # each step uses the history of the previous steps' maxima
-        w8 = moe.quantize_experts(w)
-        torch.cuda.synchronize()
-        w.w_gate = w.w_up = w.w_down = None
-        for n in ("w_gate", "w_up", "w_down"):
-            del dv[n]
-        torch.cuda.empty_cache()
+    if w8 is not None:
         scaling = moe.Fp8Scaling(hist_len=1024, device=dev)
         step = lambda: moe.forward_fp8(x, w, w8, cfg.k, buf, scaling)  # noqa: E731
     torch.cuda.synchronize()
-
-    if args.copy_calibration:
-        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            device.calibration_copy(src, dst)   # one dispatch: 1 GiB read + 1 GiB written
-        torch.cuda.synchronize()
-        del src, dst
-
-    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    print(f"[bench] {cfg.name}: warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     hip = HipEvents()
     ev = {name: [(hip.create(), hip.create()) for _ in range(args.steps)] for name in KERNEL_NAMES}
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] {cfg.name}: timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -421,31 +405,111 @@ def main():
 
     elapsed = t1 - t0
     ms_per_step = elapsed / args.steps * 1e3
-    value = cfg.T * args.steps / elapsed
     counts = buf.expert_counts.cpu().numpy()
-    esize = 1 if args.fp8 else 2
-    mfma_peak = MFMA_FP8_PEAK if args.fp8 else MFMA_BF16_PEAK
+    fp8 = w8 is not None
+    esize = 1 if fp8 else 2
+    mfma_peak = MFMA_FP8_PEAK if fp8 else MFMA_BF16_PEAK
     flops, nbytes, touched = dominant_work(cfg, counts, esize)
     dom_s = kern_ms[DOMINANT] * 1e-3
-    ai = flops / nbytes
-    if ai < mfma_peak / HBM_PEAK:
+    if flops / nbytes < mfma_peak / HBM_PEAK:
         roof = {"bound": "hbm", "achieved": nbytes / dom_s / 1e9, "peak": HBM_PEAK / 1e9,
                 "unit": "GB/s"}
     else:
         roof = {"bound": "mfma", "achieved": flops / dom_s / 1e12, "peak": mfma_peak / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = stored_traffic(cfg.name + ("_fp8" if args.fp8 else ""))
+    roof["traffic"] = stored_traffic(cfg.name + ("_fp8" if fp8 else ""))
     roof["kernel"] = ("grouped gate/up GEMM + SwiGLU (gemm_kernel GROUPED GATHER EPI_SWIGLU"
-                      + (" FP8 E4M3, E4M3 output)" if args.fp8 else ")"))
-    roof["algorithmic_per_launch"] = {"flops": flops, "bytes": nbytes, "experts_touched": touched}
+                      + (" FP8 E4M3, E4M3 output)" if fp8 else ")"))
+    roof["algorithmic_per_launch"] = {"flops": flops, "bytes": nbytes, "experts_touched": touched,
+                                      "mean_launch_ms": kern_ms[DOMINANT]}
 
     step_s = ms_per_step * 1e-3
+    lb = layer_bytes(cfg, touched, esize)
+    lf = cfg.flops()
+    # the whole layer against the roofline of its own arithmetic intensity
+    layer_bound = "hbm" if lf / lb < mfma_peak / HBM_PEAK else "mfma"
     layer = {
-        "mfma_frac": cfg.flops() / step_s / mfma_peak,
-        "hbm_frac": layer_bytes(cfg, touched, esize) / step_s / HBM_PEAK,
+        "bound": layer_bound,
+        "frac": (lb / step_s / HBM_PEAK) if layer_bound == "hbm" else (lf / step_s / mfma_peak),
+        "mfma_frac": lf / step_s / mfma_peak,
+        "hbm_frac": lb / step_s / HBM_PEAK,
+        "algorithmic": {"flops": lf, "bytes": lb},
         "kernels_ms": {k: (None if v is None else round(v, 4)) for k, v in kern_ms.items()},
     }
+    res = {"workload": cfg.description, "value": cfg.T * args.steps / elapsed,
+           "ms_per_step": ms_per_step, "roofline": roof, "layer": layer,
+           "config": {"workload": cfg.description, "name": cfg.name, "T": cfg.T, "d": cfg.d,
+                      "latent": cfg.L, "experts": cfg.E, "top_k": cfg.k, "ffn": cfg.F,
+                      "shared_ffn": cfg.Fs, "seed": cfg.seed}}
+    if rounds_info is not None:
+        rounds_info["rounds"] = int(rounds_t.item())
+        res["config"]["multi_round"] = rounds_info
+        res["roofline"] = None   # the gate/up events bracket every round of both GEMMs
+    del buf
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mixture_experts_layer_moe_amd as moe
+    from moe_synth import CONFIGS, device
+
+    if args.config is None:
+        args.config = "base1_ep8" if args.backward else "base1_compute"
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    if args.backward:
+        return bench_backward(args, cfg, dev)
+    if args.capacity > 0 and args.fp8:
+        print("--capacity runs the bf16 experts only", file=sys.stderr)
+        sys.exit(2)
+    sec = None
+    if args.secondary and args.secondary != "none":
+        sec = CONFIGS[args.secondary]
+        if not same_weights(cfg, sec) or sec.T > cfg.T:
+            print(f"[bench] secondary workload {sec.name} does not share {cfg.name}'s weights "
+                  f"and batch; not timed", file=sys.stderr)
+            sec = None
+    print(f"[bench] {cfg.description}; generating inputs on the GPU", file=sys.stderr, flush=True)
+    dv = device.device_inputs(cfg, dev)
+    w = moe.LatentMoEWeights(dv["w_router"], dv["b_router"], dv["w_dn"], dv["w_gate"], dv["w_up"],
+                             dv["w_down"], dv["w_lat_up"], dv.get("ws_gate"), dv.get("ws_up"),
+                             dv.get("ws_down"))
+    x = dv["x"]
+    w8 = None
+    if args.fp8:
+        # weights quantized once (448 / amax per expert matrix); the bf16
+        # expert weights are then dropped; activation scales are delayed:
+        # each step uses the history of the previous steps' maxima
+        w8 = moe.quantize_experts(w)
+        torch.cuda.synchronize()
+        w.w_gate = w.w_up = w.w_down = None
+        for n in ("w_gate", "w_up", "w_down"):
+            del dv[n]
+        torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            device.calibration_copy(src, dst)   # one dispatch: 1 GiB read + 1 GiB written
+        torch.cuda.synchronize()
+        del src, dst
+
+    main_res = time_forward(args, cfg, w, x, dev, w8)
+    sec_res = None
+    if sec is not None:
+        # the smaller batch: the first sec.T tokens (bit-identical to that
+        # workload's own x), same weights, its own buffers and timing
+        sec_res = time_forward(args, sec, w, x[:sec.T], dev, w8)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -453,20 +517,18 @@ def main():
         cpu = cpu_baseline(cfg, fp8=args.fp8)
 
     line = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None,
+        "metric": METRIC, "value": main_res["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3 (expert GEMMs; bf16 latent projections)" if args.fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.description, "T": cfg.T, "d": cfg.d, "latent": cfg.L,
-                   "experts": cfg.E, "top_k": cfg.k, "ffn": cfg.F, "shared_ffn": cfg.Fs,
-                   "seed": cfg.seed},
-        "roofline": roof, "layer": layer, "cpu_baseline": cpu,
+        "config": main_res["config"],
+        "roofline": main_res["roofline"], "layer": main_res["layer"], "cpu_baseline": cpu,
     }
-    if rounds_info is not None:
-        rounds_info["rounds"] = int(rounds_t.item())
-        line["config"]["multi_round"] = rounds_info
-        line["roofline"] = None   # the gate/up events bracket every round of both GEMMs
+    if sec_res is not None:
+        line["secondary"] = {k: sec_res[k] for k in ("workload", "value", "ms_per_step",
+                                                     "roofline", "layer", "config")}
+        line["secondary"]["unit"] = "tokens/s"
     print(json.dumps(line), flush=True)
 
 

@@ -100,7 +100,13 @@ def load():
 
 
 def _ptr(t):
-    return None if t is None else t.data_ptr()
+    """Device address of a tensor argument (evaluated after every shape check
+    of the call, right before the C entry point runs)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"tensor arguments must be GPU tensors, got one on {t.device}")
+    return t.data_ptr()
 
 
 def _nbytes(t):
@@ -118,17 +124,45 @@ def _check(fn, code):
         raise MoEError(fn, code)
 
 
-def _need(t, name, dtype, ndim=None):
+def _need(t, name, dtype, ndim=None, shape=None):
+    """Checks a tensor argument: dtype, contiguity, dims, shape (a tuple of
+    ints, None = any extent).  The C ABI receives only pointers and sizes and
+    cannot check extents itself, and a buffer shorter than the sizes imply
+    would be read or written out of bounds.  That every tensor lives on the
+    GPU is checked by _ptr, after all shape checks of a call."""
     if t is None:
         return
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(w) != g
+                                        for g, w in zip(t.shape, shape)):
+            want = tuple("*" if w is None else int(w) for w in shape)
+            raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
+
+
+def _numel(t, name, n):
+    """A flat buffer argument must hold exactly n values."""
+    if t is not None and t.numel() != int(n):
+        raise ValueError(f"{name} must hold {int(n)} values, got {t.numel()}")
+
+
+def _dims2(t, name):
+    if t is None or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor, got "
+                         f"{None if t is None else tuple(t.shape)}")
+    return int(t.shape[0]), int(t.shape[1])
+
+
+def _dims3(t, name):
+    if t is None or t.dim() != 3:
+        raise ValueError(f"{name} must be a 3-D tensor, got "
+                         f"{None if t is None else tuple(t.shape)}")
+    return int(t.shape[0]), int(t.shape[1]), int(t.shape[2])
 
 
 def moe_workspace_bytes(op, T, d, L, E, k, F, Fs=0):
@@ -145,16 +179,21 @@ def moe_set_kernel_events(kernel, start_event, stop_event):
     _check("moe_set_kernel_events", load().moe_set_kernel_events(kid, start_event, stop_event))
 
 
+def _route_args(x, w_router, b_router, k, topk_idx, topk_w, logits_out):
+    T, d = _dims2(x, "x")
+    E = _dims2(w_router, "w_router")[0]
+    _need(x, "x", torch.bfloat16, shape=(T, d))
+    _need(w_router, "w_router", torch.float32, shape=(E, d))
+    _need(b_router, "b_router", torch.float32, shape=(E,))
+    _need(topk_idx, "topk_idx", torch.int32, shape=(T, k))
+    _need(topk_w, "topk_w", torch.float32, shape=(T, k))
+    _need(logits_out, "logits_out", torch.float32, shape=(T, E))
+    return T, d, E
+
+
 def moe_route(x, w_router, b_router, k, topk_idx, topk_w, logits_out=None, ws=None, stream=None):
-    _need(x, "x", torch.bfloat16, 2)
-    _need(w_router, "w_router", torch.float32, 2)
-    _need(b_router, "b_router", torch.float32, 1)
-    _need(topk_idx, "topk_idx", torch.int32, 2)
-    _need(topk_w, "topk_w", torch.float32, 2)
-    _need(logits_out, "logits_out", torch.float32, 2)
+    T, d, E = _route_args(x, w_router, b_router, k, topk_idx, topk_w, logits_out)
     _need(ws, "ws", torch.uint8, 1)
-    T, d = x.shape
-    E = w_router.shape[0]
     _check("moe_route", load().moe_route(_ptr(x), _ptr(w_router), _ptr(b_router), T, d, E, k,
                                          _ptr(topk_idx), _ptr(topk_w), _ptr(logits_out), _ptr(ws),
                                          _nbytes(ws), _stream(stream)))
@@ -162,16 +201,9 @@ def moe_route(x, w_router, b_router, k, topk_idx, topk_w, logits_out=None, ws=No
 
 def moe_route_ex(x, w_router, b_router, bias_mode, k, topk_idx, topk_w, logits_out=None,
                  prob_sum=None, ws=None, stream=None):
-    _need(x, "x", torch.bfloat16, 2)
-    _need(w_router, "w_router", torch.float32, 2)
-    _need(b_router, "b_router", torch.float32, 1)
-    _need(topk_idx, "topk_idx", torch.int32, 2)
-    _need(topk_w, "topk_w", torch.float32, 2)
-    _need(logits_out, "logits_out", torch.float32, 2)
-    _need(prob_sum, "prob_sum", torch.float32, 1)
+    T, d, E = _route_args(x, w_router, b_router, k, topk_idx, topk_w, logits_out)
+    _need(prob_sum, "prob_sum", torch.float32, shape=(E,))
     _need(ws, "ws", torch.uint8, 1)
-    T, d = x.shape
-    E = w_router.shape[0]
     _check("moe_route_ex", load().moe_route_ex(
         _ptr(x), _ptr(w_router), _ptr(b_router), int(bias_mode), T, d, E, k, _ptr(topk_idx),
         _ptr(topk_w), _ptr(logits_out), _ptr(prob_sum), _ptr(ws), _nbytes(ws), _stream(stream)))
@@ -179,31 +211,51 @@ def moe_route_ex(x, w_router, b_router, bias_mode, k, topk_idx, topk_w, logits_o
 
 def moe_permute(topk_idx, E, expert_counts, expert_offsets, row_token, assign_row, ws,
                 stream=None):
-    _need(topk_idx, "topk_idx", torch.int32, 2)
-    for n, t in (("expert_counts", expert_counts), ("expert_offsets", expert_offsets),
-                 ("row_token", row_token), ("assign_row", assign_row)):
+    T, k = _dims2(topk_idx, "topk_idx")
+    E = int(E)
+    _need(topk_idx, "topk_idx", torch.int32, shape=(T, k))
+    for n, t, cnt in (("expert_counts", expert_counts, E), ("expert_offsets", expert_offsets, E + 1),
+                      ("row_token", row_token, T * k), ("assign_row", assign_row, T * k)):
+        _numel(t, n, cnt)
         _need(t, n, torch.int32)
     _need(ws, "ws", torch.uint8, 1)
-    T, k = topk_idx.shape
     _check("moe_permute", load().moe_permute(_ptr(topk_idx), T, k, E, _ptr(expert_counts),
                                              _ptr(expert_offsets), _ptr(row_token),
                                              _ptr(assign_row), _ptr(ws), _nbytes(ws),
                                              _stream(stream)))
 
 
+def _ffn_args(x, w_lat_down, expert_offsets, row_token, w_gate, w_up, w_down, ws_gate, ws_up, k,
+              y_rows, hs, wdtype):
+    """Shapes of the latent-FFN entry points: T, d from x, L from W_dn, E, F
+    from W_g, Fs from Ws_g; every other buffer must agree."""
+    T, d = _dims2(x, "x")
+    L = _dims2(w_lat_down, "w_lat_down")[0]
+    E, F, _ = _dims3(w_gate, "w_gate")
+    Fs = 0 if ws_gate is None else _dims2(ws_gate, "ws_gate")[0]
+    _need(x, "x", torch.bfloat16, shape=(T, d))
+    _need(w_lat_down, "w_lat_down", torch.bfloat16, shape=(L, d))
+    _need(w_gate, "w_gate", wdtype, shape=(E, F, L))
+    _need(w_up, "w_up", wdtype, shape=(E, F, L))
+    _need(w_down, "w_down", wdtype, shape=(E, L, F))
+    if (ws_up is None) != (ws_gate is None) or (Fs > 0 and hs is None):
+        raise ValueError("ws_gate, ws_up and hs are given together (a shared expert) or not at all")
+    _need(ws_gate, "ws_gate", torch.bfloat16, shape=(Fs, d))
+    _need(ws_up, "ws_up", torch.bfloat16, shape=(Fs, d))
+    _need(hs, "hs", torch.bfloat16, shape=(T, Fs))
+    _numel(expert_offsets, "expert_offsets", E + 1)
+    _need(expert_offsets, "expert_offsets", torch.int32, 1)
+    _numel(row_token, "row_token", T * int(k))
+    _need(row_token, "row_token", torch.int32, 1)
+    _need(y_rows, "y_rows", torch.float32, shape=(T * int(k), L))
+    return T, d, L, E, F, Fs
+
+
 def moe_latent_ffn_forward(x, w_lat_down, expert_offsets, row_token, w_gate, w_up, w_down,
                            ws_gate, ws_up, k, y_rows, hs, ws, stream=None):
-    for n, t in (("x", x), ("w_lat_down", w_lat_down), ("w_gate", w_gate), ("w_up", w_up),
-                 ("w_down", w_down), ("ws_gate", ws_gate), ("ws_up", ws_up), ("hs", hs)):
-        _need(t, n, torch.bfloat16)
-    _need(expert_offsets, "expert_offsets", torch.int32, 1)
-    _need(row_token, "row_token", torch.int32, 1)
-    _need(y_rows, "y_rows", torch.float32, 2)
+    T, d, L, E, F, Fs = _ffn_args(x, w_lat_down, expert_offsets, row_token, w_gate, w_up, w_down,
+                                  ws_gate, ws_up, k, y_rows, hs, torch.bfloat16)
     _need(ws, "ws", torch.uint8, 1)
-    T, d = x.shape
-    L = w_lat_down.shape[0]
-    E, F = w_gate.shape[0], w_gate.shape[1]
-    Fs = 0 if ws_gate is None else ws_gate.shape[0]
     _check("moe_latent_ffn_forward", load().moe_latent_ffn_forward(
         _ptr(x), _ptr(w_lat_down), _ptr(expert_offsets), _ptr(row_token), _ptr(w_gate),
         _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), T, d, L, E, k, F, Fs, _ptr(y_rows),
@@ -211,16 +263,19 @@ def moe_latent_ffn_forward(x, w_lat_down, expert_offsets, row_token, w_gate, w_u
 
 
 def moe_combine(y_rows, topk_w, assign_row, w_lat_up, hs, ws_down, out, ws, stream=None):
-    _need(y_rows, "y_rows", torch.float32, 2)
-    _need(topk_w, "topk_w", torch.float32, 2)
-    _need(assign_row, "assign_row", torch.int32, 2)
-    for n, t in (("w_lat_up", w_lat_up), ("hs", hs), ("ws_down", ws_down)):
-        _need(t, n, torch.bfloat16)
-    _need(out, "out", torch.float32, 2)
+    T, k = _dims2(topk_w, "topk_w")
+    d, L = _dims2(w_lat_up, "w_lat_up")
+    Fs = 0 if ws_down is None else _dims2(ws_down, "ws_down")[1]
+    if (hs is None) != (ws_down is None):
+        raise ValueError("hs and ws_down are given together (a shared expert) or not at all")
+    _need(y_rows, "y_rows", torch.float32, shape=(T * k, L))
+    _need(topk_w, "topk_w", torch.float32, shape=(T, k))
+    _need(assign_row, "assign_row", torch.int32, shape=(T, k))
+    _need(w_lat_up, "w_lat_up", torch.bfloat16, shape=(d, L))
+    _need(hs, "hs", torch.bfloat16, shape=(T, Fs))
+    _need(ws_down, "ws_down", torch.bfloat16, shape=(d, Fs))
+    _need(out, "out", torch.float32, shape=(T, d))
     _need(ws, "ws", torch.uint8, 1)
-    T, k = topk_w.shape
-    d, L = w_lat_up.shape
-    Fs = 0 if ws_down is None else ws_down.shape[1]
     _check("moe_combine", load().moe_combine(_ptr(y_rows), _ptr(topk_w), _ptr(assign_row),
                                              _ptr(w_lat_up), _ptr(hs), _ptr(ws_down), T, d, L, k,
                                              Fs, _ptr(out), _ptr(ws), _nbytes(ws),
@@ -229,30 +284,35 @@ def moe_combine(y_rows, topk_w, assign_row, w_lat_up, hs, ws_down, out, ws, stre
 
 def moe_fp8_amax(src, ntensor, amax, stream=None):
     """amax[t] = max |src_t| for ntensor equal bf16 tensors stored back to back in src."""
+    ntensor = int(ntensor)
+    if ntensor < 0 or (ntensor and src.numel() % ntensor):
+        raise ValueError(f"src ({src.numel()} values) does not split into {ntensor} tensors")
     _need(src, "src", torch.bfloat16)
-    _need(amax, "amax", torch.float32, 1)
-    _check("moe_fp8_amax", load().moe_fp8_amax(_ptr(src), int(ntensor), src.numel() // max(ntensor, 1),
+    _need(amax, "amax", torch.float32, shape=(ntensor,))
+    _check("moe_fp8_amax", load().moe_fp8_amax(_ptr(src), ntensor, src.numel() // max(ntensor, 1),
                                                _ptr(amax), _stream(stream)))
 
 
 def moe_fp8_quantize(src, ntensor, scale, dst, stream=None):
     """dst = e4m3(src_t * scale[t]) bytes (uint8) for ntensor equal bf16 tensors."""
+    ntensor = int(ntensor)
+    if ntensor < 0 or (ntensor and src.numel() % ntensor):
+        raise ValueError(f"src ({src.numel()} values) does not split into {ntensor} tensors")
     _need(src, "src", torch.bfloat16)
-    _need(scale, "scale", torch.float32, 1)
+    _need(scale, "scale", torch.float32, shape=(ntensor,))
+    _numel(dst, "dst", src.numel())
     _need(dst, "dst", torch.uint8)
-    if dst.numel() != src.numel():
-        raise ValueError("dst must have one byte per src value")
     _check("moe_fp8_quantize", load().moe_fp8_quantize(
-        _ptr(src), int(ntensor), src.numel() // max(ntensor, 1), _ptr(scale), _ptr(dst),
+        _ptr(src), ntensor, src.numel() // max(ntensor, 1), _ptr(scale), _ptr(dst),
         _stream(stream)))
 
 
 def moe_fp8_scale_update(history, amax, slot, scale, stream=None):
     """history [n, H] fp32: history[:, slot] = amax; scale = 448 / max over the history."""
-    _need(history, "history", torch.float32, 2)
-    _need(amax, "amax", torch.float32, 1)
-    _need(scale, "scale", torch.float32, 1)
-    n, H = history.shape
+    n, H = _dims2(history, "history")
+    _need(history, "history", torch.float32, shape=(n, H))
+    _need(amax, "amax", torch.float32, shape=(n,))
+    _need(scale, "scale", torch.float32, shape=(n,))
     _check("moe_fp8_scale_update", load().moe_fp8_scale_update(
         _ptr(history), _ptr(amax), n, H, int(slot), _ptr(scale), _stream(stream)))
 
@@ -260,22 +320,12 @@ def moe_fp8_scale_update(history, amax, slot, scale, stream=None):
 def moe_latent_ffn_forward_fp8(x, w_lat_down, expert_offsets, row_token, w_gate, w_up, w_down,
                                w_scale, act_scale, ws_gate, ws_up, k, y_rows, hs, act_amax, ws,
                                stream=None):
-    for n, t in (("x", x), ("w_lat_down", w_lat_down), ("ws_gate", ws_gate), ("ws_up", ws_up),
-                 ("hs", hs)):
-        _need(t, n, torch.bfloat16)
-    for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
-        _need(t, n, torch.uint8, 3)
-    _need(w_scale, "w_scale", torch.float32, 1)
-    _need(act_scale, "act_scale", torch.float32, 1)
-    _need(act_amax, "act_amax", torch.float32, 1)
-    _need(expert_offsets, "expert_offsets", torch.int32, 1)
-    _need(row_token, "row_token", torch.int32, 1)
-    _need(y_rows, "y_rows", torch.float32, 2)
+    T, d, L, E, F, Fs = _ffn_args(x, w_lat_down, expert_offsets, row_token, w_gate, w_up, w_down,
+                                  ws_gate, ws_up, k, y_rows, hs, torch.uint8)
+    _need(w_scale, "w_scale", torch.float32, shape=(3 * E,))
+    _need(act_scale, "act_scale", torch.float32, shape=(2,))
+    _need(act_amax, "act_amax", torch.float32, shape=(2,))
     _need(ws, "ws", torch.uint8, 1)
-    T, d = x.shape
-    L = w_lat_down.shape[0]
-    E, F = w_gate.shape[0], w_gate.shape[1]
-    Fs = 0 if ws_gate is None else ws_gate.shape[0]
     _check("moe_latent_ffn_forward_fp8", load().moe_latent_ffn_forward_fp8(
         _ptr(x), _ptr(w_lat_down), _ptr(expert_offsets), _ptr(row_token), _ptr(w_gate),
         _ptr(w_up), _ptr(w_down), _ptr(w_scale), _ptr(act_scale), _ptr(ws_gate), _ptr(ws_up), T,
@@ -290,18 +340,12 @@ def moe_workspace_bytes_rounds(T, d, L, E, k, F, Fs, capacity, group_size):
 def moe_latent_ffn_forward_rounds(x, w_lat_down, expert_offsets, row_token, w_gate, w_up, w_down,
                                   ws_gate, ws_up, k, capacity, group_size, y_rows, hs, rounds_out,
                                   ws, stream=None):
-    for n, t in (("x", x), ("w_lat_down", w_lat_down), ("w_gate", w_gate), ("w_up", w_up),
-                 ("w_down", w_down), ("ws_gate", ws_gate), ("ws_up", ws_up), ("hs", hs)):
-        _need(t, n, torch.bfloat16)
-    _need(expert_offsets, "expert_offsets", torch.int32, 1)
-    _need(row_token, "row_token", torch.int32, 1)
-    _need(y_rows, "y_rows", torch.float32, 2)
+    T, d, L, E, F, Fs = _ffn_args(x, w_lat_down, expert_offsets, row_token, w_gate, w_up, w_down,
+                                  ws_gate, ws_up, k, y_rows, hs, torch.bfloat16)
+    if rounds_out is not None and rounds_out.numel() < 1:
+        raise ValueError("rounds_out must hold one value")
     _need(rounds_out, "rounds_out", torch.int32)
     _need(ws, "ws", torch.uint8, 1)
-    T, d = x.shape
-    L = w_lat_down.shape[0]
-    E, F = w_gate.shape[0], w_gate.shape[1]
-    Fs = 0 if ws_gate is None else ws_gate.shape[0]
     _check("moe_latent_ffn_forward_rounds", load().moe_latent_ffn_forward_rounds(
         _ptr(x), _ptr(w_lat_down), _ptr(expert_offsets), _ptr(row_token), _ptr(w_gate),
         _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), T, d, L, E, k, F, Fs,
@@ -311,41 +355,64 @@ def moe_latent_ffn_forward_rounds(x, w_lat_down, expert_offsets, row_token, w_ga
 
 def moe_backward_prepare(w_lat_down, w_gate, w_up, w_down, w_lat_up, w_lat_down_t, w_gate_t,
                          w_up_t, w_down_t, w_lat_up_t, stream=None):
-    for n, t in (("w_lat_down", w_lat_down), ("w_gate", w_gate), ("w_up", w_up),
-                 ("w_down", w_down), ("w_lat_up", w_lat_up), ("w_lat_down_t", w_lat_down_t),
-                 ("w_gate_t", w_gate_t), ("w_up_t", w_up_t), ("w_down_t", w_down_t),
-                 ("w_lat_up_t", w_lat_up_t)):
-        _need(t, n, torch.bfloat16)
-    E, F, L = w_gate.shape
-    d = w_lat_up.shape[0]
+    E, F, L = _dims3(w_gate, "w_gate")
+    d = _dims2(w_lat_up, "w_lat_up")[0]
+    for n, t, shp in (("w_lat_down", w_lat_down, (L, d)), ("w_gate", w_gate, (E, F, L)),
+                      ("w_up", w_up, (E, F, L)), ("w_down", w_down, (E, L, F)),
+                      ("w_lat_up", w_lat_up, (d, L)), ("w_lat_down_t", w_lat_down_t, (d, L)),
+                      ("w_gate_t", w_gate_t, (E, L, F)), ("w_up_t", w_up_t, (E, L, F)),
+                      ("w_down_t", w_down_t, (E, F, L)), ("w_lat_up_t", w_lat_up_t, (L, d))):
+        if t is None:
+            raise ValueError(f"{n} is required")
+        _need(t, n, torch.bfloat16, shape=shp)
     _check("moe_backward_prepare", load().moe_backward_prepare(
         _ptr(w_lat_down), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(w_lat_up), d, L, E, F,
         _ptr(w_lat_down_t), _ptr(w_gate_t), _ptr(w_up_t), _ptr(w_down_t), _ptr(w_lat_up_t),
         _stream(stream)))
 
 
+def _bwd_args(x, w_router, router_logits, topk_idx, topk_w, expert_offsets, row_token,
+              assign_row, y_rows, w_lat_down, w_gate, w_up, w_lat_down_t, w_lat_up_t, g_out, dx,
+              dw_router, db_router, dw_lat_down, dw_gate, dw_up, dw_down, dw_lat_up, dtopk_w):
+    """Shapes of the backward entry points: T, d from x, E, F, L from W_g, k
+    from topk_idx; every other buffer must agree."""
+    T, d = _dims2(x, "x")
+    E, F, L = _dims3(w_gate, "w_gate")
+    k = _dims2(topk_idx, "topk_idx")[1]
+    _need(x, "x", torch.bfloat16, shape=(T, d))
+    f32 = (("w_router", w_router, (E, d)), ("router_logits", router_logits, (T, E)),
+           ("topk_w", topk_w, (T, k)), ("y_rows", y_rows, (T * k, L)), ("g_out", g_out, (T, d)),
+           ("dx", dx, (T, d)), ("dw_router", dw_router, (E, d)), ("db_router", db_router, (E,)),
+           ("dw_lat_down", dw_lat_down, (L, d)), ("dw_gate", dw_gate, (E, F, L)),
+           ("dw_up", dw_up, (E, F, L)), ("dw_down", dw_down, (E, L, F)),
+           ("dw_lat_up", dw_lat_up, (d, L)), ("dtopk_w", dtopk_w, (T, k)))
+    for n, t, shp in f32:
+        _need(t, n, torch.float32, shape=shp)
+    _need(topk_idx, "topk_idx", torch.int32, shape=(T, k))
+    _need(assign_row, "assign_row", torch.int32, shape=(T, k))
+    _numel(expert_offsets, "expert_offsets", E + 1)
+    _need(expert_offsets, "expert_offsets", torch.int32, 1)
+    _numel(row_token, "row_token", T * k)
+    _need(row_token, "row_token", torch.int32, 1)
+    for n, t, shp in (("w_lat_down", w_lat_down, (L, d)), ("w_gate", w_gate, (E, F, L)),
+                      ("w_up", w_up, (E, F, L)), ("w_lat_down_t", w_lat_down_t, (d, L)),
+                      ("w_lat_up_t", w_lat_up_t, (L, d))):
+        _need(t, n, torch.bfloat16, shape=shp)
+    return T, d, L, E, k, F
+
+
 def moe_backward(x, w_router, router_logits, bias_mode, topk_idx, topk_w, expert_offsets,
                  row_token, assign_row, y_rows, w_lat_down, w_gate, w_up, w_lat_down_t, w_gate_t,
                  w_up_t, w_down_t, w_lat_up_t, g_out, rounding, seed, dx, dw_router, db_router,
                  dw_lat_down, dw_gate, dw_up, dw_down, dw_lat_up, dtopk_w, ws, stream=None):
-    _need(x, "x", torch.bfloat16, 2)
-    for n, t in (("w_router", w_router), ("router_logits", router_logits), ("topk_w", topk_w),
-                 ("y_rows", y_rows), ("g_out", g_out), ("dx", dx), ("dw_router", dw_router),
-                 ("db_router", db_router), ("dw_lat_down", dw_lat_down), ("dw_gate", dw_gate),
-                 ("dw_up", dw_up), ("dw_down", dw_down), ("dw_lat_up", dw_lat_up),
-                 ("dtopk_w", dtopk_w)):
-        _need(t, n, torch.float32)
-    for n, t in (("topk_idx", topk_idx), ("expert_offsets", expert_offsets),
-                 ("row_token", row_token), ("assign_row", assign_row)):
-        _need(t, n, torch.int32)
-    for n, t in (("w_lat_down", w_lat_down), ("w_gate", w_gate), ("w_up", w_up),
-                 ("w_lat_down_t", w_lat_down_t), ("w_gate_t", w_gate_t), ("w_up_t", w_up_t),
-                 ("w_down_t", w_down_t), ("w_lat_up_t", w_lat_up_t)):
-        _need(t, n, torch.bfloat16)
+    T, d, L, E, k, F = _bwd_args(x, w_router, router_logits, topk_idx, topk_w, expert_offsets,
+                                 row_token, assign_row, y_rows, w_lat_down, w_gate, w_up,
+                                 w_lat_down_t, w_lat_up_t, g_out, dx, dw_router, db_router,
+                                 dw_lat_down, dw_gate, dw_up, dw_down, dw_lat_up, dtopk_w)
+    for n, t, shp in (("w_gate_t", w_gate_t, (E, L, F)), ("w_up_t", w_up_t, (E, L, F)),
+                      ("w_down_t", w_down_t, (E, F, L))):
+        _need(t, n, torch.bfloat16, shape=shp)
     _need(ws, "ws", torch.uint8, 1)
-    T, d = x.shape
-    E, F, L = w_gate.shape
-    k = topk_idx.shape[1]
     _check("moe_backward", load().moe_backward(
         _ptr(x), _ptr(w_router), _ptr(router_logits), int(bias_mode), _ptr(topk_idx),
         _ptr(topk_w), _ptr(expert_offsets), _ptr(row_token), _ptr(assign_row), _ptr(y_rows),
@@ -358,9 +425,8 @@ def moe_backward(x, w_router, router_logits, bias_mode, topk_idx, topk_w, expert
 
 def moe_grad_cast_bf16(src, rounding, seed, stream_id, dst, stream=None):
     _need(src, "src", torch.float32)
+    _numel(dst, "dst", src.numel())
     _need(dst, "dst", torch.bfloat16)
-    if dst.numel() != src.numel():
-        raise ValueError("dst must have one value per src value")
     _check("moe_grad_cast_bf16", load().moe_grad_cast_bf16(
         _ptr(src), src.numel(), int(rounding), int(seed) & 0xFFFFFFFF, int(stream_id), _ptr(dst),
         _stream(stream)))
@@ -368,10 +434,11 @@ def moe_grad_cast_bf16(src, rounding, seed, stream_id, dst, stream=None):
 
 def moe_grad_cast_e5m2(src, scale, rounding, seed, stream_id, dst, stream=None):
     _need(src, "src", torch.float32)
+    if scale is None or scale.numel() < 1:
+        raise ValueError("scale must hold one value")
     _need(scale, "scale", torch.float32)
+    _numel(dst, "dst", src.numel())
     _need(dst, "dst", torch.uint8)
-    if dst.numel() != src.numel():
-        raise ValueError("dst must have one byte per src value")
     _check("moe_grad_cast_e5m2", load().moe_grad_cast_e5m2(
         _ptr(src), src.numel(), _ptr(scale), int(rounding), int(seed) & 0xFFFFFFFF,
         int(stream_id), _ptr(dst), _stream(stream)))
@@ -382,26 +449,17 @@ def moe_backward_fp8(x, w_router, router_logits, bias_mode, topk_idx, topk_w, ex
                      w_gate_t8, w_up_t8, w_down_t8, w_scale, w_lat_up_t, g_out, grad_scale,
                      rounding, seed, dx, dw_router, db_router, dw_lat_down, dw_gate, dw_up,
                      dw_down, dw_lat_up, dtopk_w, grad_amax, ws, stream=None):
-    _need(x, "x", torch.bfloat16, 2)
-    for n, t in (("w_router", w_router), ("router_logits", router_logits), ("topk_w", topk_w),
-                 ("y_rows", y_rows), ("g_out", g_out), ("dx", dx), ("dw_router", dw_router),
-                 ("db_router", db_router), ("dw_lat_down", dw_lat_down), ("dw_gate", dw_gate),
-                 ("dw_up", dw_up), ("dw_down", dw_down), ("dw_lat_up", dw_lat_up),
-                 ("dtopk_w", dtopk_w), ("w_scale", w_scale), ("grad_scale", grad_scale),
-                 ("grad_amax", grad_amax)):
-        _need(t, n, torch.float32)
-    for n, t in (("topk_idx", topk_idx), ("expert_offsets", expert_offsets),
-                 ("row_token", row_token), ("assign_row", assign_row)):
-        _need(t, n, torch.int32)
-    for n, t in (("w_lat_down", w_lat_down), ("w_gate", w_gate), ("w_up", w_up),
-                 ("w_lat_down_t", w_lat_down_t), ("w_lat_up_t", w_lat_up_t)):
-        _need(t, n, torch.bfloat16)
-    for n, t in (("w_gate_t8", w_gate_t8), ("w_up_t8", w_up_t8), ("w_down_t8", w_down_t8)):
-        _need(t, n, torch.uint8, 3)
+    T, d, L, E, k, F = _bwd_args(x, w_router, router_logits, topk_idx, topk_w, expert_offsets,
+                                 row_token, assign_row, y_rows, w_lat_down, w_gate, w_up,
+                                 w_lat_down_t, w_lat_up_t, g_out, dx, dw_router, db_router,
+                                 dw_lat_down, dw_gate, dw_up, dw_down, dw_lat_up, dtopk_w)
+    for n, t, shp in (("w_gate_t8", w_gate_t8, (E, L, F)), ("w_up_t8", w_up_t8, (E, L, F)),
+                      ("w_down_t8", w_down_t8, (E, F, L))):
+        _need(t, n, torch.uint8, shape=shp)
+    _need(w_scale, "w_scale", torch.float32, shape=(3 * E,))
+    _need(grad_scale, "grad_scale", torch.float32, shape=(3,))
+    _need(grad_amax, "grad_amax", torch.float32, shape=(3,))
     _need(ws, "ws", torch.uint8, 1)
-    T, d = x.shape
-    E, F, L = w_gate.shape
-    k = topk_idx.shape[1]
     _check("moe_backward_fp8", load().moe_backward_fp8(
         _ptr(x), _ptr(w_router), _ptr(router_logits), int(bias_mode), _ptr(topk_idx),
         _ptr(topk_w), _ptr(expert_offsets), _ptr(row_token), _ptr(assign_row), _ptr(y_rows),

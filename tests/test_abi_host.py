@@ -277,3 +277,83 @@ def test_backward_fp8_workspace_and_bad_args():
     assert lib.moe_grad_cast_e5m2(P, 64, P, 1, 0, 6, P + 2, None) == -2
     assert lib.moe_grad_cast_e5m2(P, 64, None, 1, 0, 6, P, None) == -1
     assert lib.moe_grad_cast_e5m2(P, 0, P, 1, 0, 6, P, None) == 0
+
+
+# ---- the Python binding checks every buffer's extent against the shapes it
+# passes to the C ABI (which receives only pointers and sizes), before any
+# launch: CPU tensors of the right dtype reach the device check only when
+# every extent agrees ----
+
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _ffn_set(T=8, d=64, L=64, E=4, k=2, F=64, Fs=0):
+    import torch
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    a = dict(x=_t((T, d), bf), w_lat_down=_t((L, d), bf), expert_offsets=_t((E + 1,), i32),
+             row_token=_t((T * k,), i32), w_gate=_t((E, F, L), bf), w_up=_t((E, F, L), bf),
+             w_down=_t((E, L, F), bf), ws_gate=_t((Fs, d), bf) if Fs else None,
+             ws_up=_t((Fs, d), bf) if Fs else None, k=k, y_rows=_t((T * k, L), f32),
+             hs=_t((T, Fs), bf) if Fs else None, ws=_t((256,), torch.uint8))
+    return a
+
+
+@pytest.mark.parametrize("Fs", [0, 128])
+@pytest.mark.parametrize("bad", ["w_up", "w_down", "y_rows", "row_token", "expert_offsets", "hs",
+                                 "ws_up", "w_lat_down"])
+def test_binding_rejects_mismatched_ffn_buffers(bad, Fs):
+    import torch
+    a = _ffn_set(Fs=Fs)
+    if a.get(bad) is None:
+        pytest.skip("buffer absent without a shared expert")
+    t = a[bad]
+    a[bad] = torch.zeros((t.shape[0] + 1,) + tuple(t.shape[1:]), dtype=t.dtype)
+    with pytest.raises(ValueError, match="shape|values"):
+        _lib.moe_latent_ffn_forward(**a)
+    a = _ffn_set(Fs=Fs)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _lib.moe_latent_ffn_forward(**a)
+
+
+def test_binding_rejects_mismatched_route_permute_combine_buffers():
+    import torch
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    T, d, E, k, L = 8, 64, 4, 2, 64
+    good = dict(x=_t((T, d), bf), w_router=_t((E, d), f32), b_router=_t((E,), f32), k=k,
+                topk_idx=_t((T, k), i32), topk_w=_t((T, k), f32), logits_out=_t((T, E), f32),
+                ws=_t((256,), torch.uint8))
+    for bad, shp in (("w_router", (E, d + 64)), ("b_router", (E + 1,)), ("topk_idx", (T, k + 1)),
+                     ("topk_w", (T + 1, k)), ("logits_out", (T, E + 1))):
+        a = dict(good)
+        a[bad] = _t(shp, a[bad].dtype)
+        with pytest.raises(ValueError, match="shape"):
+            _lib.moe_route(**a)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _lib.moe_route(**good)
+    pgood = dict(topk_idx=_t((T, k), i32), E=E, expert_counts=_t((E,), i32),
+                 expert_offsets=_t((E + 1,), i32), row_token=_t((T * k,), i32),
+                 assign_row=_t((T, k), i32), ws=_t((256,), torch.uint8))
+    for bad, n in (("expert_counts", E - 1), ("expert_offsets", E), ("row_token", T * k - 1),
+                   ("assign_row", T * k + 1)):
+        a = dict(pgood)
+        a[bad] = _t((n,), i32)
+        with pytest.raises(ValueError, match="values"):
+            _lib.moe_permute(**a)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _lib.moe_permute(**pgood)
+    cgood = dict(y_rows=_t((T * k, L), f32), topk_w=_t((T, k), f32), assign_row=_t((T, k), i32),
+                 w_lat_up=_t((d, L), bf), hs=None, ws_down=None, out=_t((T, d), f32),
+                 ws=_t((256,), torch.uint8))
+    for bad, shp in (("y_rows", (T * k - 1, L)), ("assign_row", (T, k - 1)), ("out", (T, d + 1))):
+        a = dict(cgood)
+        a[bad] = _t(shp, a[bad].dtype)
+        with pytest.raises(ValueError, match="shape"):
+            _lib.moe_combine(**a)
+    a = dict(cgood)
+    a["hs"] = _t((T, 64), bf)
+    with pytest.raises(ValueError, match="together"):
+        _lib.moe_combine(**a)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _lib.moe_combine(**cgood)

@@ -212,7 +212,7 @@ def test_permute_empty_batch(cuda):
     E = 16
     counts = torch.full((E,), -7, dtype=torch.int32, device=cuda)
     offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=cuda)
-    dummy = torch.empty(16, dtype=torch.int32, device=cuda)
+    dummy = torch.empty(0, dtype=torch.int32, device=cuda)
     idx = torch.empty((0, 2), dtype=torch.int32, device=cuda)
     moe.moe_permute(idx, E, counts, offsets, dummy, dummy, None)
     torch.cuda.synchronize()
