@@ -169,6 +169,23 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E,
                 void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_permute without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, results and errors as moe_permute,
+ * minus ws / ws_bytes: its scratch (the per-chunk expert counts and bases,
+ * 2 * ceil(T / 256) * E int32) lives in a library-owned static device array
+ * of 2^21 int32 (8 MiB) per GPU, which each GPU the library runs on holds
+ * until the process ends.  Shapes that need more (ceil(T / 256) * E > 2^20,
+ * e.g. T > 524,288 at E = 512) return MOE_ERR_UNSUPPORTED with nothing
+ * enqueued.  Allocates nothing and calls no allocating routine.  Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (two
+ * streams, two host threads) race and must be serialised by the caller.
+ */
+int moe_permute_noalloc(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E,
+                        int32_t* expert_counts, int32_t* expert_offsets,
+                        int32_t* row_token, int32_t* assign_row, void* stream);
+
+/*
  * Latent down-projection and the routed SwiGLU experts as grouped GEMMs
  * (plus, for a Base-2 layer, the shared expert's gate/up half).
  * "The Training and RL Infrastructure Behind MAI-Thinking-1": model table

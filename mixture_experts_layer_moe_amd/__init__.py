@@ -9,7 +9,8 @@ from ._lib import (MOE_BIAS_LOGITS, MOE_BIAS_SELECTION, MOE_ROUND_NEAREST,  # no
                    moe_backward_fp8, moe_grad_cast_bf16, moe_grad_cast_e5m2,
                    moe_combine, moe_fp8_amax, moe_fp8_quantize, moe_fp8_scale_update,
                    moe_latent_ffn_forward, moe_latent_ffn_forward_fp8,
-                   moe_latent_ffn_forward_rounds, moe_permute, moe_route, moe_route_ex,
+                   moe_latent_ffn_forward_rounds, moe_permute, moe_permute_noalloc, moe_route,
+                   moe_route_ex,
                    moe_set_kernel_events, moe_status_string, moe_workspace_bytes,
                    moe_workspace_bytes_rounds)
 from .layer import (Fp8GradScaling, Fp8Scaling, LatentMoEBuffers,  # noqa: F401

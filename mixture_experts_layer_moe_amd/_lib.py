@@ -55,6 +55,8 @@ def load():
                                  _vp, _sz, _vp]
     lib.moe_permute.restype = ctypes.c_int
     lib.moe_permute.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.moe_permute_noalloc.restype = ctypes.c_int
+    lib.moe_permute_noalloc.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
     lib.moe_latent_ffn_forward.restype = ctypes.c_int
     lib.moe_latent_ffn_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                            _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
@@ -223,6 +225,21 @@ def moe_permute(topk_idx, E, expert_counts, expert_offsets, row_token, assign_ro
                                              _ptr(expert_offsets), _ptr(row_token),
                                              _ptr(assign_row), _ptr(ws), _nbytes(ws),
                                              _stream(stream)))
+
+
+def moe_permute_noalloc(topk_idx, E, expert_counts, expert_offsets, row_token, assign_row,
+                        stream=None):
+    """moe_permute on the library's own static scratch (no workspace)."""
+    T, k = _dims2(topk_idx, "topk_idx")
+    E = int(E)
+    _need(topk_idx, "topk_idx", torch.int32, shape=(T, k))
+    for n, t, cnt in (("expert_counts", expert_counts, E), ("expert_offsets", expert_offsets, E + 1),
+                      ("row_token", row_token, T * k), ("assign_row", assign_row, T * k)):
+        _numel(t, n, cnt)
+        _need(t, n, torch.int32)
+    _check("moe_permute_noalloc", load().moe_permute_noalloc(
+        _ptr(topk_idx), T, k, E, _ptr(expert_counts), _ptr(expert_offsets), _ptr(row_token),
+        _ptr(assign_row), _stream(stream)))
 
 
 def _ffn_args(x, w_lat_down, expert_offsets, row_token, w_gate, w_up, w_down, ws_gate, ws_up, k,

@@ -37,6 +37,14 @@ hipError_t launch_permute(const int32_t* topk_idx, int64_t T, int k, int E, int3
                           int32_t* offsets, int32_t* row_token, int32_t* assign_row,
                           int32_t* chunk_counts, int32_t* chunk_base, hipStream_t s);
 hipError_t launch_permute_empty(int E, int32_t* counts, int32_t* offsets, hipStream_t s);
+// The same permutation on library-owned scratch (a static device array of
+// PERM_SCRATCH_INTS int32 per GPU; permute_scratch_ints(T, E) of it used):
+// allocates nothing.  hipErrorInvalidValue if the shapes need more.
+constexpr int64_t PERM_SCRATCH_INTS = int64_t(1) << 21;
+int64_t permute_scratch_ints(int64_t T, int E);
+hipError_t launch_permute_noalloc(const int32_t* topk_idx, int64_t T, int k, int E,
+                                  int32_t* counts, int32_t* offsets, int32_t* row_token,
+                                  int32_t* assign_row, hipStream_t s);
 
 // expert.hip
 struct ExpertGemmPlan {

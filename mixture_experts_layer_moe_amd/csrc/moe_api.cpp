@@ -300,6 +300,21 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_
                                    (int32_t*)(base + w.base), s));
 }
 
+int moe_permute_noalloc(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E,
+                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_token,
+                        int32_t* assign_row, void* stream) {
+  if (T < 0 || E <= 0 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (k > 16 || E > 1024 || T * (int64_t)k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_idx || !row_token || !assign_row)) return MOE_ERR_INVALID_ARG;
+  if (permute_scratch_ints(T, E) > PERM_SCRATCH_INTS) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  EventScope ev(K_PERMUTE, s);
+  if (T == 0) return hip_status(launch_permute_empty(E, expert_counts, expert_offsets, s));
+  return hip_status(launch_permute_noalloc(topk_idx, T, k, E, expert_counts, expert_offsets,
+                                           row_token, assign_row, s));
+}
+
 int moe_latent_ffn_forward(const uint16_t* x, const uint16_t* w_lat_down,
                            const int32_t* expert_offsets, const int32_t* row_token,
                            const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,

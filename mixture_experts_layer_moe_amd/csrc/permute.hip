@@ -11,6 +11,8 @@
 // counts; a single scan workgroup turns the counts into expert offsets and
 // per-chunk bases; a token's rank inside its expert is the popcount of the
 // mask bits below it, so rows keep ascending token order within an expert.
+#include <mutex>
+
 #include "launch.hpp"
 #include "scan.hpp"
 
@@ -126,6 +128,52 @@ __global__ void perm_empty_kernel(int E, int32_t* __restrict__ counts,
 hipError_t launch_permute_empty(int E, int32_t* counts, int32_t* offsets, hipStream_t s) {
   hipLaunchKernelGGL(perm_empty_kernel, dim3(1), dim3(1024), 0, s, E, counts, offsets);
   return hipGetLastError();
+}
+
+// Library-owned scratch of the permutation for callers that cannot allocate
+// (moe_permute_noalloc): the per-chunk expert counts and bases, PERM_SCRATCH_INTS
+// int32 values (8 MiB) per GPU, held until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: the kernels get the
+// device address from hipGetSymbolAddress, taken once per device with that
+// device current.  Every value the kernels read is written earlier in the
+// same call (chunk counts by the count kernel, bases by the scan), so nothing
+// needs clearing; calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) int32_t scratch[PERM_SCRATCH_INTS];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t permute_scratch(int32_t** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    g_scratch_ptr[dev] = (int32_t*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+int64_t permute_scratch_ints(int64_t T, int E) { return 2 * ceil_div(T, PERM_CHUNK) * (int64_t)E; }
+
+hipError_t launch_permute_noalloc(const int32_t* topk_idx, int64_t T, int k, int E,
+                                  int32_t* counts, int32_t* offsets, int32_t* row_token,
+                                  int32_t* assign_row, hipStream_t s) {
+  if (permute_scratch_ints(T, E) > PERM_SCRATCH_INTS) return hipErrorInvalidValue;
+  int32_t* ptr = nullptr;
+  const hipError_t err = permute_scratch(&ptr);
+  if (err != hipSuccess) return err;
+  const int64_t half = ceil_div(T, PERM_CHUNK) * (int64_t)E;
+  return launch_permute(topk_idx, T, k, E, counts, offsets, row_token, assign_row, ptr,
+                        ptr + half, s);
 }
 
 }  // namespace moe

@@ -357,3 +357,15 @@ def test_binding_rejects_mismatched_route_permute_combine_buffers():
         _lib.moe_combine(**a)
     with pytest.raises(ValueError, match="GPU tensor"):
         _lib.moe_combine(**cgood)
+
+
+def test_permute_noalloc_rejects_bad_args():
+    lib = _lib.load()
+    assert lib.moe_permute_noalloc(P, -1, 2, 16, P, P, P, P, None) == -1
+    assert lib.moe_permute_noalloc(P, 8, 0, 16, P, P, P, P, None) == -1
+    assert lib.moe_permute_noalloc(P, 8, 17, 16, P, P, P, P, None) == -1
+    assert lib.moe_permute_noalloc(P, 8, 17, 32, P, P, P, P, None) == -2
+    assert lib.moe_permute_noalloc(P, 8, 2, 16, None, P, P, P, None) == -1
+    assert lib.moe_permute_noalloc(None, 8, 2, 16, P, P, P, P, None) == -1
+    # the static scratch holds 2^21 int32: 2 * ceil(T / 256) * E beyond that
+    assert lib.moe_permute_noalloc(P, 600_000, 1, 512, P, P, P, P, None) == -2
