@@ -20,6 +20,11 @@ the layer output, g_out = dLoss/d out ([T, d]):
   dw_tj = dc_t . y_r (the combine is FP32 on the pages);
 * the projections: out = c W_up^T gives dc = g_out W_up, dW_up = g_out^T c;
   z = x W_dn^T gives dx = dz W_dn, dW_dn = dz^T x;
+* the Base-2 shared expert (SwiGLU on x, added to out with weight 1): with
+  gs = x Ws_g^T, us = x Ws_u^T, hs = silu(gs) us, s = hs Ws_d^T:
+  dWs_d = g_out^T hs, dhs = g_out Ws_d, dgs = dhs us silu'(gs),
+  dus = dhs silu(gs), dx += dgs Ws_g + dus Ws_u, dWs_g = dgs^T x,
+  dWs_u = dus^T x;
 * the router: w_tj = p_t[idx_tj] with p = softmax(l), l = x W_r^T + b, the
   selection itself piecewise constant (no gradient), the weights not
   renormalised: dp_te = dw_tj where e = idx_tj (0 elsewhere),
@@ -43,7 +48,8 @@ Modes
 ``bf16_operands``  the forward as in its bf16_operands mode (z, h, c rounded
                    to bf16 with round-to-nearest-even where they feed a GEMM),
                    and the gradients rounded to bf16 where they become GEMM
-                   operands: g_out, dy, dg, du and dz, by ``rounding``:
+                   operands: g_out, dy, dg, du, dz and the shared expert's
+                   dgs and dus, by ``rounding``:
                    "rne" (nearest, ties to even) or "sr" (stochastic rounding
                    with the counter-based generator below).  dh, dz rows, the
                    combine gradient and everything on the router side stay
@@ -82,7 +88,8 @@ row-major index of the tensor) of stream s under seed S is the top 16 bits of
 where lowbias32 is the 32-bit integer mixer published by C. Wellons (hash
 prospector): x ^= x >> 16; x *= 0x7feb352d; x ^= x >> 15; x *= 0x846ca68b;
 x ^= x >> 16 (all mod 2^32).  Streams: 1 g_out [T, d], 2 dy [T*k, L] (rows in
-expert order), 3 dg and 4 du [T*k, F], 5 dz [T, L].
+expert order), 3 dg and 4 du [T*k, F], 5 dz [T, L], 9 dgs and 10 dus [T, Fs]
+(the shared expert's gate and up gradients).
 
 Parity pins: ``tests/test_oracle_backward.py`` (central finite differences of
 the independently pinned forward oracle, softmax-gradient invariants,
@@ -95,7 +102,7 @@ import numpy as np
 from . import latent_moe as F
 
 ROUNDINGS = ("rne", "sr")
-SR_STREAM = {"g_out": 1, "dy": 2, "dg": 3, "du": 4, "dz": 5}
+SR_STREAM = {"g_out": 1, "dy": 2, "dg": 3, "du": 4, "dz": 5, "dgs": 9, "dus": 10}
 FP8_STREAM = {"dy": 6, "dg": 7, "du": 8}
 E5M2_MAX = 57344.0
 E5M2_MIN_NORMAL = 2.0 ** -14
@@ -265,10 +272,33 @@ def expert_backward(zr, w_gate, w_up, w_down, dy_b, mode, dh=None):
 # whole layer
 # ---------------------------------------------------------------------------
 
+def shared_backward(x, ws_gate, ws_up, ws_down, go, mode="exact", rounding="rne", seed=0):
+    """Gradients of the Base-2 shared expert s = (silu(x Ws_g^T) (x Ws_u^T))
+    Ws_d^T (hs rounded to bf16 in bf16_operands mode, as in the forward) for
+    the upstream gradient go (already cast where it feeds the GEMMs): the
+    module notes' formulas, dgs and dus cast to bf16 (streams 9, 10) where
+    they become GEMM operands."""
+    x = np.asarray(x, np.float64)
+    wsg, wsu, wsd = (np.asarray(m, np.float64) for m in (ws_gate, ws_up, ws_down))
+    gs = x @ wsg.T
+    us = x @ wsu.T
+    hs = F._maybe_bf16(F.silu(gs) * us, mode)
+    dhs = go @ wsd
+    dgs = dhs * us * silu_grad(gs)
+    dus = dhs * F.silu(gs)
+    dgs_b = _grad_round(dgs, "dgs", mode, rounding, seed)
+    dus_b = _grad_round(dus, "dus", mode, rounding, seed)
+    return {"dx_shared": dgs_b @ wsg + dus_b @ wsu, "dWs_gate": dgs_b.T @ x,
+            "dWs_up": dus_b.T @ x, "dWs_down": go.T @ hs, "hs_b": hs, "dhs": dhs,
+            "dgs_b": dgs_b, "dus_b": dus_b}
+
+
 def backward(x, w_router, b_router, k, w_dn, experts, w_lat_up, g_out, mode="exact",
-             rounding="rne", seed=0, routing=None, bias_mode="logits", grad_fp8=None):
-    """Gradients of the LatentMoE forward (no shared expert) for dLoss/d out =
-    g_out.  ``routing`` = (topk_idx, topk_w) replays a routing (the weights'
+             rounding="rne", seed=0, routing=None, bias_mode="logits", grad_fp8=None,
+             shared=None):
+    """Gradients of the LatentMoE forward for dLoss/d out = g_out; ``shared``
+    = (Ws_gate, Ws_up, Ws_down) adds the Base-2 shared expert (its weight
+    gradients dWs_gate, dWs_up, dWs_down, and its part of dx).  ``routing`` = (topk_idx, topk_w) replays a routing (the weights'
     gradient still flows through the softmax of this oracle's own logits at
     the replayed indices).  ``grad_fp8`` = {"grad_scale": (s_dy, s_dg, s_du),
     "w_scale": (s_Wg[E], s_Wu[E], s_Wd[E])} runs the experts' data-gradient
@@ -386,9 +416,14 @@ def backward(x, w_router, b_router, k, w_dn, experts, w_lat_up, g_out, mode="exa
     else:
         db = dl.sum(axis=0)
     extra = {}
+    dx_shared = 0.0
+    if shared is not None:
+        sb = shared_backward(x, *shared, go, mode=mode, rounding=rounding, seed=seed)
+        dx_shared = sb["dx_shared"]
+        extra.update(sb)
     if grad_fp8 is not None:
         extra["grad_amax"] = tuple(float(np.abs(t).max()) if t.size else 0.0 for t in (dy, dg, du))
-    return {**extra, "dx": dx + dx_router, "dx_latent": dx, "dx_router": dx_router,
+    return {**extra, "dx": dx + dx_router + dx_shared, "dx_latent": dx, "dx_router": dx_router,
             "dW_router": dW_router, "db_router": db, "dW_dn": dW_dn, "dW_gate": dW_gate,
             "dW_up": dW_up, "dW_down": dW_down, "dW_lat_up": dW_lat_up, "dtopk_w": dtopk_w,
             "dlogits": dl, "probs": probs, "go": go, "dc": dc, "dy_b": dy_b, "dh": dh,

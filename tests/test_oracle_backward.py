@@ -20,7 +20,7 @@ from oracle import latent_moe_backward as B
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
 
-def small_layer(seed=0, T=5, d=6, L=4, E=4, k=2, Fw=3, bias=True):
+def small_layer(seed=0, T=5, d=6, L=4, E=4, k=2, Fw=3, bias=True, Fs=0):
     rng = np.random.default_rng(seed)
     p = {
         "x": rng.standard_normal((T, d)),
@@ -33,19 +33,27 @@ def small_layer(seed=0, T=5, d=6, L=4, E=4, k=2, Fw=3, bias=True):
         "w_lat_up": rng.standard_normal((d, L)) / np.sqrt(L),
         "g_out": rng.standard_normal((T, d)),
     }
+    if Fs:
+        p["ws_gate"] = rng.standard_normal((Fs, d)) / np.sqrt(d)
+        p["ws_up"] = rng.standard_normal((Fs, d)) / np.sqrt(d)
+        p["ws_down"] = rng.standard_normal((d, Fs)) / np.sqrt(Fs)
     return p, k
+
+
+def _shared(p):
+    return (p["ws_gate"], p["ws_up"], p["ws_down"]) if "ws_gate" in p else None
 
 
 def fwd_out(p, k):
     experts = [(p["w_gate"][e], p["w_up"][e], p["w_down"][e]) for e in range(p["w_gate"].shape[0])]
     return oracle.forward(p["x"], p["w_router"], p["b_router"], k, p["w_dn"], experts,
-                          p["w_lat_up"], mode="exact")
+                          p["w_lat_up"], shared=_shared(p), mode="exact")
 
 
 def bwd(p, k, **kw):
     experts = [(p["w_gate"][e], p["w_up"][e], p["w_down"][e]) for e in range(p["w_gate"].shape[0])]
     return oracle.backward(p["x"], p["w_router"], p["b_router"], k, p["w_dn"], experts,
-                           p["w_lat_up"], p["g_out"], **kw)
+                           p["w_lat_up"], p["g_out"], shared=_shared(p), **kw)
 
 
 def loss(p, k):
@@ -61,13 +69,20 @@ GRAD_OF = {"x": "dx", "w_router": "dW_router", "b_router": "db_router", "w_dn": 
            "w_gate": "dW_gate", "w_up": "dW_up", "w_down": "dW_down", "w_lat_up": "dW_lat_up"}
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_finite_differences_every_parameter(seed):
-    p, k = small_layer(seed)
+SHARED_GRAD_OF = {"x": "dx", "ws_gate": "dWs_gate", "ws_up": "dWs_up", "ws_down": "dWs_down",
+                  "w_lat_up": "dW_lat_up", "w_dn": "dW_dn"}
+
+
+@pytest.mark.parametrize("seed,Fs", [(0, 0), (1, 0), (2, 0), (5, 4), (6, 7)])
+def test_finite_differences_every_parameter(seed, Fs):
+    """Every parameter and x; with Fs > 0 the layer has a shared expert (its
+    three weights too, and its part of dx)."""
+    p, k = small_layer(seed, Fs=Fs)
     assert selection_gap(p, k) > 1e-3      # the perturbation below never changes selection
     g = bwd(p, k, mode="exact")
     eps = 1e-6
-    for name, gname in GRAD_OF.items():
+    names = dict(GRAD_OF, **SHARED_GRAD_OF) if Fs else GRAD_OF
+    for name, gname in names.items():
         base = p[name]
         num = np.zeros_like(base)
         for i in np.ndindex(base.shape):
@@ -369,3 +384,62 @@ def test_fp8_grad_mode_close_to_bf16_mode_and_reports_maxima():
         assert 1e-4 < rel < 0.1, (n, rel)     # FP8 noise: present, and small
     for n in ("dW_down", "dW_lat_up"):        # upstream of / outside the FP8 GEMMs
         np.testing.assert_array_equal(got[n], ref[n])
+
+
+def test_shared_expert_gradients_alone():
+    """With W_up = 0 and W_r = 0 (uniform routing, no routed contribution to
+    out) the layer is the shared expert alone: its gradients are those of a
+    dense SwiGLU FFN, checked here by finite differences of the forward
+    oracle's shared_expert directly; dx is the shared expert's alone (the
+    latent path's dz is 0 because dc = g_out W_up = 0)."""
+    p, k = small_layer(7, Fs=5)
+    p["w_lat_up"][:] = 0.0
+    g = bwd(p, k, mode="exact")
+    eps = 1e-6
+
+    def lossf(q):
+        return float(np.sum(p["g_out"] * oracle.shared_expert(q["x"], q["ws_gate"], q["ws_up"],
+                                                                q["ws_down"], mode="exact")))
+    for name, gname in (("ws_gate", "dWs_gate"), ("ws_up", "dWs_up"), ("ws_down", "dWs_down")):
+        base = p[name]
+        num = np.zeros_like(base)
+        for i in np.ndindex(base.shape):
+            old = base[i]
+            base[i] = old + eps
+            lp = lossf(p)
+            base[i] = old - eps
+            lm = lossf(p)
+            base[i] = old
+            num[i] = (lp - lm) / (2 * eps)
+        assert np.max(np.abs(g[gname] - num)) < 1e-6 * max(1.0, np.max(np.abs(num))), name
+    assert np.all(g["dx_latent"] == 0)
+    np.testing.assert_allclose(g["dx_shared"] + g["dx_router"], g["dx"], rtol=0, atol=1e-12)
+
+
+def test_shared_expert_stochastic_rounding_streams():
+    """In bf16_operands mode with stochastic rounding the shared expert's
+    gate and up gradients are cast stochastically: every cast value is one
+    of the two bf16 neighbours of the float32 value (truncated, or one bf16
+    step further from zero), both occur, and another seed changes the bits;
+    nearest rounding gives the nearest neighbour."""
+    p, k = small_layer(8, T=40, Fs=16)
+    g1 = bwd(p, k, mode="bf16_operands", rounding="sr", seed=1)
+    g2 = bwd(p, k, mode="bf16_operands", rounding="sr", seed=2)
+    gn = bwd(p, k, mode="bf16_operands", rounding="rne", seed=1)
+    gs = p["x"] @ p["ws_gate"].T
+    us = p["x"] @ p["ws_up"].T
+    hs = oracle.round_bf16(oracle.silu(gs) * us)
+    np.testing.assert_array_equal(g1["hs_b"], hs)
+    exact = {"dgs_b": g1["dhs"] * us * B.silu_grad(gs), "dus_b": g1["dhs"] * oracle.silu(gs)}
+    for name, v in exact.items():
+        u = np.ascontiguousarray(v.astype(np.float32)).view(np.uint32).astype(np.uint64)
+        lo = (u & 0xFFFF0000).astype(np.uint32).view(np.float32).astype(np.float64)
+        hi = ((u & 0xFFFF0000) + 0x10000).astype(np.uint32).view(np.float32).astype(np.float64)
+        got = g1[name]
+        assert np.all((got == lo) | (got == hi)), name
+        assert np.any(got == lo) and np.any(got == hi), name
+        assert not np.array_equal(got, g2[name]), name
+    # nearest rounding (g_out itself is then rounded to nearest, so dhs differs)
+    ex_n = {"dgs_b": gn["dhs"] * us * B.silu_grad(gs), "dus_b": gn["dhs"] * oracle.silu(gs)}
+    for name, v in ex_n.items():
+        np.testing.assert_array_equal(gn[name], oracle.round_bf16(v.astype(np.float32)))
