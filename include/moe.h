@@ -49,7 +49,10 @@
  * - Limits: 1 <= k <= min(E, 16); E <= 1024; d, L, F, Fs multiples of 64
  *   (Fs may be 0 = no shared expert); T * k < 2^31; T * L * 2 < 2^31 bytes.
  * - Thread safety: calls from several host threads on different streams are
- *   safe; the only library state is the per-thread profiling-event registry.
+ *   safe.  Library state: the per-thread profiling-event registry, a
+ *   per-device cache of the compute-unit count (atomic), and the per-device
+ *   scratch address of moe_permute_noalloc (taken under a mutex; calls of
+ *   that entry point that overlap on one GPU race, see there).
  */
 #ifndef LATENT_MOE_H
 #define LATENT_MOE_H
@@ -329,8 +332,8 @@ int moe_latent_ffn_forward_rounds(const uint16_t* x, const uint16_t* w_lat_down,
                                   int32_t* rounds_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- backward pass ---------------------------------------------------------
- * Gradients of the forward pass above (no shared expert: Fs must be 0) for a
- * gradient g_out = dLoss/d out [T, d] fp32.  Math, per "The Training and RL
+ * Gradients of the forward pass above for a gradient g_out = dLoss/d out
+ * [T, d] fp32 (a Base-2 layer's shared expert: moe_shared_backward below).  Math, per "The Training and RL
  * Infrastructure Behind MAI-Thinking-1", section 2 "Numerics":
  *   dW_up = g^T c,  dc = g W_up                        (g = g_out cast to bf16)
  *   dy_r = w[t,j] dc_t,  dw[t,j] = dc_t . y_r          (combine backward, FP32)
@@ -373,8 +376,9 @@ int moe_latent_ffn_forward_rounds(const uint16_t* x, const uint16_t* w_lat_down,
  * gradient of the gate weights).  Workspace: MOE_OP_BACKWARD.  Limits and
  * errors as for the forward, and T * k + 64 * E < 2^22 (the weight-gradient
  * GEMMs address 256-row tiles of the transposed operands with 32-bit
- * offsets); otherwise MOE_ERR_UNSUPPORTED.  There is no shared expert in the
- * backward.  Deterministic: every reduction has a fixed order.
+ * offsets); otherwise MOE_ERR_UNSUPPORTED.  The shared expert's gradients
+ * come from moe_shared_backward.  Deterministic: every reduction has a fixed
+ * order.
  */
 /* moe_grad_cast_bf16: dst[i] = src[i] cast to bf16 with the backward's
  * gradient rounding (MOE_ROUND_NEAREST, or MOE_ROUND_STOCHASTIC with the
@@ -401,6 +405,84 @@ int moe_backward(const uint16_t* x, const float* w_router, const float* router_l
                  float* dx, float* dw_router, float* db_router, float* dw_lat_down,
                  float* dw_gate, float* dw_up, float* dw_down, float* dw_lat_up, float* dtopk_w,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* ---- backward on the multi-round dropless schedule -----------------------------
+ * "Frontier Pre-training at Microsoft AI", "Dropless MoE with tunable,
+ * fixed-size memory usage" (the backward recomputes per expert group on the
+ * multi-round schedule); "The Training and RL Infrastructure Behind
+ * MAI-Thinking-1", section "Memory and dropless MoE" (static-memory dropless
+ * mode: recomputation per expert and per round).
+ * moe_backward with the routed experts' part on the forward's round schedule
+ * (moe_latent_ffn_forward_rounds: groups of group_size experts share
+ * group_size * capacity rows per round): in round r the rows that round
+ * holds get dh = dy W_d, the recomputed gate/up GEMM with the SwiGLU
+ * backward (dg, du, h) and their latent gradient, in buffers of
+ * min(T k, E capacity) rows whatever the routing, and add their share of
+ * dW_d, dW_g, dW_u (round 0 writes them, later rounds add, in round order:
+ * deterministic).  Every row's data gradients are moe_backward's bit for bit
+ * (same tiles along K, the same stochastic-rounding element indices), so dx,
+ * dW_dn, dW_up, the router's gradients and dtopk_w equal moe_backward's;
+ * the expert weight gradients equal them up to the fp32 summation order
+ * (their K sums split at round boundaries).  The host enqueues the most
+ * rounds any routing can need (as the forward does); surplus rounds find no
+ * rows.  bf16 data gradients only.  Arguments as for moe_backward plus
+ * capacity, group_size (>= 1, MOE_ERR_INVALID_ARG otherwise); workspace
+ * moe_workspace_bytes_backward_rounds.  MOE_KERNEL_BWD_DGRAD brackets every
+ * round (MOE_KERNEL_BWD_WGRAD is not recorded).
+ */
+size_t moe_workspace_bytes_backward_rounds(int64_t T, int32_t d, int32_t L, int32_t E, int32_t k,
+                                           int32_t F, int32_t capacity, int32_t group_size);
+int moe_backward_rounds(const uint16_t* x, const float* w_router, const float* router_logits,
+                        int32_t bias_mode, const int32_t* topk_idx, const float* topk_w,
+                        const int32_t* expert_offsets, const int32_t* row_token,
+                        const int32_t* assign_row, const float* y_rows,
+                        const uint16_t* w_lat_down, const uint16_t* w_gate, const uint16_t* w_up,
+                        const uint16_t* w_lat_down_t, const uint16_t* w_gate_t,
+                        const uint16_t* w_up_t, const uint16_t* w_down_t,
+                        const uint16_t* w_lat_up_t, const float* g_out, int64_t T, int32_t d,
+                        int32_t L, int32_t E, int32_t k, int32_t F, int32_t capacity,
+                        int32_t group_size, int32_t rounding, uint32_t seed, float* dx,
+                        float* dw_router, float* db_router, float* dw_lat_down, float* dw_gate,
+                        float* dw_up, float* dw_down, float* dw_lat_up, float* dtopk_w, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* ---- backward of the shared expert (Base-2) -----------------------------------
+ * "MAI-Base-2: Microsoft's 2.8T base model...", section "The model": one
+ * shared expert that every token passes through, a SwiGLU FFN on the full
+ * hidden state (not down/up projected), added to the layer output.  With
+ * gs = x Ws_g^T, us = x Ws_u^T, hs = bf16(silu(gs) us) (the forward's hs)
+ * and g = g_out cast to bf16 exactly as moe_backward casts it (stream 1):
+ *   dWs_d = g^T hs,  dhs = g Ws_d,  dgs = dhs us silu'(gs),  dus = dhs silu(gs)
+ *   dx   += dgs Ws_g + dus Ws_u,   dWs_g = dgs^T x,   dWs_u = dus^T x
+ * dgs and dus are cast to bf16 where they become GEMM operands (nearest, or
+ * stochastic with streams 9 and 10, element index t * Fs + f); dhs and the
+ * accumulations are FP32; gs, us and hs are recomputed (the forward's
+ * values bit for bit).  The shared expert stays bf16 in moe_backward_fp8's
+ * setting too.
+ *
+ * moe_backward_prepare_shared: the transposed bf16 copies the data-gradient
+ * GEMMs read: ws_gate_t, ws_up_t [d, Fs] (of Ws_g, Ws_u [Fs, d]) and
+ * ws_down_t [Fs, d] (of Ws_d [d, Fs]); call once per weight update.
+ *
+ * moe_shared_backward: inputs x [T, d] bf16, g_out [T, d] fp32, the forward
+ * weights ws_gate, ws_up [Fs, d] and the prepared transposes.  Outputs (fp32,
+ * caller-allocated): dx [T, d] is ACCUMULATED (dx += the shared expert's
+ * part; run it after moe_backward, which overwrites dx), dws_gate,
+ * dws_up [Fs, d] and dws_down [d, Fs] are overwritten.  Workspace:
+ * MOE_OP_SHARED_BACKWARD (T, d and Fs used).  Errors as for the forward
+ * (Fs must be a positive multiple of 64).  Deterministic.
+ */
+#define MOE_OP_SHARED_BACKWARD 7
+int moe_backward_prepare_shared(const uint16_t* ws_gate, const uint16_t* ws_up,
+                                const uint16_t* ws_down, int32_t d, int32_t Fs,
+                                uint16_t* ws_gate_t, uint16_t* ws_up_t, uint16_t* ws_down_t,
+                                void* stream);
+int moe_shared_backward(const uint16_t* x, const float* g_out, const uint16_t* ws_gate,
+                        const uint16_t* ws_up, const uint16_t* ws_gate_t,
+                        const uint16_t* ws_up_t, const uint16_t* ws_down_t, int64_t T,
+                        int32_t d, int32_t Fs, int32_t rounding, uint32_t seed, float* dx,
+                        float* dws_gate, float* dws_up, float* dws_down, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /* ---- backward with FP8 data gradients ----------------------------------------
  * "The Training and RL Infrastructure Behind MAI-Thinking-1", section 2

@@ -22,6 +22,7 @@ MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_LATENT_FFN, MOE_OP_COMBINE = 0, 1, 2, 3
 MOE_OP_LATENT_FFN_FP8 = 4
 MOE_OP_BACKWARD = 5
 MOE_OP_BACKWARD_FP8 = 6
+MOE_OP_SHARED_BACKWARD = 7
 MOE_ROUND_NEAREST, MOE_ROUND_STOCHASTIC = 0, 1
 KERNELS = {"router_gemm": 0, "router_topk": 1, "permute": 2, "latent_down": 3, "gate_up": 4,
            "expert_down": 5, "combine": 6, "latent_up": 7, "bwd_up": 8, "bwd_combine": 9,
@@ -95,6 +96,18 @@ def load():
     lib.moe_backward_fp8.argtypes = ([_vp, _vp, _vp, _i32] + [_vp] * 17 + [_i64, _i32, _i32, _i32,
                                       _i32, _i32, _i32, ctypes.c_uint32] + [_vp] * 11 +
                                      [_sz, _vp])
+    lib.moe_workspace_bytes_backward_rounds.restype = _sz
+    lib.moe_workspace_bytes_backward_rounds.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                        _i32]
+    lib.moe_backward_rounds.restype = ctypes.c_int
+    lib.moe_backward_rounds.argtypes = ([_vp, _vp, _vp, _i32] + [_vp] * 15 +
+                                        [_i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                         ctypes.c_uint32] + [_vp] * 10 + [_sz, _vp])
+    lib.moe_backward_prepare_shared.restype = ctypes.c_int
+    lib.moe_backward_prepare_shared.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]
+    lib.moe_shared_backward.restype = ctypes.c_int
+    lib.moe_shared_backward.argtypes = ([_vp] * 7 + [_i64, _i32, _i32, _i32, ctypes.c_uint32] +
+                                        [_vp] * 5 + [_sz, _vp])
     lib.moe_set_kernel_events.restype = ctypes.c_int
     lib.moe_set_kernel_events.argtypes = [ctypes.c_int, _vp, _vp]
     _lib = lib
@@ -486,3 +499,69 @@ def moe_backward_fp8(x, w_router, router_logits, bias_mode, topk_idx, topk_w, ex
         _ptr(dw_router), _ptr(db_router), _ptr(dw_lat_down), _ptr(dw_gate), _ptr(dw_up),
         _ptr(dw_down), _ptr(dw_lat_up), _ptr(dtopk_w), _ptr(grad_amax), _ptr(ws), _nbytes(ws),
         _stream(stream)))
+
+
+def moe_backward_prepare_shared(ws_gate, ws_up, ws_down, ws_gate_t, ws_up_t, ws_down_t,
+                                stream=None):
+    """Transposed copies of the shared expert's weights for moe_shared_backward."""
+    Fs, d = _dims2(ws_gate, "ws_gate")
+    for n, t, shp in (("ws_gate", ws_gate, (Fs, d)), ("ws_up", ws_up, (Fs, d)),
+                      ("ws_down", ws_down, (d, Fs)), ("ws_gate_t", ws_gate_t, (d, Fs)),
+                      ("ws_up_t", ws_up_t, (d, Fs)), ("ws_down_t", ws_down_t, (Fs, d))):
+        if t is None:
+            raise ValueError(f"{n} is required")
+        _need(t, n, torch.bfloat16, shape=shp)
+    _check("moe_backward_prepare_shared", load().moe_backward_prepare_shared(
+        _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), d, Fs, _ptr(ws_gate_t), _ptr(ws_up_t),
+        _ptr(ws_down_t), _stream(stream)))
+
+
+def moe_shared_backward(x, g_out, ws_gate, ws_up, ws_gate_t, ws_up_t, ws_down_t, rounding, seed,
+                        dx, dws_gate, dws_up, dws_down, ws, stream=None):
+    """Gradients of the shared expert; dx is accumulated into (dx += ...)."""
+    T, d = _dims2(x, "x")
+    Fs = _dims2(ws_gate, "ws_gate")[0]
+    _need(x, "x", torch.bfloat16, shape=(T, d))
+    for n, t, shp in (("ws_gate", ws_gate, (Fs, d)), ("ws_up", ws_up, (Fs, d)),
+                      ("ws_gate_t", ws_gate_t, (d, Fs)), ("ws_up_t", ws_up_t, (d, Fs)),
+                      ("ws_down_t", ws_down_t, (Fs, d))):
+        if t is None:
+            raise ValueError(f"{n} is required")
+        _need(t, n, torch.bfloat16, shape=shp)
+    for n, t, shp in (("g_out", g_out, (T, d)), ("dx", dx, (T, d)), ("dws_gate", dws_gate, (Fs, d)),
+                      ("dws_up", dws_up, (Fs, d)), ("dws_down", dws_down, (d, Fs))):
+        if t is None:
+            raise ValueError(f"{n} is required")
+        _need(t, n, torch.float32, shape=shp)
+    _need(ws, "ws", torch.uint8, 1)
+    _check("moe_shared_backward", load().moe_shared_backward(
+        _ptr(x), _ptr(g_out), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_gate_t), _ptr(ws_up_t),
+        _ptr(ws_down_t), T, d, Fs, int(rounding), int(seed) & 0xFFFFFFFF, _ptr(dx), _ptr(dws_gate),
+        _ptr(dws_up), _ptr(dws_down), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_workspace_bytes_backward_rounds(T, d, L, E, k, F, capacity, group_size):
+    return int(load().moe_workspace_bytes_backward_rounds(T, d, L, E, k, F, capacity, group_size))
+
+
+def moe_backward_rounds(x, w_router, router_logits, bias_mode, topk_idx, topk_w, expert_offsets,
+                        row_token, assign_row, y_rows, w_lat_down, w_gate, w_up, w_lat_down_t,
+                        w_gate_t, w_up_t, w_down_t, w_lat_up_t, g_out, capacity, group_size,
+                        rounding, seed, dx, dw_router, db_router, dw_lat_down, dw_gate, dw_up,
+                        dw_down, dw_lat_up, dtopk_w, ws, stream=None):
+    T, d, L, E, k, F = _bwd_args(x, w_router, router_logits, topk_idx, topk_w, expert_offsets,
+                                 row_token, assign_row, y_rows, w_lat_down, w_gate, w_up,
+                                 w_lat_down_t, w_lat_up_t, g_out, dx, dw_router, db_router,
+                                 dw_lat_down, dw_gate, dw_up, dw_down, dw_lat_up, dtopk_w)
+    for n, t, shp in (("w_gate_t", w_gate_t, (E, L, F)), ("w_up_t", w_up_t, (E, L, F)),
+                      ("w_down_t", w_down_t, (E, F, L))):
+        _need(t, n, torch.bfloat16, shape=shp)
+    _need(ws, "ws", torch.uint8, 1)
+    _check("moe_backward_rounds", load().moe_backward_rounds(
+        _ptr(x), _ptr(w_router), _ptr(router_logits), int(bias_mode), _ptr(topk_idx),
+        _ptr(topk_w), _ptr(expert_offsets), _ptr(row_token), _ptr(assign_row), _ptr(y_rows),
+        _ptr(w_lat_down), _ptr(w_gate), _ptr(w_up), _ptr(w_lat_down_t), _ptr(w_gate_t),
+        _ptr(w_up_t), _ptr(w_down_t), _ptr(w_lat_up_t), _ptr(g_out), T, d, L, E, k, F,
+        int(capacity), int(group_size), int(rounding), int(seed) & 0xFFFFFFFF, _ptr(dx),
+        _ptr(dw_router), _ptr(db_router), _ptr(dw_lat_down), _ptr(dw_gate), _ptr(dw_up),
+        _ptr(dw_down), _ptr(dw_lat_up), _ptr(dtopk_w), _ptr(ws), _nbytes(ws), _stream(stream)))

@@ -86,22 +86,26 @@ hipError_t launch_cvt_e5m2(const float* src, int64_t n, const float* scale, int 
 // K stage width), kpre[E] the padded total
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void kpad_prefix_kernel(const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ ends,
                                                            int E, int32_t* __restrict__ kpre) {
   const int e = threadIdx.x;
-  const int rows = e < E ? offsets[e + 1] - offsets[e] : 0;
+  // expert e's rows: offsets[e] .. ends[e] (ends null: offsets[e + 1])
+  const int rows = e < E ? (ends ? ends[e] : offsets[e + 1]) - offsets[e] : 0;
   int total;
   const int ex = block_exclusive_scan((rows + 63) / 64 * 64, &total);
   if (e < E) kpre[e] = ex;
   if (e == 0) kpre[E] = total;
 }
 
-hipError_t launch_kpad_prefix(const int32_t* offsets, int E, int32_t* kpre, hipStream_t s) {
-  hipLaunchKernelGGL(kpad_prefix_kernel, dim3(1), dim3(1024), 0, s, offsets, E, kpre);
+hipError_t launch_kpad_prefix(const int32_t* offsets, int E, int32_t* kpre, hipStream_t s,
+                              const int32_t* ends) {
+  hipLaunchKernelGGL(kpad_prefix_kernel, dim3(1), dim3(1024), 0, s, offsets, ends, E, kpre);
   return hipGetLastError();
 }
 
 // Transpose of a bf16 matrix through LDS in 64 x 64 tiles, into the padded
-// K layout.  Source rows of group e: off[e] .. off[e + 1] (rows of src, or
+// K layout.  Source rows of group e: off[e] .. off_end[e] (off_end null:
+// off[e + 1]) (rows of src, or
 // rows gather[r] of src when gather is given); they land in destination
 // columns kpre[e] .. and the rest of the group's padded range is zero.
 // Without groups (off == nullptr) the single group is rows 0 .. nrows with
@@ -109,9 +113,9 @@ hipError_t launch_kpad_prefix(const int32_t* offsets, int E, int32_t* kpre, hipS
 // chunks, z = batch (src / dst advance by the batch strides).
 __global__ __launch_bounds__(256) void transpose_pad_kernel(
     const uint16_t* __restrict__ src, int64_t lds_, const int32_t* __restrict__ gather,
-    int64_t gather_rows, int C, const int32_t* __restrict__ off, const int32_t* __restrict__ kpre,
-    int G, int64_t nrows, uint16_t* __restrict__ dst, int64_t ldd, int64_t src_batch,
-    int64_t dst_batch) {
+    int64_t gather_rows, int C, const int32_t* __restrict__ off,
+    const int32_t* __restrict__ off_end, const int32_t* __restrict__ kpre, int G, int64_t nrows,
+    uint16_t* __restrict__ dst, int64_t ldd, int64_t src_batch, int64_t dst_batch) {
   __shared__ uint16_t tile[64][66];
   const int64_t kc0 = (int64_t)blockIdx.x * 64;     // first padded destination column
   const int c0 = blockIdx.y * 64;                    // first source column
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(
       if (kpre[mid] <= kc0) lo = mid; else hi = mid - 1;
     }
     r_begin = off[lo];
-    r_end = off[lo + 1];
+    r_end = off_end ? off_end[lo] : off[lo + 1];
     k_begin = kpre[lo];
   }
   const int tid = threadIdx.x;
@@ -177,19 +181,21 @@ hipError_t launch_transpose_dense(const uint16_t* src, int64_t nrows, int C, uin
   hipLaunchKernelGGL(transpose_pad_kernel, dim3((unsigned)(ldd / 64), (unsigned)ceil_div(C, 64),
                                                 (unsigned)batch),
                      dim3(256), 0, s, src, (int64_t)C, (const int32_t*)nullptr, (int64_t)0, C,
-                     (const int32_t*)nullptr, (const int32_t*)nullptr, 0, nrows, dst, ldd,
-                     src_batch, dst_batch);
+                     (const int32_t*)nullptr, (const int32_t*)nullptr, (const int32_t*)nullptr, 0,
+                     nrows, dst, ldd, src_batch, dst_batch);
   return hipGetLastError();
 }
 
 // grouped: rows of E experts (src rows, or rows gather[r] of a src with
-// gather_rows rows) -> dst [C, ldd] in the padded K layout kpre
+// gather_rows rows; expert e's rows offsets[e] .. ends[e], ends null:
+// offsets[e + 1]) -> dst [C, ldd] in the padded K layout kpre
 hipError_t launch_transpose_grouped(const uint16_t* src, const int32_t* gather, int64_t gather_rows,
                                     int C, const int32_t* offsets, const int32_t* kpre, int E,
-                                    uint16_t* dst, int64_t ldd, hipStream_t s) {
+                                    uint16_t* dst, int64_t ldd, hipStream_t s,
+                                    const int32_t* ends) {
   hipLaunchKernelGGL(transpose_pad_kernel, dim3((unsigned)(ldd / 64), (unsigned)ceil_div(C, 64), 1),
-                     dim3(256), 0, s, src, (int64_t)C, gather, gather_rows, C, offsets, kpre, E,
-                     (int64_t)0, dst, ldd, (int64_t)0, (int64_t)0);
+                     dim3(256), 0, s, src, (int64_t)C, gather, gather_rows, C, offsets, ends, kpre,
+                     E, (int64_t)0, dst, ldd, (int64_t)0, (int64_t)0);
   return hipGetLastError();
 }
 
@@ -533,11 +539,25 @@ hipError_t launch_dense_f32(const uint16_t* A, int64_t lda, const uint16_t* B, i
   return dense_gemm_auto<EPI_F32, 1>(a, M, s);
 }
 
+hipError_t launch_dense_f32_add2(const uint16_t* A1, int64_t lda1, const uint16_t* B1,
+                                 int64_t ldb1, int64_t K1, const uint16_t* A2, int64_t lda2,
+                                 const uint16_t* B2, int64_t ldb2, int64_t K2, int64_t M, int N,
+                                 float* C, int64_t ldc, hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = A1; a.seg[0].lda = lda1; a.seg[0].B = B1; a.seg[0].ldb = ldb1; a.seg[0].K = (int)K1;
+  a.seg[1].A = A2; a.seg[1].lda = lda2; a.seg[1].B = B2; a.seg[1].ldb = ldb2; a.seg[1].K = (int)K2;
+  a.nseg = 2;
+  a.N = N;
+  a.C = C;
+  a.ldc = ldc;
+  return dense_gemm_auto<EPI_F32_ADD, 2>(a, M, s);
+}
+
 // per-expert weight gradient: C_e[M, N] = A[:, K_e] B[:, K_e]^T, K_e expert
 // e's padded column range kpre[e] .. kpre[e + 1] of A [M, lda] and B [N, ldb]
 hipError_t launch_kgrouped_f32(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                                const int32_t* kpre, int E, int M, int N, float* C,
-                               int64_t c_expert_stride, hipStream_t s) {
+                               int64_t c_expert_stride, hipStream_t s, bool accumulate) {
   using Cfg = TileBig;
   GemmArgs a = {};
   a.seg[0].A = A; a.seg[0].lda = lda; a.seg[0].B = B; a.seg[0].ldb = ldb; a.seg[0].K = 0;
@@ -551,6 +571,9 @@ hipError_t launch_kgrouped_f32(const uint16_t* A, int64_t lda, const uint16_t* B
   a.c_expert_stride = c_expert_stride;
   a.m_tiles = (int)ceil_div(M, Cfg::bm);
   a.n_tiles = (int)ceil_div(N, Cfg::bn);
+  if (accumulate)
+    return launch_gemm<Cfg, false, false, EPI_F32_ADD, 1, F8_NONE, true>(
+        a, (int64_t)E * a.m_tiles * a.n_tiles, s);
   return launch_gemm<Cfg, false, false, EPI_F32, 1, F8_NONE, true>(
       a, (int64_t)E * a.m_tiles * a.n_tiles, s);
 }

@@ -6,6 +6,8 @@
 // expert group, device-resident token metadata).  Also the Base-2 shared
 // expert's gate/up half, on the full hidden width ("MAI-Base-2: Microsoft's
 // 2.8T base model...", section "The model").
+#include <atomic>
+
 #include "launch.hpp"
 #include "gemm.hpp"
 #include "scan.hpp"
@@ -65,6 +67,7 @@ hipError_t dense_gemm_auto(GemmArgs a, int64_t M, hipStream_t s) {
 }
 template hipError_t dense_gemm_auto<EPI_F32, 1>(GemmArgs, int64_t, hipStream_t);
 template hipError_t dense_gemm_auto<EPI_F32, 2>(GemmArgs, int64_t, hipStream_t);
+template hipError_t dense_gemm_auto<EPI_F32_ADD, 2>(GemmArgs, int64_t, hipStream_t);
 
 hipError_t launch_latent_down(const uint16_t* x, const uint16_t* w_dn, int64_t T, int d, int L,
                               uint16_t* z, hipStream_t s) {
@@ -103,6 +106,31 @@ hipError_t launch_shared_gate_up(const uint16_t* x, const uint16_t* wsg, const u
   a.C = hs;
   a.ldc = Fs;
   return dense_gemm_auto<EPI_SWIGLU, 1>(a, T, s);
+}
+
+// Backward of the shared expert (Base-2): its gate/up GEMM on x again
+// (recomputation: the forward's tiles, so g, u and hs are the forward's bit
+// for bit) with the SwiGLU backward in the epilogue: dgs = dhs us silu'(gs),
+// dus = dhs silu(gs) cast to bf16 (nearest or stochastic with the stream
+// keys), and hs.
+hipError_t launch_shared_gate_up_bwd(const uint16_t* x, const uint16_t* wsg, const uint16_t* wsu,
+                                     const float* dhs, int64_t T, int d, int Fs, int sr,
+                                     uint32_t key_dg, uint32_t key_du, uint16_t* dgs_b,
+                                     uint16_t* dus_b, uint16_t* hs_b, hipStream_t s) {
+  GemmArgs a = {};
+  a.seg[0].A = x; a.seg[0].lda = d; a.seg[0].B = wsg; a.seg[0].B2 = wsu; a.seg[0].ldb = d;
+  a.seg[0].K = d;
+  a.nseg = 1;
+  a.N = Fs;
+  a.C = dgs_b;
+  a.C2 = dus_b;
+  a.C3 = hs_b;
+  a.aux_g = dhs;
+  a.sr = sr;
+  a.sr_key_c = key_dg;
+  a.sr_key_c2 = key_du;
+  a.ldc = Fs;
+  return dense_gemm_auto<EPI_GU_BWD, 1>(a, T, s);
 }
 
 // Per-expert M-tile counts -> exclusive prefix, and the expert of every M
@@ -152,11 +180,12 @@ __global__ __launch_bounds__(1024) void round_tables_kernel(
     const int32_t* __restrict__ offsets, int E, int G, int C, int round, int bm_a, int bm_b,
     int32_t* __restrict__ seg_start, int32_t* __restrict__ seg_end, int32_t* __restrict__ h_base,
     int32_t* __restrict__ pre_a, int32_t* __restrict__ pre_b, int32_t* __restrict__ exp_a,
-    int32_t* __restrict__ exp_b, int32_t* __restrict__ queues, int32_t* __restrict__ rounds_out) {
+    int32_t* __restrict__ exp_b, int32_t* __restrict__ queues, int32_t* __restrict__ rounds_out,
+    int32_t* __restrict__ h_end) {
   __shared__ int red[32];
   const int e = threadIdx.x;
   if (e < 16) queues[e] = 0;
-  int rows = 0, need = 0;
+  int rows = 0, need = 0, hb = 0;
   if (e < E) {
     const int g0 = e / G * G, g1 = min(g0 + G, E);
     const int64_t cap = (int64_t)(g1 - g0) * C;
@@ -167,9 +196,19 @@ __global__ __launch_bounds__(1024) void round_tables_kernel(
     const int64_t en = max(min((int64_t)offsets[e + 1], w1), b);
     seg_start[e] = (int32_t)b;
     seg_end[e] = (int32_t)en;
-    h_base[e] = (int32_t)((int64_t)g0 * C + min(max(b - w0, (int64_t)0), cap));
+    hb = (int)((int64_t)g0 * C + min(max(b - w0, (int64_t)0), cap));
     rows = (int)(en - b);
     if (e == g0) need = (int)((hi - lo + cap - 1) / cap);   // this group's rounds
+  }
+  // h_end given (the backward): the round's rows packed in expert order, so
+  // the buffers need only as many rows as the round holds (at most
+  // min(T k, E C)); else the forward's slot layout (group g's slots from row
+  // first_expert(g) * C)
+  int packed_total;
+  const int packed = block_exclusive_scan(rows, &packed_total);
+  if (e < E) {
+    h_base[e] = h_end ? packed : hb;
+    if (h_end) h_end[e] = packed + rows;   // the rows' end in the round buffer
   }
   const int ma = e < E ? (rows + bm_a - 1) / bm_a : 0;
   const int mb = e < E ? (rows + bm_b - 1) / bm_b : 0;
@@ -203,10 +242,11 @@ __global__ __launch_bounds__(1024) void round_tables_kernel(
 hipError_t launch_round_tables(const int32_t* offsets, int E, int G, int C, int round, int bm_a,
                                int bm_b, int32_t* seg_start, int32_t* seg_end, int32_t* h_base,
                                int32_t* pre_a, int32_t* pre_b, int32_t* exp_a, int32_t* exp_b,
-                               int32_t* queues, int32_t* rounds_out, hipStream_t s) {
+                               int32_t* queues, int32_t* rounds_out, hipStream_t s,
+                               int32_t* h_end) {
   hipLaunchKernelGGL(round_tables_kernel, dim3(1), dim3(1024), 0, s, offsets, E, G, C, round, bm_a,
                      bm_b, seg_start, seg_end, h_base, pre_a, pre_b, exp_a, exp_b, queues,
-                     rounds_out);
+                     rounds_out, h_end);
   return hipGetLastError();
 }
 
@@ -549,17 +589,114 @@ hipError_t launch_round_experts(const uint16_t* z, const int32_t* seg_start,
                      : grouped_gemm<256, false, EPI_F32>(b, rows_bound, s);
 }
 
+// One round of the multi-round backward (the forward's round tables: expert
+// e's rows this round are [seg_start[e], seg_end[e]) of the permutation, at
+// rows h_base[e].. of the round buffers):
+//   dh = dy W_d[e]                     dy rows (permutation order) -> dh (round rows)
+//   g, u recomputed from the gathered z; dg, du, h by the SwiGLU backward
+//                                      -> dg_b, du_b, h (round rows)
+//   dzp = dg W_g[e] + du W_u[e]        round rows -> dzp (permutation order)
+// with the tile plans of the single-pass backward, so every row's values
+// are the single pass's bit for bit.  queues: 24 per-XCD counters, zeroed by
+// the round-table kernel (first 16) and here (last 8).
+hipError_t launch_round_expert_bwd(const uint16_t* dy_b, const uint16_t* z,
+                                   const int32_t* row_token, const int32_t* seg_start,
+                                   const int32_t* seg_end, const int32_t* h_base,
+                                   const int32_t* pre_a, const int32_t* exp_a,
+                                   const int32_t* pre_b, const int32_t* exp_b, int32_t* queues,
+                                   const uint16_t* w_gate, const uint16_t* w_up,
+                                   const uint16_t* w_gate_t, const uint16_t* w_up_t,
+                                   const uint16_t* w_down_t, int64_t T, int64_t rows_bound, int E,
+                                   int L, int F, int bm_a, int bm_b, int sr, uint32_t key_dg,
+                                   uint32_t key_du, float* dh, uint16_t* dg_b, uint16_t* du_b,
+                                   uint16_t* h, float* dzp, hipStream_t s) {
+  hipError_t err = launch_zero_u32((uint32_t*)queues + 16, 8, s);
+  if (err != hipSuccess) return err;
+  // dh = dy W_d[e] (B = W_d[e]^T [F, L]): A rows in permutation order, C rows
+  // in the round buffer
+  GemmArgs a = {};
+  a.seg[0].A = dy_b; a.seg[0].lda = L; a.seg[0].B = w_down_t; a.seg[0].ldb = L; a.seg[0].K = L;
+  a.nseg = 1;
+  a.N = F;
+  a.offsets = seg_start;
+  a.seg_end = seg_end;
+  a.h_base = h_base;
+  a.h_side = 1;
+  a.tile_prefix = pre_b;
+  a.tile_expert = exp_b;
+  a.queue = queues;
+  a.E = E;
+  a.b_expert_stride = (int64_t)F * L;
+  a.C = dh;
+  a.ldc = F;
+  err = bm_b == 128 ? grouped_gemm<128, false, EPI_F32>(a, rows_bound, s)
+                    : grouped_gemm<256, false, EPI_F32>(a, rows_bound, s);
+  if (err != hipSuccess) return err;
+  // the gate/up GEMM again with the SwiGLU backward in its epilogue: A = the
+  // gathered z of the round's rows; dh (aux), dg, du and h at round rows
+  GemmArgs g = {};
+  g.seg[0].A = z; g.seg[0].lda = L; g.seg[0].B = w_gate; g.seg[0].B2 = w_up; g.seg[0].ldb = L;
+  g.seg[0].K = L;
+  g.nseg = 1;
+  g.N = F;
+  g.offsets = seg_start;
+  g.seg_end = seg_end;
+  g.h_base = h_base;
+  g.h_side = 1;
+  g.tile_prefix = pre_a;
+  g.tile_expert = exp_a;
+  g.E = E;
+  g.b_expert_stride = (int64_t)F * L;
+  g.row_token = row_token;
+  g.queue = queues + 8;
+  g.M = (int)T;
+  g.C = dg_b;
+  g.C2 = du_b;
+  g.C3 = h;
+  g.aux_g = dh;
+  g.sr = sr;
+  g.sr_key_c = key_dg;
+  g.sr_key_c2 = key_du;
+  g.ldc = F;
+  err = bm_a == 128 ? grouped_gemm<128, true, EPI_GU_BWD>(g, rows_bound, s)
+                    : grouped_gemm<256, true, EPI_GU_BWD>(g, rows_bound, s);
+  if (err != hipSuccess) return err;
+  // dzp = dg W_g[e] + du W_u[e] (B = W_g[e]^T, W_u[e]^T [L, F]): A rows in the
+  // round buffer, C rows in permutation order
+  GemmArgs b = {};
+  b.seg[0].A = dg_b; b.seg[0].lda = F; b.seg[0].B = w_gate_t; b.seg[0].ldb = F; b.seg[0].K = F;
+  b.seg[1].A = du_b; b.seg[1].lda = F; b.seg[1].B = w_up_t; b.seg[1].ldb = F; b.seg[1].K = F;
+  b.nseg = 2;
+  b.N = L;
+  b.offsets = seg_start;
+  b.seg_end = seg_end;
+  b.h_base = h_base;
+  b.h_side = 2;
+  b.tile_prefix = pre_b;
+  b.tile_expert = exp_b;
+  b.queue = queues + 16;
+  b.E = E;
+  b.b_expert_stride = (int64_t)L * F;
+  b.C = dzp;
+  b.ldc = L;
+  return bm_b == 128 ? grouped_gemm<128, false, EPI_F32, F8_NONE, 2>(b, rows_bound, s)
+                     : grouped_gemm<256, false, EPI_F32, F8_NONE, 2>(b, rows_bound, s);
+}
+
+// Compute units of the current device, queried once per device.  The cache
+// entries are atomics: threads that race on a first query store the same
+// value, so calls from several host threads are safe.
 int device_cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 }  // namespace moe

@@ -43,8 +43,10 @@
 //     experts.  Device tables (prefix of per-expert M-tile counts and the
 //     expert of every M-tile) map a tile index to (expert, M-tile, N-tile)
 //     with no host sync; an expert's rows are split into its M tiles evenly
-//     (heights a multiple of 32 rows).  Order: expert, then N tile, then M tile, so M tiles
-//     of one expert that read the same weight tile run side by side.
+//     (heights a multiple of 32 rows).  Order: expert, then groups of
+//     GROUPED_GM M tiles, then N tile, then M tile, so M tiles of one expert
+//     that read the same weight tile run side by side, and an expert with
+//     many M tiles does not re-stream its activation panels once per N tile.
 //     GATHER: A row r is row row_token[r] of the activations (the token
 //     permutation is fused into the A load).
 //   * EPI_SWIGLU: the B tile interleaves 32-row blocks of W_g and W_u for the
@@ -68,6 +70,8 @@
 //     own scales: at the second segment's first stage the accumulators are
 //     multiplied by dq_1 / dq_2 and the epilogue by dq_2 (so each segment's
 //     products end up divided by their own scales).
+//   * EPI_F32_ADD: fp32 C += the product (each element read and written by
+//     the one lane that owns it: deterministic).
 //   * EPI_GU_BWD / EPI_GU_BWD_Q8: the gate/up GEMM of the backward
 //     (recomputation) with the SwiGLU backward in the epilogue; the _Q8
 //     variant also writes dg and du as E5M2 codes and records their maxima.
@@ -81,9 +85,16 @@ namespace moe {
 
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9)
 constexpr int DENSE_GM = 4;                     // M panels per tile group (dense GEMMs)
+// M tiles per tile group inside one expert of a grouped GEMM.  An expert with
+// many M tiles (a hot expert of an imbalanced routing: 128 tiles of 256 rows)
+// would otherwise have all its M tiles read one weight tile after another,
+// re-streaming each activation panel once per N tile; in groups, the ~32
+// tiles an XCD runs side by side span a few M panels and a few N tiles
+// (4 x 8), so both operands are shared through its L2.
+constexpr int GROUPED_GM = 4;
 
 enum GemmEpi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_BIAS = 2, EPI_SWIGLU = 3, EPI_Q8 = 4,
-               EPI_SWIGLU_Q8 = 5, EPI_GU_BWD = 6, EPI_GU_BWD_Q8 = 7 };
+               EPI_SWIGLU_Q8 = 5, EPI_GU_BWD = 6, EPI_GU_BWD_Q8 = 7, EPI_F32_ADD = 8 };
 
 // FP8 operand formats of a GEMM (template parameter F8): none (bf16), both
 // operands E4M3, or the activation operand (A) E5M2 and the weights E4M3
@@ -337,8 +348,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       const int p0 = __builtin_amdgcn_readfirstlane(a.tile_prefix[e]);
       const int mt = __builtin_amdgcn_readfirstlane(a.tile_prefix[e + 1]) - p0;
       const int rem = t - p0 * a.n_tiles;
-      n_tile = rem / mt;
-      const int m_local = rem - n_tile * mt;
+      // inside the expert, groups of GROUPED_GM M tiles: a group goes N tile
+      // by N tile with the M tile fastest (an expert with at most GROUPED_GM
+      // M tiles is one group: N tile, then M tile)
+      const int grp = rem / (GROUPED_GM * a.n_tiles);
+      const int gm = min(GROUPED_GM, mt - grp * GROUPED_GM);
+      const int rg = rem - grp * GROUPED_GM * a.n_tiles;
+      n_tile = rg / gm;
+      const int m_local = grp * GROUPED_GM + (rg - n_tile * gm);
       const int rs = __builtin_amdgcn_readfirstlane(a.offsets[e]);
       const int re = __builtin_amdgcn_readfirstlane(a.seg_end ? a.seg_end[e] : a.offsets[e + 1]);
       // the expert's rows split into mt tiles of equal height (a multiple of
@@ -367,6 +384,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       kg_k0 = __builtin_amdgcn_readfirstlane(a.kpre[kg_e]);
       kg_k = __builtin_amdgcn_readfirstlane(a.kpre[kg_e + 1]) - kg_k0;
       nk = kg_k / KE;
+      // accumulating (a later round of the multi-round backward): an expert
+      // with no rows adds nothing, so its tiles are skipped
+      if constexpr (EPI == EPI_F32_ADD)
+        if (kg_k == 0) continue;
     } else {
       // Groups of DENSE_GM M panels: inside a group the tiles go N tile by N
       // tile with the M panel fastest, so a window of concurrent tiles spans a
@@ -632,13 +653,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
               const uint16_t hb = f32_to_bf16_rne(g / (1.0f + __expf(-g)) * u);
               if constexpr (epi_gu_bwd(EPI)) {
                 const int64_t o = row * a.ldc + n0 + cl;
+                // the random stream's element index is the row's place in the
+                // permutation order (r0 + rl), also when the rows sit in a
+                // round buffer (h_side 1)
+                const int64_t osr = (a.h_side == 1 ? (int64_t)(r0 + rl) : row) * a.ldc + n0 + cl;
                 const float dh = a.aux_g[o];
                 const float sg = 1.0f / (1.0f + __expf(-g));
                 const float dg = dh * u * (sg * (1.0f + g * (1.0f - sg)));
                 const float du = dh * (g * sg);
                 if (a.sr) {
-                  ((uint16_t*)a.C)[o] = f32_to_bf16_sr(dg, a.sr_key_c, (uint64_t)o);
-                  ((uint16_t*)a.C2)[o] = f32_to_bf16_sr(du, a.sr_key_c2, (uint64_t)o);
+                  ((uint16_t*)a.C)[o] = f32_to_bf16_sr(dg, a.sr_key_c, (uint64_t)osr);
+                  ((uint16_t*)a.C2)[o] = f32_to_bf16_sr(du, a.sr_key_c2, (uint64_t)osr);
                 } else {
                   ((uint16_t*)a.C)[o] = f32_to_bf16_rne(dg);
                   ((uint16_t*)a.C2)[o] = f32_to_bf16_rne(du);
@@ -647,8 +672,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
                 if constexpr (GBQ8) {
                   amax_dg = fmaxf(amax_dg, fabsf(dg));
                   amax_du = fmaxf(amax_du, fabsf(du));
-                  ((uint8_t*)a.C4)[o] = f32_to_e5m2(dg * q5_dg, a.sr, a.sr_key_c4, (uint64_t)o);
-                  ((uint8_t*)a.C5)[o] = f32_to_e5m2(du * q5_du, a.sr, a.sr_key_c5, (uint64_t)o);
+                  ((uint8_t*)a.C4)[o] = f32_to_e5m2(dg * q5_dg, a.sr, a.sr_key_c4, (uint64_t)osr);
+                  ((uint8_t*)a.C5)[o] = f32_to_e5m2(du * q5_du, a.sr, a.sr_key_c5, (uint64_t)osr);
                 }
               } else if constexpr (EPI == EPI_SWIGLU_Q8) {
                 const float hv = bf16_to_f32(hb);
@@ -674,6 +699,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
               ((uint8_t*)a.C)[row * a.ldc + col] = f32_to_e4m3_sat(zv * oscale);
             } else if constexpr (EPI == EPI_F32_BIAS) {
               ((float*)a.C)[c_off + row * a.ldc + col] = val + (a.bias ? a.bias[col] : 0.f);
+            } else if constexpr (EPI == EPI_F32_ADD) {
+              // C += result: every element is owned by one lane of one tile
+              ((float*)a.C)[c_off + row * a.ldc + col] += val;
             } else {
               ((float*)a.C)[c_off + row * a.ldc + col] = val;
             }

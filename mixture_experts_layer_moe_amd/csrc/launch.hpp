@@ -85,10 +85,27 @@ hipError_t launch_expert_down_fp8(const uint8_t* H8, const int32_t* offsets,
                                   int bm, float* Y, hipStream_t s);
 
 // multi-round dropless schedule (expert.hip)
+// h_end (nullable, the backward): the round's rows packed in expert order in
+// the round buffer (h_base = exclusive prefix of the rows each expert has this
+// round, h_end[e] = h_base[e] + its rows); null: the forward's slot layout
+// (group g's rows from row first_expert(g) * C)
 hipError_t launch_round_tables(const int32_t* offsets, int E, int G, int C, int round, int bm_a,
                                int bm_b, int32_t* seg_start, int32_t* seg_end, int32_t* h_base,
                                int32_t* pre_a, int32_t* pre_b, int32_t* exp_a, int32_t* exp_b,
-                               int32_t* queues, int32_t* rounds_out, hipStream_t s);
+                               int32_t* queues, int32_t* rounds_out, hipStream_t s,
+                               int32_t* h_end = nullptr);
+// one round of the multi-round backward's expert data gradients (expert.hip)
+hipError_t launch_round_expert_bwd(const uint16_t* dy_b, const uint16_t* z,
+                                   const int32_t* row_token, const int32_t* seg_start,
+                                   const int32_t* seg_end, const int32_t* h_base,
+                                   const int32_t* pre_a, const int32_t* exp_a,
+                                   const int32_t* pre_b, const int32_t* exp_b, int32_t* queues,
+                                   const uint16_t* w_gate, const uint16_t* w_up,
+                                   const uint16_t* w_gate_t, const uint16_t* w_up_t,
+                                   const uint16_t* w_down_t, int64_t T, int64_t rows_bound, int E,
+                                   int L, int F, int bm_a, int bm_b, int sr, uint32_t key_dg,
+                                   uint32_t key_du, float* dh, uint16_t* dg_b, uint16_t* du_b,
+                                   uint16_t* h, float* dzp, hipStream_t s);
 hipError_t launch_round_experts(const uint16_t* z, const int32_t* seg_start,
                                 const int32_t* seg_end, const int32_t* h_base,
                                 const int32_t* row_token, const int32_t* pre_a,
@@ -139,7 +156,19 @@ hipError_t launch_dzp_fp8(const uint8_t* dg8, const uint8_t* du8, const int32_t*
                           const float* wu_scale, int64_t rows, int E, int L, int F, int bm,
                           float* dzp, hipStream_t s);
 
+// shared expert backward (expert.hip): the gate/up recompute with the SwiGLU
+// backward in its epilogue
+hipError_t launch_shared_gate_up_bwd(const uint16_t* x, const uint16_t* wsg, const uint16_t* wsu,
+                                     const float* dhs, int64_t T, int d, int Fs, int sr,
+                                     uint32_t key_dg, uint32_t key_du, uint16_t* dgs_b,
+                                     uint16_t* dus_b, uint16_t* hs_b, hipStream_t s);
+
 // backward.hip
+// C[M, N] += A1 B1^T + A2 B2^T (fp32 C; bf16 operands, K-contiguous)
+hipError_t launch_dense_f32_add2(const uint16_t* A1, int64_t lda1, const uint16_t* B1,
+                                 int64_t ldb1, int64_t K1, const uint16_t* A2, int64_t lda2,
+                                 const uint16_t* B2, int64_t ldb2, int64_t K2, int64_t M, int N,
+                                 float* C, int64_t ldc, hipStream_t s);
 hipError_t launch_cvt_e5m2(const float* src, int64_t n, const float* scale, int sr, uint32_t key,
                            uint8_t* dst, hipStream_t s);
 hipError_t launch_combine_bwd_q8(const float* dc, const float* y_rows, const float* topk_w,
@@ -149,13 +178,15 @@ hipError_t launch_combine_bwd_q8(const float* dc, const float* y_rows, const flo
                                  hipStream_t s);
 hipError_t launch_cvt_grad(const float* src, int64_t n, int sr, uint32_t key, uint16_t* dst,
                            hipStream_t s);
-hipError_t launch_kpad_prefix(const int32_t* offsets, int E, int32_t* kpre, hipStream_t s);
+hipError_t launch_kpad_prefix(const int32_t* offsets, int E, int32_t* kpre, hipStream_t s,
+                              const int32_t* ends = nullptr);
 hipError_t launch_transpose_dense(const uint16_t* src, int64_t nrows, int C, uint16_t* dst,
                                   int64_t ldd, int batch, int64_t src_batch, int64_t dst_batch,
                                   hipStream_t s);
 hipError_t launch_transpose_grouped(const uint16_t* src, const int32_t* gather, int64_t gather_rows,
                                     int C, const int32_t* offsets, const int32_t* kpre, int E,
-                                    uint16_t* dst, int64_t ldd, hipStream_t s);
+                                    uint16_t* dst, int64_t ldd, hipStream_t s,
+                                    const int32_t* ends = nullptr);
 hipError_t launch_combine_bwd(const float* dc, const float* y_rows, const float* topk_w,
                               const int32_t* assign_row, int64_t T, int L, int k, int sr,
                               uint32_t key, uint16_t* dy_b, float* dw, hipStream_t s);
@@ -173,9 +204,10 @@ hipError_t launch_router_db(const float* dl, int64_t T, int E, float* part, floa
                             hipStream_t s);
 hipError_t launch_dense_f32(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                             int64_t K, int64_t M, int N, float* C, int64_t ldc, hipStream_t s);
+// accumulate: C_e += (tiles of experts with an empty K range are skipped)
 hipError_t launch_kgrouped_f32(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                                const int32_t* kpre, int E, int M, int N, float* C,
-                               int64_t c_expert_stride, hipStream_t s);
+                               int64_t c_expert_stride, hipStream_t s, bool accumulate = false);
 
 // fp8.hip: per-tensor amax of bf16 tensors (ntensor tensors of numel values,
 // numel a multiple of 8; amax holds float bits), E4M3 quantization with one

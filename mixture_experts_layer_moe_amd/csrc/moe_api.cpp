@@ -121,16 +121,22 @@ int64_t max_rounds(int64_t T, int E, int k, int G, int C) {
 // activations, the padded K layout of the weight-gradient GEMMs
 struct BwdWs {
   size_t go, goT, z, cb, cbT, dc, dyb, dtw, dh, h, dgb, dub, dzp, dzb, dzbT, xT, kpre, dybT, hT,
-      dgbT, dubT, zpT, dl, dbp, dwp, pre_a, pre_b, exp_a, exp_b, queues, dy8, dg8, du8, total;
-  int64_t Tp, Rp;
+      dgbT, dubT, zpT, dl, dbp, dwp, pre_a, pre_b, exp_a, exp_b, queues, dy8, dg8, du8,
+      rs_start, rs_end, rh_base, rh_end, total;
+  int64_t Tp, Rp, RF;
 };
 // fp8: the E5M2 codes of dy, dg and du as well (FP8 data gradients)
-BwdWs bwd_ws(int64_t T, int d, int L, int E, int k, int F, bool fp8 = false) {
+// rounds > 0 (the multi-round backward, capacity C per expert and round):
+// the expert rows' F-wide buffers and the weight gradients' transposes hold
+// one round's rows, at most min(T k, E C), instead of all T k rows
+BwdWs bwd_ws(int64_t T, int d, int L, int E, int k, int F, bool fp8 = false, int C = 0) {
   BwdWs w;
   const int64_t R = T * k;
+  w.RF = C > 0 ? round_rows_bound(T, E, k, C) : R;  // rows of the per-round buffers
   w.Tp = ceil_div(T, 64) * 64;
-  w.Rp = ceil_div(R, 64) * 64 + (int64_t)64 * E;   // >= sum_e ceil64(rows_e)
-  const size_t mt = (size_t)grouped_mtile_bound(R, E, 128);
+  w.Rp = ceil_div(w.RF, 64) * 64 + (int64_t)64 * E;   // >= sum_e ceil64(rows_e)
+  const size_t mt = (size_t)grouped_mtile_bound(w.RF, E, 128);
+  const int64_t RF = w.RF;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align_up(bytes); return at; };
   w.go = take((size_t)T * d * 2);
@@ -141,10 +147,10 @@ BwdWs bwd_ws(int64_t T, int d, int L, int E, int k, int F, bool fp8 = false) {
   w.dc = take((size_t)T * L * 4);
   w.dyb = take((size_t)R * L * 2);
   w.dtw = take((size_t)R * 4);
-  w.dh = take((size_t)R * F * 4);
-  w.h = take((size_t)R * F * 2);
-  w.dgb = take((size_t)R * F * 2);
-  w.dub = take((size_t)R * F * 2);
+  w.dh = take((size_t)RF * F * 4);
+  w.h = take((size_t)RF * F * 2);
+  w.dgb = take((size_t)RF * F * 2);
+  w.dub = take((size_t)RF * F * 2);
   w.dzp = take((size_t)R * L * 4);
   w.dzb = take((size_t)T * L * 2);
   w.dzbT = take((size_t)L * w.Tp * 2);
@@ -166,6 +172,32 @@ BwdWs bwd_ws(int64_t T, int d, int L, int E, int k, int F, bool fp8 = false) {
   w.dy8 = fp8 ? take((size_t)R * L) : 0;
   w.dg8 = fp8 ? take((size_t)R * F) : 0;
   w.du8 = fp8 ? take((size_t)R * F) : 0;
+  w.rs_start = C > 0 ? take((size_t)E * 4) : 0;
+  w.rs_end = C > 0 ? take((size_t)E * 4) : 0;
+  w.rh_base = C > 0 ? take((size_t)E * 4) : 0;
+  w.rh_end = C > 0 ? take((size_t)E * 4) : 0;
+  w.total = o;
+  return w;
+}
+
+// backward of the shared expert: g_out cast and its transpose, dhs, the
+// recomputed hs and the cast gate/up gradients, their transposes and x^T
+struct SharedBwdWs { size_t go, goT, dhs, hs, dgs, dus, hsT, dgsT, dusT, xT, total; int64_t Tp; };
+SharedBwdWs shared_bwd_ws(int64_t T, int d, int Fs) {
+  SharedBwdWs w;
+  w.Tp = ceil_div(T, 64) * 64;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align_up(bytes); return at; };
+  w.go = take((size_t)T * d * 2);
+  w.goT = take((size_t)d * w.Tp * 2);
+  w.dhs = take((size_t)T * Fs * 4);
+  w.hs = take((size_t)T * Fs * 2);
+  w.dgs = take((size_t)T * Fs * 2);
+  w.dus = take((size_t)T * Fs * 2);
+  w.hsT = take((size_t)Fs * w.Tp * 2);
+  w.dgsT = take((size_t)Fs * w.Tp * 2);
+  w.dusT = take((size_t)Fs * w.Tp * 2);
+  w.xT = take((size_t)d * w.Tp * 2);
   w.total = o;
   return w;
 }
@@ -193,7 +225,8 @@ extern "C" {
 
 size_t moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t L, int32_t E, int32_t k,
                            int32_t F, int32_t Fs) {
-  (void)Fs;
+  if (op == MOE_OP_SHARED_BACKWARD)   // the shared expert: no experts or top-k involved
+    return (T >= 0 && d > 0 && Fs > 0) ? shared_bwd_ws(T, d, Fs).total : 0;
   if (T < 0 || E <= 0 || k < 1) return 0;
   switch (op) {
     case MOE_OP_ROUTE: return d > 0 ? route_ws(T, d, E).total : 0;
@@ -205,6 +238,7 @@ size_t moe_workspace_bytes(int op, int64_t T, int32_t d, int32_t L, int32_t E, i
       return (d > 0 && L > 0 && F > 0) ? bwd_ws(T, d, L, E, k, F).total : 0;
     case MOE_OP_BACKWARD_FP8:
       return (d > 0 && L > 0 && F > 0) ? bwd_ws(T, d, L, E, k, F, true).total : 0;
+    case MOE_OP_SHARED_BACKWARD: return (d > 0 && Fs > 0) ? shared_bwd_ws(T, d, Fs).total : 0;
     default: return 0;
   }
 }
@@ -629,7 +663,8 @@ int backward_impl(const uint16_t* x, const float* w_router, const float* router_
                   int32_t L, int32_t E, int32_t k, int32_t F, int32_t rounding, uint32_t seed,
                   float* dx, float* dw_router, float* db_router, float* dw_lat_down,
                   float* dw_gate, float* dw_up, float* dw_down, float* dw_lat_up, float* dtopk_w,
-                  void* ws, size_t ws_bytes, void* stream, const BwdFp8* f8) {
+                  void* ws, size_t ws_bytes, void* stream, const BwdFp8* f8,
+                  int32_t capacity = 0, int32_t group_size = 0) {
   if (T < 0 || E <= 0 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
   if (bias_mode != MOE_BIAS_LOGITS && bias_mode != MOE_BIAS_SELECTION) return MOE_ERR_INVALID_ARG;
   if (rounding != MOE_ROUND_NEAREST && rounding != MOE_ROUND_STOCHASTIC)
@@ -639,6 +674,8 @@ int backward_impl(const uint16_t* x, const float* w_router, const float* router_
     return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (f8 && (L % 128 != 0 || F % 128 != 0)) return MOE_ERR_UNSUPPORTED;
+  const bool rounds = capacity > 0;
+  if (rounds && (f8 || (int64_t)E * capacity >= (int64_t(1) << 31))) return MOE_ERR_UNSUPPORTED;
   // the expert data-gradient GEMMs read the bf16 transposes, or (f8) the
   // E4M3 ones
   const void* wg_t = f8 ? (const void*)f8->w_gate_t8 : (const void*)w_gate_t;
@@ -656,7 +693,7 @@ int backward_impl(const uint16_t* x, const float* w_router, const float* router_
                       dw_router, dw_lat_down, dw_gate, dw_up, dw_down, dw_lat_up, ws};
   for (const void* p : al)
     if (!aligned16(p)) return MOE_ERR_UNSUPPORTED;
-  const BwdWs w = bwd_ws(T, d, L, E, k, F, f8 != nullptr);
+  const BwdWs w = bwd_ws(T, d, L, E, k, F, f8 != nullptr, rounds ? capacity : 0);
   // the weight-gradient GEMMs read 256-row tiles of the transposed operands
   // (row length Tp or Rp) through 32-bit buffer offsets
   if ((int64_t)256 * 2 * (w.Tp > w.Rp ? w.Tp : w.Rp) >= (int64_t(1) << 31))
@@ -671,7 +708,7 @@ int backward_impl(const uint16_t* x, const float* w_router, const float* router_
   const int64_t R = T * k;
   const int64_t Tp = w.Tp, Rp = w.Rp;
   float* dtw = dtopk_w ? dtopk_w : F32(w.dtw);
-  const ExpertGemmPlan plan = plan_expert_gemms(R, E);
+  const ExpertGemmPlan plan = plan_expert_gemms(w.RF, E);
   int st;
   {
     // up-projection: g = bf16(g_out), dW_up = g^T c, dc = g W_up
@@ -701,6 +738,52 @@ int backward_impl(const uint16_t* x, const float* w_router, const float* router_
     }
   }
   if (st) return st;
+  if (rounds) {
+    // the multi-round schedule: per round, the expert data gradients of the
+    // round's rows (fixed-size buffers of round_rows_bound rows) and that
+    // round's contribution to the expert weight gradients (round 0 writes,
+    // later rounds add).  The host enqueues the most rounds any routing can
+    // need; surplus rounds find no rows (their weight-gradient tiles are
+    // skipped).  K_BWD_DGRAD brackets every round.
+    EventScope ev(K_BWD_DGRAD, s);
+    int32_t* kpre = I32(w.kpre);
+    int32_t* r0 = I32(w.rs_start);
+    int32_t* r1 = I32(w.rs_end);
+    int32_t* hb = I32(w.rh_base);
+    int32_t* he = I32(w.rh_end);
+    st = hip_status(launch_latent_down(x, w_lat_down, T, d, L, B16(w.z), s));
+    const int64_t NR = max_rounds(T, E, k, group_size, capacity);
+    for (int64_t r = 0; r < NR && !st; ++r) {
+      st = hip_status(launch_round_tables(expert_offsets, E, group_size, capacity, (int)r,
+                                          plan.bm_gate_up, plan.bm_down, r0, r1, hb, I32(w.pre_a),
+                                          I32(w.pre_b), I32(w.exp_a), I32(w.exp_b),
+                                          I32(w.queues), nullptr, s, he));
+      if (!st) st = hip_status(launch_round_expert_bwd(
+          B16(w.dyb), B16(w.z), row_token, r0, r1, hb, I32(w.pre_a), I32(w.exp_a), I32(w.pre_b),
+          I32(w.exp_b), I32(w.queues), w_gate, w_up, w_gate_t, w_up_t, w_down_t, T, w.RF, E, L, F,
+          plan.bm_gate_up, plan.bm_down, sr, sr_stream_key(seed, 3), sr_stream_key(seed, 4),
+          F32(w.dh), B16(w.dgb), B16(w.dub), B16(w.h), F32(w.dzp), s));
+      // this round's weight gradients: dW_d += dy^T h, dW_g += dg^T z, dW_u += du^T z
+      const bool acc = r > 0;
+      if (!st) st = hip_status(launch_kpad_prefix(r0, E, kpre, s, r1));
+      if (!st) st = hip_status(launch_transpose_grouped(B16(w.dyb), nullptr, 0, L, r0, kpre, E,
+                                                        B16(w.dybT), Rp, s, r1));
+      if (!st) st = hip_status(launch_transpose_grouped(B16(w.h), nullptr, 0, F, hb, kpre, E,
+                                                        B16(w.hT), Rp, s, he));
+      if (!st) st = hip_status(launch_kgrouped_f32(B16(w.dybT), Rp, B16(w.hT), Rp, kpre, E, L, F,
+                                                   dw_down, (int64_t)L * F, s, acc));
+      if (!st) st = hip_status(launch_transpose_grouped(B16(w.dgb), nullptr, 0, F, hb, kpre, E,
+                                                        B16(w.dgbT), Rp, s, he));
+      if (!st) st = hip_status(launch_transpose_grouped(B16(w.dub), nullptr, 0, F, hb, kpre, E,
+                                                        B16(w.dubT), Rp, s, he));
+      if (!st) st = hip_status(launch_transpose_grouped(B16(w.z), row_token, T, L, r0, kpre, E,
+                                                        B16(w.zpT), Rp, s, r1));
+      if (!st) st = hip_status(launch_kgrouped_f32(B16(w.dgbT), Rp, B16(w.zpT), Rp, kpre, E, F, L,
+                                                   dw_gate, (int64_t)F * L, s, acc));
+      if (!st) st = hip_status(launch_kgrouped_f32(B16(w.dubT), Rp, B16(w.zpT), Rp, kpre, E, F, L,
+                                                   dw_up, (int64_t)F * L, s, acc));
+    }
+  } else {
   {
     // experts: dh = dy W_d; z and the gate/up GEMM recomputed with the SwiGLU
     // backward in its epilogue (dg, du, and h for dW_d); the rows' latent
@@ -765,6 +848,7 @@ int backward_impl(const uint16_t* x, const float* w_router, const float* router_
                                                  dw_gate, (int64_t)F * L, s));
     if (!st) st = hip_status(launch_kgrouped_f32(B16(w.dubT), Rp, B16(w.zpT), Rp, kpre, E, F, L,
                                                  dw_up, (int64_t)F * L, s));
+  }
   }
   if (st) return st;
   {
@@ -847,6 +931,120 @@ int moe_grad_cast_e5m2(const float* src, int64_t n, const float* scale, int32_t 
   return hip_status(launch_cvt_e5m2(src, n, scale, rounding == MOE_ROUND_STOCHASTIC,
                                     sr_stream_key(seed, (uint32_t)stream_id), dst,
                                     (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int moe_backward_prepare_shared(const uint16_t* ws_gate, const uint16_t* ws_up,
+                                const uint16_t* ws_down, int32_t d, int32_t Fs,
+                                uint16_t* ws_gate_t, uint16_t* ws_up_t, uint16_t* ws_down_t,
+                                void* stream) {
+  if (d <= 0 || Fs <= 0) return MOE_ERR_INVALID_ARG;
+  if (!dims_ok(d) || !dims_ok(Fs)) return MOE_ERR_UNSUPPORTED;
+  const void* ptrs[] = {ws_gate, ws_up, ws_down, ws_gate_t, ws_up_t, ws_down_t};
+  for (const void* p : ptrs) {
+    if (!p) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  int st = hip_status(launch_transpose_dense(ws_gate, Fs, d, ws_gate_t, Fs, 1, 0, 0, s));
+  if (!st) st = hip_status(launch_transpose_dense(ws_up, Fs, d, ws_up_t, Fs, 1, 0, 0, s));
+  if (!st) st = hip_status(launch_transpose_dense(ws_down, d, Fs, ws_down_t, d, 1, 0, 0, s));
+  return st;
+}
+
+int moe_shared_backward(const uint16_t* x, const float* g_out, const uint16_t* ws_gate,
+                        const uint16_t* ws_up, const uint16_t* ws_gate_t,
+                        const uint16_t* ws_up_t, const uint16_t* ws_down_t, int64_t T,
+                        int32_t d, int32_t Fs, int32_t rounding, uint32_t seed, float* dx,
+                        float* dws_gate, float* dws_up, float* dws_down, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (T < 0 || d <= 0 || Fs <= 0) return MOE_ERR_INVALID_ARG;
+  if (rounding != MOE_ROUND_NEAREST && rounding != MOE_ROUND_STOCHASTIC)
+    return MOE_ERR_INVALID_ARG;
+  if (!dims_ok(d) || !dims_ok(Fs)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  const void* req[] = {x, g_out, ws_gate, ws_up, ws_gate_t, ws_up_t, ws_down_t, dx, dws_gate,
+                       dws_up, dws_down, ws};
+  for (const void* p : req) {
+    if (!p) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  }
+  const SharedBwdWs w = shared_bwd_ws(T, d, Fs);
+  // the weight-gradient GEMMs read 256-row tiles of the transposed operands
+  // (row length Tp) through 32-bit buffer offsets; rows of x, g and the
+  // [T, Fs] gradients likewise within a tile
+  if ((int64_t)256 * 2 * w.Tp >= (int64_t(1) << 31) || (int64_t)256 * 4 * Fs >= (int64_t(1) << 31) ||
+      T * (int64_t)Fs >= (int64_t(1) << 40))
+    return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  auto B16 = [&](size_t off) { return (uint16_t*)(base + off); };
+  auto F32 = [&](size_t off) { return (float*)(base + off); };
+  const int sr = rounding == MOE_ROUND_STOCHASTIC;
+  const int64_t Tp = w.Tp;
+  // g = bf16(g_out) (the same cast as moe_backward's: stream 1), and g^T
+  int st = hip_status(launch_cvt_grad(g_out, T * d, sr, sr_stream_key(seed, 1), B16(w.go), s));
+  if (!st) st = hip_status(launch_transpose_dense(B16(w.go), T, d, B16(w.goT), Tp, 1, 0, 0, s));
+  // dhs = g Ws_d  (B = Ws_d^T [Fs, d])
+  if (!st) st = hip_status(launch_dense_f32(B16(w.go), d, ws_down_t, d, d, T, Fs, F32(w.dhs), Fs,
+                                            s));
+  // gs, us, hs recomputed; dgs, dus cast (streams 9, 10)
+  if (!st) st = hip_status(launch_shared_gate_up_bwd(x, ws_gate, ws_up, F32(w.dhs), T, d, Fs, sr,
+                                                     sr_stream_key(seed, 9),
+                                                     sr_stream_key(seed, 10), B16(w.dgs),
+                                                     B16(w.dus), B16(w.hs), s));
+  // dx += dgs Ws_g + dus Ws_u  (B = Ws_g^T, Ws_u^T [d, Fs])
+  if (!st) st = hip_status(launch_dense_f32_add2(B16(w.dgs), Fs, ws_gate_t, Fs, Fs, B16(w.dus), Fs,
+                                                 ws_up_t, Fs, Fs, T, d, dx, d, s));
+  // weight gradients over the tokens (K = Tp, zero-padded transposes):
+  // dWs_d = g^T hs, dWs_g = dgs^T x, dWs_u = dus^T x
+  if (!st) st = hip_status(launch_transpose_dense(B16(w.hs), T, Fs, B16(w.hsT), Tp, 1, 0, 0, s));
+  if (!st) st = hip_status(launch_dense_f32(B16(w.goT), Tp, B16(w.hsT), Tp, Tp, d, Fs, dws_down,
+                                            Fs, s));
+  if (!st) st = hip_status(launch_transpose_dense(B16(w.dgs), T, Fs, B16(w.dgsT), Tp, 1, 0, 0, s));
+  if (!st) st = hip_status(launch_transpose_dense(B16(w.dus), T, Fs, B16(w.dusT), Tp, 1, 0, 0, s));
+  if (!st) st = hip_status(launch_transpose_dense(x, T, d, B16(w.xT), Tp, 1, 0, 0, s));
+  if (!st) st = hip_status(launch_dense_f32(B16(w.dgsT), Tp, B16(w.xT), Tp, Tp, Fs, d, dws_gate, d,
+                                            s));
+  if (!st) st = hip_status(launch_dense_f32(B16(w.dusT), Tp, B16(w.xT), Tp, Tp, Fs, d, dws_up, d,
+                                            s));
+  return st;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t moe_workspace_bytes_backward_rounds(int64_t T, int32_t d, int32_t L, int32_t E, int32_t k,
+                                           int32_t F, int32_t capacity, int32_t group_size) {
+  if (T < 0 || E <= 0 || k < 1 || d <= 0 || L <= 0 || F <= 0 || capacity < 1 || group_size < 1)
+    return 0;
+  return bwd_ws(T, d, L, E, k, F, false, capacity).total;
+}
+
+int moe_backward_rounds(const uint16_t* x, const float* w_router, const float* router_logits,
+                        int32_t bias_mode, const int32_t* topk_idx, const float* topk_w,
+                        const int32_t* expert_offsets, const int32_t* row_token,
+                        const int32_t* assign_row, const float* y_rows,
+                        const uint16_t* w_lat_down, const uint16_t* w_gate, const uint16_t* w_up,
+                        const uint16_t* w_lat_down_t, const uint16_t* w_gate_t,
+                        const uint16_t* w_up_t, const uint16_t* w_down_t,
+                        const uint16_t* w_lat_up_t, const float* g_out, int64_t T, int32_t d,
+                        int32_t L, int32_t E, int32_t k, int32_t F, int32_t capacity,
+                        int32_t group_size, int32_t rounding, uint32_t seed, float* dx,
+                        float* dw_router, float* db_router, float* dw_lat_down, float* dw_gate,
+                        float* dw_up, float* dw_down, float* dw_lat_up, float* dtopk_w, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (capacity < 1 || group_size < 1) return MOE_ERR_INVALID_ARG;
+  return backward_impl(x, w_router, router_logits, bias_mode, topk_idx, topk_w, expert_offsets,
+                       row_token, assign_row, y_rows, w_lat_down, w_gate, w_up, w_lat_down_t,
+                       w_gate_t, w_up_t, w_down_t, w_lat_up_t, g_out, T, d, L, E, k, F, rounding,
+                       seed, dx, dw_router, db_router, dw_lat_down, dw_gate, dw_up, dw_down,
+                       dw_lat_up, dtopk_w, ws, ws_bytes, stream, nullptr, capacity, group_size);
 }
 
 }  // extern "C"

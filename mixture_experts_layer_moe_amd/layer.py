@@ -184,12 +184,16 @@ def forward_rounds(x, w: LatentMoEWeights, k, buf: LatentMoEBuffers, capacity, g
 
 @dataclasses.dataclass
 class LatentMoETransposed:
-    """Transposed bf16 weight copies of the backward's data-gradient GEMMs."""
+    """Transposed bf16 weight copies of the backward's data-gradient GEMMs
+    (and of the shared expert's, for a layer that has one)."""
     w_lat_down_t: torch.Tensor   # [d, L]
     w_gate_t: torch.Tensor       # [E, L, F]
     w_up_t: torch.Tensor         # [E, L, F]
     w_down_t: torch.Tensor       # [E, F, L]
     w_lat_up_t: torch.Tensor     # [L, d]
+    ws_gate_t: torch.Tensor | None = None   # [d, Fs]
+    ws_up_t: torch.Tensor | None = None     # [d, Fs]
+    ws_down_t: torch.Tensor | None = None   # [Fs, d]
 
 
 def backward_prepare(w: LatentMoEWeights, stream=None) -> LatentMoETransposed:
@@ -204,14 +208,23 @@ def backward_prepare(w: LatentMoEWeights, stream=None) -> LatentMoETransposed:
     _lib.moe_backward_prepare(w.w_lat_down, w.w_gate, w.w_up, w.w_down, w.w_lat_up,
                               t.w_lat_down_t, t.w_gate_t, t.w_up_t, t.w_down_t, t.w_lat_up_t,
                               stream=stream)
+    if w.ws_gate is not None:
+        Fs = w.ws_gate.shape[0]
+        t.ws_gate_t = torch.empty((d, Fs), dtype=bf, device=dev)
+        t.ws_up_t = torch.empty((d, Fs), dtype=bf, device=dev)
+        t.ws_down_t = torch.empty((Fs, d), dtype=bf, device=dev)
+        _lib.moe_backward_prepare_shared(w.ws_gate, w.ws_up, w.ws_down, t.ws_gate_t, t.ws_up_t,
+                                         t.ws_down_t, stream=stream)
     return t
 
 
 class LatentMoEGrads:
     """fp32 gradients of every parameter and of x, the gate weights' gradient,
-    and the backward's workspace."""
+    and the backward's workspace (Fs > 0: also the shared expert's weight
+    gradients and its workspace)."""
 
-    def __init__(self, T, d, L, E, k, F, device="cuda", bias=True, fp8=False):
+    def __init__(self, T, d, L, E, k, F, device="cuda", bias=True, fp8=False, Fs=0,
+                 workspace=True):
         dev = torch.device(device)
         f32 = torch.float32
         self.dx = torch.empty((T, d), dtype=f32, device=dev)
@@ -225,7 +238,15 @@ class LatentMoEGrads:
         self.dtopk_w = torch.empty((T, k), dtype=f32, device=dev)
         op = _lib.MOE_OP_BACKWARD_FP8 if fp8 else _lib.MOE_OP_BACKWARD
         nb = _lib.moe_workspace_bytes(op, T, d, L, E, k, F, 0)
-        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        self.dws_gate = self.dws_up = self.dws_down = None
+        if Fs:
+            self.dws_gate = torch.empty((Fs, d), dtype=f32, device=dev)
+            self.dws_up = torch.empty((Fs, d), dtype=f32, device=dev)
+            self.dws_down = torch.empty((d, Fs), dtype=f32, device=dev)
+            # one workspace for both calls (they run in order on one stream)
+            nb = max(nb, _lib.moe_workspace_bytes(_lib.MOE_OP_SHARED_BACKWARD, T, d, L, E, k, F, Fs))
+        # workspace=False: no workspace (backward_rounds brings its own)
+        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev) if workspace else None
 
 
 def backward(x, w: LatentMoEWeights, wt: LatentMoETransposed, buf: LatentMoEBuffers, g_out,
@@ -241,7 +262,55 @@ def backward(x, w: LatentMoEWeights, wt: LatentMoETransposed, buf: LatentMoEBuff
                       wt.w_lat_up_t, g_out, rounding, seed, grads.dx, grads.dw_router,
                       grads.db_router, grads.dw_lat_down, grads.dw_gate, grads.dw_up,
                       grads.dw_down, grads.dw_lat_up, grads.dtopk_w, grads.ws, stream=stream)
+    _shared_backward(x, w, wt, g_out, grads, rounding, seed, stream)
     return grads
+
+
+def backward_rounds(x, w: LatentMoEWeights, wt: LatentMoETransposed, buf: LatentMoEBuffers, g_out,
+                    grads: LatentMoEGrads, capacity, group_size, ws_rounds=None,
+                    rounding=_lib.MOE_ROUND_STOCHASTIC, seed=0, bias_mode=_lib.MOE_BIAS_LOGITS,
+                    stream=None):
+    """The backward pass with the routed experts on the multi-round schedule
+    (fixed per-expert capacity per round, shared inside groups of group_size
+    experts): the experts' activation buffers hold one round's rows.
+    ``ws_rounds``: workspace of moe_workspace_bytes_backward_rounds bytes (and
+    of the shared expert's backward, for a layer that has one), allocated
+    here if None; grads' own workspace is not used."""
+    if buf.logits is None:
+        raise ValueError("the forward buffers must keep the router logits (keep_logits=True)")
+    d, L, E, F, Fs = w.dims
+    if ws_rounds is None:
+        nb = _lib.moe_workspace_bytes_backward_rounds(buf.T, d, L, E, buf.k, F, capacity,
+                                                      group_size)
+        if Fs:
+            nb = max(nb, _lib.moe_workspace_bytes(_lib.MOE_OP_SHARED_BACKWARD, buf.T, d, L, E,
+                                                  buf.k, F, Fs))
+        ws_rounds = torch.empty(max(nb, 256), dtype=torch.uint8, device=x.device)
+    _lib.moe_backward_rounds(x, w.w_router, buf.logits, bias_mode, buf.topk_idx, buf.topk_w,
+                             buf.expert_offsets, buf.row_token, buf.assign_row, buf.y_rows,
+                             w.w_lat_down, w.w_gate, w.w_up, wt.w_lat_down_t, wt.w_gate_t,
+                             wt.w_up_t, wt.w_down_t, wt.w_lat_up_t, g_out, capacity, group_size,
+                             rounding, seed, grads.dx, grads.dw_router, grads.db_router,
+                             grads.dw_lat_down, grads.dw_gate, grads.dw_up, grads.dw_down,
+                             grads.dw_lat_up, grads.dtopk_w, ws_rounds, stream=stream)
+    if w.ws_gate is not None:
+        _lib.moe_shared_backward(x, g_out, w.ws_gate, w.ws_up, wt.ws_gate_t, wt.ws_up_t,
+                                 wt.ws_down_t, rounding, seed, grads.dx, grads.dws_gate,
+                                 grads.dws_up, grads.dws_down, ws_rounds, stream=stream)
+    return grads
+
+
+def _shared_backward(x, w, wt, g_out, grads, rounding, seed, stream):
+    """The shared expert's gradients (a layer with one), after moe_backward
+    (which overwrites dx; this adds the shared expert's part)."""
+    if w.ws_gate is None:
+        return
+    if wt.ws_gate_t is None or grads.dws_gate is None:
+        raise ValueError("a layer with a shared expert needs backward_prepare's shared transposes "
+                         "and LatentMoEGrads(..., Fs=Fs)")
+    _lib.moe_shared_backward(x, g_out, w.ws_gate, w.ws_up, wt.ws_gate_t, wt.ws_up_t, wt.ws_down_t,
+                             rounding, seed, grads.dx, grads.dws_gate, grads.dws_up,
+                             grads.dws_down, grads.ws, stream=stream)
 
 
 # ---------------------------------------------------------------------------
@@ -308,6 +377,7 @@ def backward_fp8(x, w: LatentMoEWeights, wt: LatentMoETransposed, wt8: LatentMoE
                           grads.db_router, grads.dw_lat_down, grads.dw_gate, grads.dw_up,
                           grads.dw_down, grads.dw_lat_up, grads.dtopk_w, scaling.amax, grads.ws,
                           stream=stream)
+    _shared_backward(x, w, wt, g_out, grads, rounding, seed, stream)
     if update_scaling:
         scaling.update(stream=stream)
     return grads

@@ -369,3 +369,31 @@ def test_permute_noalloc_rejects_bad_args():
     assert lib.moe_permute_noalloc(None, 8, 2, 16, P, P, P, P, None) == -1
     # the static scratch holds 2^21 int32: 2 * ceil(T / 256) * E beyond that
     assert lib.moe_permute_noalloc(P, 600_000, 1, 512, P, P, P, P, None) == -2
+
+
+def test_backward_rounds_and_shared_backward_args():
+    lib = _lib.load()
+    T, d, L, E, k, F = 64, 128, 64, 8, 2, 128
+    assert lib.moe_workspace_bytes_backward_rounds(T, d, L, E, k, F, 0, 4) == 0
+    assert lib.moe_workspace_bytes_backward_rounds(T, d, L, E, k, F, 16, 0) == 0
+    single = lib.moe_workspace_bytes(5, T, d, L, E, k, F, 0)
+    # a round holds at most min(T k, E C) rows: the per-round buffers shrink
+    # with the capacity, and never exceed the single pass's
+    small = lib.moe_workspace_bytes_backward_rounds(T, d, L, E, k, F, 4, 2)
+    large = lib.moe_workspace_bytes_backward_rounds(T, d, L, E, k, F, 1000, 2)
+    assert 0 < small < large and large >= single
+    args = [P] * 18 + [T, d, L, E, k, F]
+    tail = [1, 12, P, P, P, P, P, P, P, P, P, P, 1 << 40, None]
+    assert lib.moe_backward_rounds(*(args[:3] + [0] + args[3:] + [0, 4] + tail)) == -1
+    assert lib.moe_backward_rounds(*(args[:3] + [0] + args[3:] + [16, 0] + tail)) == -1
+    # the shared expert's backward
+    assert lib.moe_workspace_bytes(7, T, d, 0, 0, 0, 0, 128) > 0
+    assert lib.moe_workspace_bytes(7, T, d, 0, 0, 0, 0, 0) == 0
+    sargs = [P] * 7
+    assert lib.moe_shared_backward(*sargs, T, d, 128, 2, 0, P, P, P, P, P, 1 << 40, None) == -1
+    assert lib.moe_shared_backward(*sargs, T, d, 100, 1, 0, P, P, P, P, P, 1 << 40, None) == -2
+    assert lib.moe_shared_backward(*sargs, T, d, 128, 1, 0, P, P, P, P, None, 1 << 40, None) == -1
+    assert lib.moe_shared_backward(*sargs, T, d, 128, 1, 0, P, P, P, P, P, 16, None) == -3
+    assert lib.moe_shared_backward(*sargs, 0, d, 128, 1, 0, P, P, P, P, P, 0, None) == 0
+    assert lib.moe_backward_prepare_shared(P, P, P, d, 0, P, P, P, None) == -1
+    assert lib.moe_backward_prepare_shared(P, P, None, d, 128, P, P, P, None) == -1
