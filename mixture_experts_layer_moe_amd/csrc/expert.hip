@@ -252,7 +252,10 @@ hipError_t launch_round_tables(const int32_t* offsets, int E, int G, int C, int 
 
 template <int BM, bool GATHER, int EPI, int F8 = F8_NONE, int NSEG = 1>
 static hipError_t grouped_gemm(GemmArgs a, int64_t rows, hipStream_t s) {
-  using C = std::conditional_t<BM == 128, TileStream, TileBig>;
+  // the forward's FP8 weight stream takes the wide FP8 tile; the FP8
+  // gradient GEMMs (E5M2 A, K segments) keep the bf16 stream tile
+  using CS = std::conditional_t<F8 == F8_E4M3 && NSEG == 1, TileStreamF8, TileStream>;
+  using C = std::conditional_t<BM == 128, CS, TileBig>;
   static_assert(C::bm == BM, "tile height");
   a.n_tiles = (int)ceil_div(epi_swiglu(EPI) ? 2 * (int64_t)a.N : a.N, C::bn);
   const int64_t bound = grouped_mtile_bound(rows, a.E, BM) * a.n_tiles;

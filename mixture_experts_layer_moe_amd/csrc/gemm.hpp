@@ -267,7 +267,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   static_assert(!SWG || WTN % 64 == 0, "swiglu pairs");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4 && LPS * (NSTAGE - 2) < 64, "stages");
   static_assert(NSEG >= 1 && NSEG <= 3 && (!GATHER || NSEG == 1), "K segments");
-  __shared__ uint4 smem[NSTAGE * STAGE + 1];
+  __shared__ uint4 smem[NSTAGE * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -313,12 +313,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
   float amax_run = 0.f;     // Q8: largest |bf16 output| this lane wrote
   float amax_dg = 0.f, amax_du = 0.f;   // GBQ8: largest |dg|, |du| of this lane
 
-  // The queue's tile index is broadcast through the last 16-byte slot of the
-  // LDS array (one LDS object only, so the compiler's LDS-DMA alias tracking
-  // does not add waits in the K loop).
+  // The queue's tile index is broadcast through the first 16 bytes of the
+  // ring's last stage (one LDS object only, so the compiler's LDS-DMA alias
+  // tracking does not add waits in the K loop; and the ring can take the
+  // whole LDS).  That stage is free here: the previous tile's loads have all
+  // landed and its reads ended at its last barrier; the next tile's first
+  // stages go to the other slots, and the loop loads into the last one only
+  // after its first barrier, which every wave reaches after reading the
+  // index.
   auto next_tile = [&](int prev) -> int {
     if (a.queue == nullptr) return prev < 0 ? t_begin + (blockIdx.x >> 3) : prev + nj;
-    int* slot = (int*)&smem[NSTAGE * STAGE];
+    int* slot = (int*)&smem[(NSTAGE - 1) * STAGE];
     if (tid == 0) {
       // the XCD's kq-th tile: chunks of n_tiles consecutive tiles are dealt
       // to the XCDs in turn (chunk c to XCD c % 8)
@@ -385,7 +390,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a) {
       kg_k = __builtin_amdgcn_readfirstlane(a.kpre[kg_e + 1]) - kg_k0;
       nk = kg_k / KE;
       // accumulating (a later round of the multi-round backward): an expert
-      // with no rows adds nothing, so its tiles are skipped
+      // with no rows adds nothing, so its tiles are skipped (K-grouped
+      // launches take the static tile order, whose next_tile touches no LDS,
+      // so skipping the tile's barriers is safe)
       if constexpr (EPI == EPI_F32_ADD)
         if (kg_k == 0) continue;
     } else {
@@ -748,6 +755,7 @@ inline int persistent_grid(int64_t tiles_upper_bound) {
 //   Mid    : 128 x 256, BK 64, 2 x 4 waves, 3 stages -- smaller dense GEMMs
 //            and the routing GEMM at mid and small batches
 //   Wide   : 256 x 192 (below)
+//   StreamF8: 128 x 512 (below)
 // (the dense GEMMs choose among Big, Wide and Mid by rounds x tile area /
 // efficiency)
 template <int BM, int BN, int BK, int WM, int WN, int NSTAGE, bool BNT>
@@ -762,12 +770,22 @@ using TileMid = TileCfg<128, 256, 64, 2, 4, 3, false>;
 //        e.g. M 4,096 x N 3,072: 256 tiles fill the chip exactly once, where
 //        128 x 256 tiles take 1.5 waves
 using TileWide = TileCfg<256, 192, 64, 4, 2, 2, false>;
+// StreamF8 : 128 x 512, BK 64 (a 128-byte stage row holds 128 FP8 K values),
+//            2 x 4 waves (64 x 128 each), 2 stages (160 KB, the whole LDS),
+//            non-temporal weight loads -- the FP8 weight stream: a K step of
+//            FP8 weights is half the bytes of a bf16 one, so the tile is twice
+//            as wide as Stream to move as many weight bytes per tile (the
+//            per-tile fixed cost of queue, tables and first-stage latency
+//            then weighs as little as in bf16; measured 7.6 -> 5.7 ms for the
+//            Base-1 gate/up at T = 4,096)
+using TileStreamF8 = TileCfg<128, 512, 64, 2, 4, 2, true>;
 
 template <class C, bool GROUPED, bool GATHER, int EPI, int NSEG = 1, int F8 = F8_NONE,
           bool KG = false>
 hipError_t launch_gemm(const GemmArgs& a, int64_t tiles_upper_bound, hipStream_t s) {
   if (tiles_upper_bound <= 0) return hipSuccess;
   if (a.nseg != NSEG) return hipErrorInvalidValue;
+  if (KG && a.queue != nullptr) return hipErrorInvalidValue;   // K-grouped: static tile order
   const int grid = persistent_grid(tiles_upper_bound);
   hipLaunchKernelGGL((gemm_kernel<C::bm, C::bn, C::bk, C::wm, C::wn, C::nstage, GROUPED, GATHER,
                                   EPI, C::bnt, NSEG, F8, KG>),

@@ -27,7 +27,8 @@ CASES = {
     "wide": MoEConfig("wide", T=130, d=256, L=128, E=1024, k=16, F=128, seed=7),
     # few experts with many rows each: several M tiles per expert
     "deep": MoEConfig("deep", T=2048, d=256, L=256, E=8, k=2, F=512, seed=9),
-    # ~750 rows per expert: the 640-row tile, two M tiles per expert, N and K tails
+    # ~750 rows per expert: three M tiles per expert of equal height (a
+    # multiple of 32, at most 256), the last one ragged; N and K tails
     "deeptail": MoEConfig("deeptail", T=3000, d=320, L=192, E=4, k=1, F=320, seed=13),
     # Zipf-like router bias: hot experts and empty experts
     "zipf": MoEConfig("zipf", T=1024, d=256, L=128, E=64, k=4, F=256, zipf_bias=True, seed=11),
