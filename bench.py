@@ -50,7 +50,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default=None,
-                   help="workload (default: base1_compute; base1_ep8 with --backward)")
+                   help="workload (default: base1_compute; base1_ep8 with --backward; "
+                        "base2_ep8 is the backward's Base-2 share, with the shared expert)")
     p.add_argument("--secondary", default="base1_small_batch",
                    help="a second workload with the same weights and a smaller batch, timed in "
                         "the same run and reported under 'secondary' ('none' to skip)")
@@ -238,34 +239,41 @@ def backward_flops(cfg):
     """(model, executed) FLOPs of one backward pass.  Model: twice the
     forward's (the data and the weight gradient of every GEMM), the count MFU
     uses on the pages (recomputation excluded).  Executed adds the
-    recomputation of z (2TdL) and of the experts' gate/up (4TkLF)."""
-    T, d, L, E, k, F = cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F
-    model = 2.0 * (2.0 * T * d * E + 4.0 * T * d * L + 6.0 * T * k * L * F)
-    return model, model + 2.0 * T * d * L + 4.0 * T * k * L * F
+    recomputation of z (2TdL), of the experts' gate/up (4TkLF) and of the
+    shared expert's gate/up (4TdFs)."""
+    T, d, L, E, k, F, Fs = cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, cfg.Fs
+    model = 2.0 * (2.0 * T * d * E + 4.0 * T * d * L + 6.0 * T * k * L * F + 6.0 * T * d * Fs)
+    return model, model + 2.0 * T * d * L + 4.0 * T * k * L * F + 4.0 * T * d * Fs
 
 
 def bench_backward(args, cfg, dev):
     """Time K backward passes (after one forward pass that keeps the router
-    logits) of the layer on seeded synthetic inputs and output gradient."""
+    logits) of the layer on seeded synthetic inputs and output gradient: the
+    single pass (moe_backward, or moe_backward_fp8), or with --capacity the
+    multi-round schedule (moe_backward_rounds); a layer with a shared expert
+    adds moe_shared_backward."""
     import numpy as np
     import torch
 
     import mixture_experts_layer_moe_amd as moe
     from moe_synth import device
-    if cfg.Fs:
-        print("the backward pass has no shared expert", file=sys.stderr)
+    if args.capacity > 0 and args.grad_fp8:
+        print("--capacity with --backward runs the bf16 gradients only", file=sys.stderr)
         sys.exit(2)
     print(f"[bench] backward: {cfg.description}; generating inputs on the GPU", file=sys.stderr,
           flush=True)
     dv = device.device_inputs(cfg, dev)
     w = moe.LatentMoEWeights(dv["w_router"], dv["b_router"], dv["w_dn"], dv["w_gate"], dv["w_up"],
-                             dv["w_down"], dv["w_lat_up"])
-    buf = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, device=dev,
+                             dv["w_down"], dv["w_lat_up"], dv.get("ws_gate"), dv.get("ws_up"),
+                             dv.get("ws_down"))
+    buf = moe.LatentMoEBuffers(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, cfg.Fs, device=dev,
                                keep_logits=True)
     moe.forward(dv["x"], w, cfg.k, buf)
     wt = moe.backward_prepare(w)
+    rounds_info = None
     grads = moe.LatentMoEGrads(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F, device=dev,
-                               bias=dv["b_router"] is not None, fp8=args.grad_fp8)
+                               bias=dv["b_router"] is not None, fp8=args.grad_fp8, Fs=cfg.Fs,
+                               workspace=args.capacity <= 0)
     g = torch.Generator(device=dev)
     g.manual_seed(1234)
     g_out = torch.randn((cfg.T, cfg.d), generator=g, dtype=torch.float32, device=dev)
@@ -277,27 +285,42 @@ def bench_backward(args, cfg, dev):
         gsc = moe.Fp8GradScaling(device=dev)
         step = lambda i: moe.backward_fp8(dv["x"], w, wt, wt8, buf, g_out, grads, gsc,  # noqa: E731
                                           rounding=rounding, seed=i)
+    elif args.capacity > 0:
+        cap = max(1, int(round(args.capacity * cfg.T * cfg.k / cfg.E)))
+        gs = min(args.group_size, cfg.E)
+        nb = moe.moe_workspace_bytes_backward_rounds(cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F,
+                                                     cap, gs)
+        if cfg.Fs:
+            nb = max(nb, moe.moe_workspace_bytes(moe.MOE_OP_SHARED_BACKWARD, cfg.T, cfg.d, cfg.L,
+                                                 cfg.E, cfg.k, cfg.F, cfg.Fs))
+        ws_r = torch.empty(nb, dtype=torch.uint8, device=dev)
+        rounds_info = {"capacity": cap, "group_size": gs, "workspace_bytes": nb,
+                       "single_pass_workspace_bytes": moe.moe_workspace_bytes(
+                           moe.MOE_OP_BACKWARD, cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F)}
+        step = lambda i: moe.backward_rounds(dv["x"], w, wt, buf, g_out, grads,  # noqa: E731
+                                             cap, gs, ws_rounds=ws_r, rounding=rounding, seed=i)
     else:
         step = lambda i: moe.backward(dv["x"], w, wt, buf, g_out, grads,  # noqa: E731
                                       rounding=rounding, seed=i)
+    bwd_kernels = BWD_KERNELS + (["bwd_shared"] if cfg.Fs else [])
     torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup} backward steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     hip = HipEvents()
-    ev = {name: [(hip.create(), hip.create()) for _ in range(args.steps)] for name in BWD_KERNELS}
+    ev = {name: [(hip.create(), hip.create()) for _ in range(args.steps)] for name in bwd_kernels}
     print(f"[bench] timing {args.steps} backward steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        for name in BWD_KERNELS:
+        for name in bwd_kernels:
             moe.moe_set_kernel_events(name, *ev[name][i])
         step(args.warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for name in BWD_KERNELS:
+    for name in bwd_kernels:
         moe.moe_set_kernel_events(name, None, None)
-    kern_ms = {n: float(np.mean([hip.elapsed_ms(a, b) for a, b in ev[n]])) for n in BWD_KERNELS}
+    kern_ms = {n: float(np.mean([hip.elapsed_ms(a, b) for a, b in ev[n]])) for n in bwd_kernels}
     for pairs in ev.values():
         for a, b in pairs:
             hip.destroy(a)
@@ -323,8 +346,9 @@ def bench_backward(args, cfg, dev):
         "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16, fp8 data gradients" if args.grad_fp8 else "bf16", "data": "synthetic",
         "config": {"workload": cfg.description, "T": cfg.T, "d": cfg.d, "latent": cfg.L,
-                   "experts": cfg.E, "top_k": cfg.k, "ffn": cfg.F, "seed": cfg.seed,
-                   "rounding": args.rounding, "grad_fp8": bool(args.grad_fp8)},
+                   "experts": cfg.E, "top_k": cfg.k, "ffn": cfg.F, "shared_ffn": cfg.Fs,
+                   "seed": cfg.seed, "rounding": args.rounding, "grad_fp8": bool(args.grad_fp8),
+                   "multi_round": rounds_info},
         "roofline": {"bound": "mfma", "kernel": "expert data-gradient group (gate/up "
                      "recompute, dh + SwiGLU backward, dz rows)",
                      "achieved": dgrad_flops / dgrad_s / 1e12,
@@ -473,7 +497,9 @@ def main():
     sec = None
     if args.secondary and args.secondary != "none":
         sec = CONFIGS[args.secondary]
-        if not same_weights(cfg, sec) or sec.T > cfg.T:
+        if sec.name == cfg.name:
+            sec = None     # the workload itself: nothing more to time
+        elif not same_weights(cfg, sec) or sec.T > cfg.T:
             print(f"[bench] secondary workload {sec.name} does not share {cfg.name}'s weights "
                   f"and batch; not timed", file=sys.stderr)
             sec = None

@@ -569,7 +569,8 @@ int moe_backward_fp8(const uint16_t* x, const float* w_router, const float* rout
 #define MOE_KERNEL_BWD_WGRAD    11   /* backward: padded transposes, dW_d/g/u   */
 #define MOE_KERNEL_BWD_LATENT   12   /* backward: gather dz, dx, dW_dn          */
 #define MOE_KERNEL_BWD_ROUTER   13   /* backward: softmax backward, router GEMMs */
-#define MOE_KERNEL_COUNT        14
+#define MOE_KERNEL_BWD_SHARED   14   /* moe_shared_backward: the whole call      */
+#define MOE_KERNEL_COUNT        15
 int moe_set_kernel_events(int kernel, void* start_event, void* stop_event);
 
 #ifdef __cplusplus

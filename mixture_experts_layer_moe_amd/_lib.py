@@ -26,7 +26,8 @@ MOE_OP_SHARED_BACKWARD = 7
 MOE_ROUND_NEAREST, MOE_ROUND_STOCHASTIC = 0, 1
 KERNELS = {"router_gemm": 0, "router_topk": 1, "permute": 2, "latent_down": 3, "gate_up": 4,
            "expert_down": 5, "combine": 6, "latent_up": 7, "bwd_up": 8, "bwd_combine": 9,
-           "bwd_dgrad": 10, "bwd_wgrad": 11, "bwd_latent": 12, "bwd_router": 13}
+           "bwd_dgrad": 10, "bwd_wgrad": 11, "bwd_latent": 12, "bwd_router": 13,
+           "bwd_shared": 14}
 
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 

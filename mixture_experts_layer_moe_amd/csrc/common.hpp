@@ -16,7 +16,7 @@ enum KernelId {
   K_ROUTER_GEMM = 0, K_ROUTER_TOPK = 1, K_PERMUTE = 2, K_LATENT_DOWN = 3,
   K_GATE_UP = 4, K_EXPERT_DOWN = 5, K_COMBINE = 6, K_LATENT_UP = 7, K_BWD_UP = 8,
   K_BWD_COMBINE = 9, K_BWD_DGRAD = 10, K_BWD_WGRAD = 11, K_BWD_LATENT = 12, K_BWD_ROUTER = 13,
-  K_COUNT = 14
+  K_BWD_SHARED = 14, K_COUNT = 15
 };
 
 // Records the caller's start/stop events (if registered on this thread)

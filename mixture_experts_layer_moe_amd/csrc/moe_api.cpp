@@ -986,6 +986,7 @@ int moe_shared_backward(const uint16_t* x, const float* g_out, const uint16_t* w
   auto F32 = [&](size_t off) { return (float*)(base + off); };
   const int sr = rounding == MOE_ROUND_STOCHASTIC;
   const int64_t Tp = w.Tp;
+  EventScope ev(K_BWD_SHARED, s);
   // g = bf16(g_out) (the same cast as moe_backward's: stream 1), and g^T
   int st = hip_status(launch_cvt_grad(g_out, T * d, sr, sr_stream_key(seed, 1), B16(w.go), s));
   if (!st) st = hip_status(launch_transpose_dense(B16(w.go), T, d, B16(w.goT), Tp, 1, 0, 0, s));
