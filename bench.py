@@ -95,7 +95,10 @@ class HipEvents:
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
         rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
-        return ms.value if rc == 0 else None   # None: a kernel that this path does not launch
+        if rc != 0:
+            self.hip.hipGetLastError()   # clear it: a later runtime check must not report it
+            return None                  # a kernel that this path does not launch
+        return ms.value
 
     def destroy(self, e):
         self.hip.hipEventDestroy(ctypes.c_void_p(e))
@@ -320,7 +323,11 @@ def bench_backward(args, cfg, dev):
     t1 = time.perf_counter()
     for name in bwd_kernels:
         moe.moe_set_kernel_events(name, None, None)
-    kern_ms = {n: float(np.mean([hip.elapsed_ms(a, b) for a, b in ev[n]])) for n in bwd_kernels}
+    kern_ms = {}
+    for n in bwd_kernels:
+        vals = [hip.elapsed_ms(a, b) for a, b in ev[n]]
+        if all(v is not None for v in vals):     # groups this path records
+            kern_ms[n] = float(np.mean(vals))
     for pairs in ev.values():
         for a, b in pairs:
             hip.destroy(a)
@@ -329,13 +336,16 @@ def bench_backward(args, cfg, dev):
     ms = elapsed / args.steps * 1e3
     model, executed = backward_flops(cfg)
     # the experts' data-gradient group (gate/up recompute, dh + SwiGLU
-    # backward, the rows' latent gradient): 10 T k L F executed FLOPs
-    dgrad_flops = 10.0 * cfg.T * cfg.k * cfg.L * cfg.F
-    wgrad_flops = 6.0 * cfg.T * cfg.k * cfg.L * cfg.F
+    # backward, the rows' latent gradient): 10 T k L F executed FLOPs; on the
+    # multi-round schedule the group brackets every round, whose expert
+    # weight gradients (6 T k L F) it then includes
+    tkLF = cfg.T * cfg.k * cfg.L * cfg.F
+    wgrad_flops = 6.0 * tkLF
+    rounds = rounds_info is not None
+    dgrad_flops = (16.0 if rounds else 10.0) * tkLF
     # its time at peak: all bf16, or (FP8 data gradients) the gate/up
     # recompute (4 T k L F) at the bf16 peak and dh + dz rows (6 T k L F) at
     # the FP8 peak
-    tkLF = cfg.T * cfg.k * cfg.L * cfg.F
     dgrad_peak_s = (4.0 * tkLF / MFMA_BF16_PEAK + 6.0 * tkLF / MFMA_FP8_PEAK) if args.grad_fp8 \
         else dgrad_flops / MFMA_BF16_PEAK
     dgrad_s = kern_ms["bwd_dgrad"] * 1e-3
@@ -350,7 +360,8 @@ def bench_backward(args, cfg, dev):
                    "seed": cfg.seed, "rounding": args.rounding, "grad_fp8": bool(args.grad_fp8),
                    "multi_round": rounds_info},
         "roofline": {"bound": "mfma", "kernel": "expert data-gradient group (gate/up "
-                     "recompute, dh + SwiGLU backward, dz rows)",
+                     "recompute, dh + SwiGLU backward, dz rows" +
+                     ("; every round, with its expert weight gradients)" if rounds else ")"),
                      "achieved": dgrad_flops / dgrad_s / 1e12,
                      "peak": dgrad_flops / dgrad_peak_s / 1e12, "unit": "TFLOP/s",
                      "frac": dgrad_peak_s / dgrad_s,
@@ -358,7 +369,8 @@ def bench_backward(args, cfg, dev):
         "layer": {"model_flops": model, "executed_flops": executed,
                   "mfma_frac_model": model / (ms * 1e-3) / MFMA_BF16_PEAK,
                   "mfma_frac_executed": executed / (ms * 1e-3) / MFMA_BF16_PEAK,
-                  "expert_wgrad_tflops": wgrad_flops / (kern_ms["bwd_wgrad"] * 1e-3) / 1e12,
+                  "expert_wgrad_tflops": (wgrad_flops / (kern_ms["bwd_wgrad"] * 1e-3) / 1e12
+                                          if "bwd_wgrad" in kern_ms else None),
                   "kernels_ms": {k: round(v, 4) for k, v in kern_ms.items()}},
         "cpu_baseline": None,
     }
