@@ -128,13 +128,14 @@ def stored_traffic(config_name):
 def dominant_work(cfg, counts, esize=2):
     """Algorithmic FLOPs and bytes of one launch of the grouped gate/up GEMM:
     2 GEMMs of 2*rows*L*F FLOPs; bytes = gate+up weights of every expert that
-    received a row (each read once) + the gathered latent rows + H out, all
-    of esize bytes per value (2: bf16, 1: FP8 E4M3)."""
+    received a row (each read once) + the latent rows z (each token's row
+    once: the GEMM gathers it k times, the algorithm needs it once) + H out,
+    all of esize bytes per value (2: bf16, 1: FP8 E4M3)."""
     import numpy as np
     touched = int(np.count_nonzero(counts))
     rows = cfg.T * cfg.k
     flops = 4.0 * rows * cfg.L * cfg.F
-    nbytes = (touched * 2.0 * cfg.F * cfg.L + rows * cfg.L + rows * cfg.F) * esize
+    nbytes = (touched * 2.0 * cfg.F * cfg.L + cfg.T * cfg.L + rows * cfg.F) * esize
     return flops, nbytes, touched
 
 
