@@ -15,6 +15,11 @@ computed round by round in buffers of min(T k, E capacity) rows).
 * Schedules from one round down to many rounds, with and without capacity
   borrowing inside expert groups; a layer with a shared expert (its
   gradients from moe_shared_backward after the rounds).
+* At full size, one EP-8 rank's share of Base-1 (T = 32,768, 64 experts,
+  ~4,096 rows per expert) with a capacity of half the mean rows per expert in
+  groups of 8 (the schedule bench.py --backward --capacity 0.5 times): the
+  same comparison with the single pass at that shape, whose gradients
+  tests/test_gpu_backward_fullsize.py checks against the oracle.
 """
 import numpy as np
 import pytest
@@ -22,7 +27,7 @@ import torch
 
 import mixture_experts_layer_moe_amd as moe
 import oracle
-from moe_synth import MoEConfig, device, gen
+from moe_synth import CONFIGS, MoEConfig, device, gen
 from tests import gpu_util as U
 from tests.test_gpu_backward import GRAD_TOL_MAX, GRAD_TOL_RMS
 
@@ -115,3 +120,59 @@ def test_backward_rounds(cuda, name, rounding, sched):
         emax, erms = U.rel_err(U.to_np(getattr(gr, gname)), ref[oname])
         assert emax <= GRAD_TOL_MAX and erms <= GRAD_TOL_RMS, (gname, emax, erms)
     U.log(f"[{tag}] bitwise equal to the single pass on {same}; oracle rules met")
+
+
+@pytest.mark.fullsize
+@pytest.mark.timeout(900)
+def test_backward_rounds_full_size(cuda):
+    cfg = CONFIGS["base1_ep8"]
+    T, d, L, E, k, F = cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F
+    seed = 4321
+    rmode = moe.MOE_ROUND_STOCHASTIC
+    U.log(f"[bwd rounds full] {cfg.description}: inputs on the GPU, forward")
+    dv = device.device_inputs(cfg, cuda)
+    w = moe.LatentMoEWeights(dv["w_router"], dv["b_router"], dv["w_dn"], dv["w_gate"], dv["w_up"],
+                             dv["w_down"], dv["w_lat_up"])
+    buf = moe.LatentMoEBuffers(T, d, L, E, k, F, device=cuda, keep_logits=True)
+    moe.forward(dv["x"], w, k, buf)
+    wt = moe.backward_prepare(w)
+    g = torch.Generator(device=cuda)
+    g.manual_seed(seed)
+    g_out = torch.randn((T, d), generator=g, dtype=torch.float32, device=cuda)
+    U.log("[bwd rounds full] single pass")
+    single = moe.LatentMoEGrads(T, d, L, E, k, F, device=cuda, bias=dv["b_router"] is not None)
+    moe.backward(dv["x"], w, wt, buf, g_out, single, rounding=rmode, seed=seed)
+    torch.cuda.synchronize()
+    single.ws = None               # the single pass's workspace is not needed any more
+    torch.cuda.empty_cache()
+    capacity = int(round(0.5 * T * k / E))
+    group = 8
+    n_rounds, _ = oracle.round_schedule(buf.expert_offsets.cpu().numpy(), capacity, group)
+    tag = f"bwd rounds full, capacity {capacity} in groups of {group}"
+    U.log(f"[{tag}] {n_rounds} rounds")
+    assert n_rounds >= 2
+    gr = moe.LatentMoEGrads(T, d, L, E, k, F, device=cuda, bias=dv["b_router"] is not None,
+                            workspace=False)
+    moe.backward_rounds(dv["x"], w, wt, buf, g_out, gr, capacity, group, rounding=rmode,
+                        seed=seed)
+    torch.cuda.synchronize()
+    for n in SAME:
+        a, b = getattr(gr, n), getattr(single, n)
+        if a is None:
+            continue
+        assert torch.equal(a, b), f"{tag}: {n} differs from the single pass"
+    for n in SPLIT:
+        a, b = getattr(gr, n), getattr(single, n)
+        assert bool(torch.isfinite(a).all()), n
+        dmax = dsq = bsq = 0.0
+        for e in range(E):        # one expert at a time: float64 temporaries stay small
+            de = (a[e] - b[e]).double()
+            dmax = max(dmax, float(de.abs().max()))
+            dsq += float(de.pow(2).sum())
+            bsq += float(b[e].double().pow(2).sum())
+        rms = (bsq / b.numel()) ** 0.5
+        emax = dmax / rms
+        erms = (dsq / b.numel()) ** 0.5 / rms
+        U.log(f"[{tag}] {n} vs single pass: max|diff|/RMS {emax:.1e}, RMS {erms:.1e}")
+        assert emax <= 1e-4 and erms <= 1e-5, (n, emax, erms)
+    U.log(f"[{tag}] bitwise equal to the single pass on {SAME}")
