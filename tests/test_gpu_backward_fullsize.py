@@ -2,7 +2,7 @@
 rank's share of the MAI-Base-1 layer (T = 32,768 tokens, d = 6,656, latent
 3,072, 64 experts of SwiGLU width 10,240, top-8; ~4,096 rows per expert), in
 the launch configuration ``bench.py --backward`` times (and ``--grad-fp8``),
-with stochastic rounding.
+with stochastic rounding; and the routed experts of the Base-2 share (bf16).
 
 The float64 oracle cannot run this backward whole, so it computes, from the
 pages' definitions in the same rounding model as tests/test_gpu_backward.py
@@ -151,8 +151,8 @@ def _token_pass(hst, gi, g_out, toks, gscale):
     return dtw, dz, amax
 
 
-def _run(cuda, fp8):
-    cfg = CONFIGS["base1_ep8"]
+def _run(cuda, fp8, name="base1_ep8"):
+    cfg = CONFIGS[name]
     T, d, L, E, k, F = cfg.T, cfg.d, cfg.L, cfg.E, cfg.k, cfg.F
     U.log(f"[bwd full{' fp8' if fp8 else ''}] {cfg.description}: inputs on the GPU, forward")
     dv = device.device_inputs(cfg, cuda)
@@ -253,3 +253,11 @@ def test_backward_full_size_sampled(cuda):
 @pytest.mark.timeout(1200)
 def test_backward_fp8_full_size_sampled(cuda):
     _run(cuda, fp8=True)
+
+
+@pytest.mark.timeout(1200)
+def test_backward_full_size_sampled_base2_share(cuda):
+    # the routed experts of one EP-8 rank's share of Base-2 (T = 16,384,
+    # d = 8,704, latent 4,096, 64 experts of width 8,192, top-7; ~1,792 rows
+    # per expert); the shared expert's backward has its own full-size test
+    _run(cuda, fp8=False, name="base2_ep8")
