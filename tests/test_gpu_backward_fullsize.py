@@ -2,7 +2,8 @@
 rank's share of the MAI-Base-1 layer (T = 32,768 tokens, d = 6,656, latent
 3,072, 64 experts of SwiGLU width 10,240, top-8; ~4,096 rows per expert), in
 the launch configuration ``bench.py --backward`` times (and ``--grad-fp8``),
-with stochastic rounding; and the routed experts of the Base-2 share (bf16).
+with stochastic rounding; and the routed experts of the Base-2 share (bf16
+and FP8 data gradients).
 
 The float64 oracle cannot run this backward whole, so it computes, from the
 pages' definitions in the same rounding model as tests/test_gpu_backward.py
@@ -261,3 +262,8 @@ def test_backward_full_size_sampled_base2_share(cuda):
     # d = 8,704, latent 4,096, 64 experts of width 8,192, top-7; ~1,792 rows
     # per expert); the shared expert's backward has its own full-size test
     _run(cuda, fp8=False, name="base2_ep8")
+
+
+@pytest.mark.timeout(1200)
+def test_backward_fp8_full_size_sampled_base2_share(cuda):
+    _run(cuda, fp8=True, name="base2_ep8")
