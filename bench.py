@@ -64,6 +64,10 @@ def parse():
                         "multiple of the mean rows per expert (0: single pass)")
     p.add_argument("--group-size", type=int, default=8,
                    help="experts sharing capacity in the multi-round schedule")
+    p.add_argument("--balancer", action="store_true",
+                   help="route with moe_route_ex: the router bias steers the selection only "
+                        "(loss-free balancer) and the per-expert probability sums of the "
+                        "load-balancing loss are computed (bf16 single-pass forward)")
     p.add_argument("--backward", action="store_true",
                    help="time the backward pass (moe_backward) after one forward pass instead "
                         "of the forward (default workload then: base1_ep8)")
@@ -409,6 +413,13 @@ def time_forward(args, cfg, w, x, dev, w8=None):
         rounds_info = {"capacity": cap, "group_size": gs, "workspace_bytes": nb}
         step = lambda: moe.forward_rounds(x, w, cfg.k, buf, cap, gs, ws_rounds=ws_r,  # noqa: E731
                                           rounds_out=rounds_t)
+    if args.balancer:
+        prob_sum = torch.zeros(cfg.E, dtype=torch.float32, device=dev)
+
+        def step():
+            moe.moe_route_ex(x, w.w_router, w.b_router, moe.MOE_BIAS_SELECTION, cfg.k,
+                             buf.topk_idx, buf.topk_w, prob_sum=prob_sum, ws=buf.ws)
+            moe.forward(x, w, cfg.k, buf, route=False)
     if w8 is not None:
         scaling = moe.Fp8Scaling(hist_len=1024, device=dev)
         step = lambda: moe.forward_fp8(x, w, w8, cfg.k, buf, scaling)  # noqa: E731
@@ -479,6 +490,9 @@ def time_forward(args, cfg, w, x, dev, w8=None):
            "config": {"workload": cfg.description, "name": cfg.name, "T": cfg.T, "d": cfg.d,
                       "latent": cfg.L, "experts": cfg.E, "top_k": cfg.k, "ffn": cfg.F,
                       "shared_ffn": cfg.Fs, "seed": cfg.seed}}
+    if args.balancer:
+        res["config"]["router"] = ("moe_route_ex: selection-only bias (loss-free balancer), "
+                                   "per-expert probability sums")
     if rounds_info is not None:
         rounds_info["rounds"] = int(rounds_t.item())
         res["config"]["multi_round"] = rounds_info
@@ -506,6 +520,9 @@ def main():
         return bench_backward(args, cfg, dev)
     if args.capacity > 0 and args.fp8:
         print("--capacity runs the bf16 experts only", file=sys.stderr)
+        sys.exit(2)
+    if args.balancer and (args.fp8 or args.capacity > 0):
+        print("--balancer runs the bf16 single-pass forward only", file=sys.stderr)
         sys.exit(2)
     sec = None
     if args.secondary and args.secondary != "none":
